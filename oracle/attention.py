@@ -1,0 +1,187 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package's smoke check and the benchmark's CPU-baseline
+leg may import this module.  It shares no code with the HIP library and never
+calls it.  Everything here is the plain mathematical definition, evaluated in
+float64 with numpy; a matrix product is the only library step used.
+
+Pages cited (by title and section):
+  [CH18]  "第 18 章 FlashAttention" (AI algorithm guide, theaiera.top)
+  [L21]   "CMU 11-868 L21 FlashAttention" lecture digest (quidproquo.cc)
+
+Conventions (readings of the pages where they are silent or disagree):
+  * scores are multiplied by ``scale`` (the spec convention); [CH18]
+    §18.2.1 writes the same thing as a division by sqrt(d_k).
+  * GQA: query head hq reads KV head hq // (Hq // Hkv)  ([CH18] §18.2.2 requires
+    Hq to be a multiple of Hkv; the contiguous-group map is our reading).
+  * causal is top-left aligned and only defined for Nq == Nk: key j is allowed
+    for query i iff j <= i  ([CH18] §18.2.2 item 3, mask M_ij).
+  * the saved row statistic is LSE_i = m_i + ln(l_i) in natural-log units.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_head(hq: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head ``hq`` (contiguous groups of Hq//Hkv)."""
+    assert Hq % Hkv == 0
+    return hq // (Hq // Hkv)
+
+
+def allowed(Nq: int, Nk: int, causal: bool, rows=None) -> np.ndarray:
+    """Boolean [len(rows)][Nk] mask of keys each query may attend.
+
+    [CH18] §18.2.2 (3): M_ij = 0 for j <= i and -inf for j > i.
+    """
+    rows = np.arange(Nq) if rows is None else np.asarray(rows)
+    if not causal:
+        return np.ones((len(rows), Nk), dtype=bool)
+    assert Nq == Nk, "causal attention is defined here for Nq == Nk only"
+    return np.arange(Nk)[None, :] <= rows[:, None]
+
+
+def scores(q, k, scale, causal, rows=None):
+    """S = scale * Q K^T for one head, with masked entries set to -inf.
+
+    q: [Nq][d], k: [Nk][d]; ``rows`` selects query rows.  [CH18] §18.2.1 and
+    §18.2.2 (3).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    r = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    s = scale * (q[r] @ k.T)
+    if causal:
+        s = np.where(allowed(q.shape[0], k.shape[0], True, r), s, -np.inf)
+    return s
+
+
+def softmax_rows(s):
+    """Row softmax with the row max subtracted first ([CH18] §18.4.2 (2), safe
+    softmax).  Returns (P, m, l) with P = exp(s - m) / l."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def head_forward(q, k, v, scale, causal, rows=None):
+    """O and LSE for one (b, head): O = softmax(scale Q K^T + M) V.
+
+    [CH18] §18.2.1 (definition), §18.2.2 (causal mask); LSE as stored by the
+    forward for the recomputation backward ([CH18] §18.2.4, Fig. 18-6).
+    """
+    s = scores(q, k, scale, causal, rows)
+    p, m, l = softmax_rows(s)
+    o = p @ _f64(v)
+    return o, m + np.log(l)
+
+
+def forward(q, k, v, scale, causal=False, rows=None):
+    """Batched forward.  q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] -> (O, LSE) fp64.
+
+    ``rows`` optionally restricts the queries evaluated (each row of O depends
+    only on its own query row, so a subset is still the plain definition).
+    """
+    q = _f64(q)
+    B, Hq, Nq, d = q.shape
+    Hkv = k.shape[1]
+    nr = Nq if rows is None else len(rows)
+    o = np.empty((B, Hq, nr, v.shape[-1]))
+    lse = np.empty((B, Hq, nr))
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head(h, Hq, Hkv)
+            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, hk], v[b, hk], scale,
+                                              causal, rows)
+    return o, lse
+
+
+def probabilities(q, k, scale, causal=False):
+    """Full attention matrix P for one head (used by invariance checks)."""
+    p, _, _ = softmax_rows(scores(q, k, scale, causal))
+    return p
+
+
+def softmax_backward(p, dp):
+    """dS = P * (dP - rowsum(P * dP)): the softmax Jacobian applied row by row,
+    [CH18] §18.2.4 (1)."""
+    return p * (dp - (p * dp).sum(axis=1, keepdims=True))
+
+
+def head_backward(q, k, v, do, scale, causal):
+    """Materialising backward for one head, [CH18] §18.2.4 (2):
+    dV = P^T dO, dP = dO V^T, dS = softmax_backward(P, dP), dQ = scale dS K,
+    dK = scale dS^T Q.  Returns (dq, dk, dv, delta) with delta_i = sum_j P_ij dP_ij.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    p, _, _ = softmax_rows(scores(q, k, scale, causal))
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = softmax_backward(p, dp)
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    delta = (p * dp).sum(axis=1)
+    return dq, dk, dv, delta
+
+
+def backward(q, k, v, do, scale, causal=False):
+    """Batched backward -> (dQ, dK, dV) fp64.  A KV head's gradient is the sum
+    over the query heads that read it (GQA broadcast, [CH18] §18.2.2)."""
+    q = _f64(q)
+    B, Hq, Nq, d = q.shape
+    Hkv = k.shape[1]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head(h, Hq, Hkv)
+            a, bk, bv, _ = head_backward(q[b, h], k[b, hk], v[b, hk], do[b, h],
+                                         scale, causal)
+            dq[b, h] = a
+            dk[b, hk] += bk
+            dv[b, hk] += bv
+    return dq, dk, dv
+
+
+def decode_split(q, k, v, scale, num_splits):
+    """Flash-Decoding, [CH18] §18.8.2 (2): split the KV length into
+    ``num_splits`` equal chunks, attend each chunk on its own, then merge.
+
+    q [B][Hq][1][d], k/v [B][Hkv][Nk][d].  Each chunk's partial is stored as
+    (O_c normalised, lse_c); the merge is lse = M + ln sum_c exp(lse_c - M),
+    O = sum_c exp(lse_c - lse) O_c, which equals the page's
+    sum_t O_t e^{m_t - m} / sum_t l_t e^{m_t - m} with unnormalised O_t.
+    Returns (O [B][Hq][1][d], lse [B][Hq][1], O_parts [B][Hq][S][d],
+    lse_parts [B][Hq][S]).
+    """
+    q = _f64(q)
+    B, Hq, Nq, d = q.shape
+    assert Nq == 1
+    Nk = k.shape[2]
+    assert Nk % num_splits == 0
+    c = Nk // num_splits
+    o_parts = np.empty((B, Hq, num_splits, v.shape[-1]))
+    lse_parts = np.empty((B, Hq, num_splits))
+    for s in range(num_splits):
+        o_s, l_s = forward(q, k[:, :, s * c:(s + 1) * c], v[:, :, s * c:(s + 1) * c],
+                           scale, causal=False)
+        o_parts[:, :, s] = o_s[:, :, 0]
+        lse_parts[:, :, s] = l_s[:, :, 0]
+    o, lse = combine(o_parts, lse_parts)
+    return o[:, :, None, :], lse[:, :, None], o_parts, lse_parts
+
+
+def combine(o_parts, lse_parts):
+    """Merge split partials with their log-sum-exp weights ([CH18] §18.8.2 (2),
+    the reduction step).  o_parts [..][S][d], lse_parts [..][S]."""
+    M = lse_parts.max(axis=-1, keepdims=True)
+    lse = M[..., 0] + np.log(np.exp(lse_parts - M).sum(axis=-1))
+    w = np.exp(lse_parts - lse[..., None])
+    o = (w[..., None] * o_parts).sum(axis=-2)
+    return o, lse

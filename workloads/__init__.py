@@ -1,0 +1,123 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and shapes them; it holds none of the
+attention arithmetic.  Both the HIP path's callers (tests, bench, smoke) and the
+fp64 oracle take their inputs from here, so the two sides always see the same
+values.
+
+Every tensor is contiguous [B][H][N][d] ("BHSD").  Values are drawn with
+``torch.randn`` in float32 (the pages' checks and benchmarks all use
+``torch.randn`` inputs) and then rounded to bf16 (round-to-nearest-even) where
+the workload is bf16.  Draw order inside one workload: Q, K, V, dO, then the
+FP8 extras (Q outlier positions, Q outlier signs, K outlier positions, K outlier
+signs, the Hadamard sign vector).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str            # "f32", "bf16" or "fp8"
+    causal: bool = False
+    backward: bool = False
+    num_splits: int = 0   # >0: split-KV decode
+    seed: int = 0
+    outlier_frac: float = 0.0
+    outlier_mag: float = 0.0
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def fwd_flops(self) -> float:
+        # two GEMMs of 2*Nq*Nk*d each per (b, hq); causal keeps half.
+        f = 4.0 * self.B * self.Hq * self.Nq * self.Nk * self.d
+        return f * 0.5 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        return 2.5 * self.fwd_flops()
+
+    def scaled(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, 1, 1, 256, 256, 64, "f32", causal=False,
+                         backward=True, seed=8301,
+                         note="fp32, 64-row tiles => 4 KV blocks of online rescaling"),
+    "prefill_bf16": Workload("prefill_bf16", 4, 16, 16, 2048, 2048, 64, "bf16",
+                             causal=False, seed=8302),
+    "causal_bf16": Workload("causal_bf16", 2, 16, 16, 8192, 8192, 128, "bf16",
+                            causal=True, backward=True, seed=8303),
+    "decode_gqa": Workload("decode_gqa", 8, 32, 8, 1, 131072, 128, "bf16",
+                           num_splits=64, seed=8304),
+    "fp8_fwd": Workload("fp8_fwd", 2, 16, 16, 8192, 8192, 128, "fp8", causal=False,
+                        seed=8305, outlier_frac=1e-3, outlier_mag=50.0),
+}
+
+
+def _gen(seed: int, device: str) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _randn(shape, gen, device):
+    return torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+
+
+def make_inputs(w: Workload, device: str = "cpu", seed: int | None = None):
+    """Draw Q, K, V (and dO for backward workloads) for workload ``w``.
+
+    Returns a dict of tensors on ``device``: q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d],
+    optionally do [B][Hq][Nq][d].  bf16 and fp8 workloads return bf16 tensors
+    (the fp8 path quantises them itself); f32 returns float32.  fp8 workloads
+    also get outliers planted in Q and K and a ``signs`` int8 vector of +-1 of
+    length d for the Hadamard rotation.
+    """
+    gen = _gen(w.seed if seed is None else seed, device)
+    qs = (w.B, w.Hq, w.Nq, w.d)
+    ks = (w.B, w.Hkv, w.Nk, w.d)
+    q = _randn(qs, gen, device)
+    k = _randn(ks, gen, device)
+    v = _randn(ks, gen, device)
+    out = {}
+    if w.backward:
+        out["do"] = _randn(qs, gen, device)
+    if w.outlier_frac > 0:
+        for name, t in (("q", q), ("k", k)):
+            n = t.numel()
+            cnt = int(round(w.outlier_frac * n))
+            pos = torch.randperm(n, generator=gen, device=device)[:cnt]
+            sgn = torch.randint(0, 2, (cnt,), generator=gen, device=device).float() * 2 - 1
+            t.view(-1)[pos] = sgn * w.outlier_mag
+    if w.dtype == "fp8":
+        out["signs"] = (torch.randint(0, 2, (w.d,), generator=gen, device=device)
+                        .to(torch.int8) * 2 - 1)
+    cast = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    out["q"] = q.to(cast).contiguous()
+    out["k"] = k.to(cast).contiguous()
+    out["v"] = v.to(cast).contiguous()
+    if "do" in out:
+        out["do"] = out["do"].to(cast).contiguous()
+    return out
+
+
+def to_f64(t: torch.Tensor):
+    """Exact widening of a bf16 / fp32 tensor to a float64 numpy array."""
+    return t.detach().to("cpu", torch.float64).numpy()
