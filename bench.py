@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X exact-attention library.
+
+One step = the headline workload's whole training pass: bf16 causal forward
+plus backward at B=2, H=16, N=8192, d=128 (fa_fwd, then fa_bwd's three
+stages), inputs resident in HBM.  The value is its aggregate throughput in
+TFLOP/s, counting 4*B*H*N*N*d/2 for the causal forward and 2.5x that for the
+backward.  The remaining rows of the path are timed after the steps, each on
+its own workload, and reported under "parts": the non-causal forward at the
+same shape, the d=64 prefill forward, the split-KV decode (GB/s of the
+algorithmic bytes K+V+Q+O+LSE) and the fp8 forward.
+
+Prints ONE JSON line.  --gpus above 1 is not supported (one-GPU build).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def timed(fn, iters, stream):
+    """Average ms of fn() over iters calls, measured with HIP events on stream."""
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(iters):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def cpu_baseline(w):
+    """The fp64 oracle on the host cores: forward + backward of one (b, h) head
+    of the headline workload at full sequence length."""
+    import numpy as np
+    import torch
+    from oracle import attention as A
+    from workloads import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    mk = lambda: to_f64(torch.randn(w.Nq, w.d, generator=g).to(torch.bfloat16))
+    q, k, v, do = mk(), mk(), mk(), mk()
+    t0 = time.perf_counter()
+    A.head_forward(q, k, v, w.scale, w.causal)
+    A.head_backward(q, k, v, do, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    one = w.scaled(B=1, Hq=1, Hkv=1)
+    flops = one.fwd_flops() + one.bwd_flops()
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"forward+backward of 1 of {w.B * w.Hq} heads "
+                      f"(N={w.Nq}, d={w.d}, causal), numpy fp64"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of parts to time (default all)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py: --gpus {a.gpus} is not supported; this library and its benchmark "
+              "run on one GPU (the multi-GPU design is described, not built).", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_83_amd as fa
+    from workloads import WORKLOADS, make_inputs
+
+    fa.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    parts = {}
+    only = set(x for x in a.only.split(",") if x)
+
+    # ------------------------------------------------ headline: causal fwd+bwd
+    w = WORKLOADS["causal_bf16"]
+    log(f"inputs {w.name}")
+    x = make_inputs(w, device="cuda")
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_workspace_size(w.B, w.Hq, w.Nq, w.d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    args = (w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    sh = stream.cuda_stream
+
+    def fwd(causal=True):
+        fa.fa_fwd(q, k, v, o, lse, *args, w.scale, causal, sh)
+
+    def bwd_pre():
+        fa.fa_bwd_pre(o, do, ws, ws_bytes, w.B, w.Hq, w.Nq, w.d, sh)
+
+    def bwd_main():
+        fa.fa_bwd_main(q, k, v, do, lse, dk, dv, ws, ws_bytes, *args, w.scale, True, sh)
+
+    def bwd_post():
+        fa.fa_bwd_post(ws, ws_bytes, dq, w.B, w.Hq, w.Nq, w.d, sh)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    log("warmup")
+    for _ in range(a.warmup):
+        fwd(); bwd_pre(); bwd_main(); bwd_post()
+    torch.cuda.synchronize()
+    marks = [(ev(), ev(), ev(), ev()) for _ in range(a.steps)]
+    t_start, t_end = ev(), ev()
+    log(f"timing {a.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for f0, f1, m0, m1 in marks:
+        f0.record(stream)
+        fwd()
+        f1.record(stream)
+        bwd_pre()
+        m0.record(stream)
+        bwd_main()
+        m1.record(stream)
+        bwd_post()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / a.steps
+    fwd_ms = sum(f0.elapsed_time(f1) for f0, f1, _, _ in marks) / a.steps
+    main_ms = sum(m0.elapsed_time(m1) for _, _, m0, m1 in marks) / a.steps
+    step_flops = w.fwd_flops() + w.bwd_flops()
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    fwd_tf = w.fwd_flops() / (fwd_ms * 1e-3) / 1e12
+    main_tf = w.bwd_flops() / (main_ms * 1e-3) / 1e12
+    bwd_ms = ms_step - fwd_ms
+    parts["fwd_causal"] = {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 1),
+                           "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)}
+    parts["bwd_causal"] = {"ms": round(bwd_ms, 4), "main_kernel_ms": round(main_ms, 4),
+                           "tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
+                           "frac_peak": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
+                                              / PEAK_BF16_TFLOPS, 4)}
+    log(f"step {ms_step:.3f} ms: fwd {fwd_ms:.3f} ms ({fwd_tf:.0f} TF), bwd main {main_ms:.3f} ms "
+        f"({main_tf:.0f} TF)")
+
+    iters = max(5, a.steps)
+    if not only or "fwd" in only:
+        t = timed(lambda: fwd(False), iters, stream)
+        tf = 2 * w.fwd_flops() / (t * 1e-3) / 1e12
+        parts["fwd_noncausal"] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                                  "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"fwd non-causal {t:.3f} ms {tf:.0f} TF")
+    del x, q, k, v, do, o, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+
+    if not only or "prefill" in only:
+        wp = WORKLOADS["prefill_bf16"]
+        xp = make_inputs(wp, device="cuda")
+        op = torch.empty_like(xp["q"])
+        lp = torch.empty(wp.B, wp.Hq, wp.Nq, dtype=torch.float32, device="cuda")
+        f = lambda: fa.fa_fwd(xp["q"], xp["k"], xp["v"], op, lp, wp.B, wp.Hq, wp.Hkv, wp.Nq,
+                              wp.Nk, wp.d, wp.scale, False, sh)
+        f()
+        t = timed(f, iters, stream)
+        tf = wp.fwd_flops() / (t * 1e-3) / 1e12
+        parts["fwd_prefill_d64"] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                                    "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"prefill d=64 {t:.3f} ms {tf:.0f} TF")
+        del xp, op, lp
+
+    if not only or "decode" in only:
+        wd = WORKLOADS["decode_gqa"]
+        log("decode inputs")
+        xd = make_inputs(wd, device="cuda")
+        S = wd.num_splits
+        od = torch.empty_like(xd["q"])
+        ld = torch.empty(wd.B, wd.Hq, 1, dtype=torch.float32, device="cuda")
+        opart = torch.empty(wd.B, wd.Hq, S, wd.d, dtype=torch.float32, device="cuda")
+        lpart = torch.empty(wd.B, wd.Hq, S, dtype=torch.float32, device="cuda")
+
+        def split():
+            fa.fa_decode_splitkv(xd["q"], xd["k"], xd["v"], opart, lpart, wd.B, wd.Hq, wd.Hkv,
+                                 wd.Nk, wd.d, wd.scale, S, sh)
+
+        def combine():
+            fa.fa_decode_combine(opart, lpart, od, ld, wd.B, wd.Hq, wd.d, S, sh)
+
+        split(); combine()
+        t_all = timed(lambda: (split(), combine()), iters, stream)
+        t_split = timed(split, iters, stream)
+        t_comb = timed(combine, iters, stream)
+        nbytes = 2 * wd.B * wd.Hkv * wd.Nk * wd.d * 2 + 2 * wd.B * wd.Hq * wd.d * 2 + wd.B * wd.Hq * 4
+        gbs = nbytes / (t_all * 1e-3) / 1e9
+        parts["decode"] = {"ms": round(t_all, 4), "split_ms": round(t_split, 4),
+                           "combine_ms": round(t_comb, 4), "algorithmic_bytes": nbytes,
+                           "GB/s": round(gbs, 1), "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
+                           "split_GB/s": round(nbytes / (t_split * 1e-3) / 1e9, 1)}
+        log(f"decode {t_all:.3f} ms {gbs:.0f} GB/s (split {t_split:.3f} ms)")
+        del xd, od, ld, opart, lpart
+
+    if not only or "fp8" in only:
+        wf = WORKLOADS["fp8_fwd"]
+        log("fp8 inputs")
+        xf = make_inputs(wf, device="cuda")
+        q8, qs = fa.quantize_fp8(xf["q"], xf["signs"])
+        k8, ks = fa.quantize_fp8(xf["k"], xf["signs"])
+        v8, vs = fa.quantize_fp8(xf["v"], None)
+        of = torch.empty_like(xf["q"])
+        lf = torch.empty(wf.B, wf.Hq, wf.Nq, dtype=torch.float32, device="cuda")
+
+        def quant():
+            fa.fa_quantize_fp8(xf["q"], xf["signs"], q8, qs, wf.B, wf.Hq, wf.Nq, wf.d, sh)
+            fa.fa_quantize_fp8(xf["k"], xf["signs"], k8, ks, wf.B, wf.Hkv, wf.Nk, wf.d, sh)
+            fa.fa_quantize_fp8(xf["v"], None, v8, vs, wf.B, wf.Hkv, wf.Nk, wf.d, sh)
+
+        def f8():
+            fa.fa_fwd_fp8(q8, k8, v8, qs, ks, vs, of, lf, wf.B, wf.Hq, wf.Hkv, wf.Nq, wf.Nk,
+                          wf.d, wf.scale, False, sh)
+
+        f8()
+        t = timed(f8, iters, stream)
+        tq = timed(quant, iters, stream)
+        tf = wf.fwd_flops() / (t * 1e-3) / 1e12
+        qbytes = 3 * wf.B * wf.Hq * wf.Nq * wf.d * (2 + 1)
+        parts["fp8_fwd"] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                            "frac_peak_fp8": round(tf / PEAK_FP8_TFLOPS, 4),
+                            "quant_ms": round(tq, 4),
+                            "quant_GB/s": round(qbytes / (tq * 1e-3) / 1e9, 1),
+                            "tflops_incl_quant": round(wf.fwd_flops() / ((t + tq) * 1e-3) / 1e12, 1)}
+        log(f"fp8 fwd {t:.3f} ms {tf:.0f} TF, quant {tq:.3f} ms")
+        del xf
+
+    result = {
+        "metric": "attention TFLOPS (fwd, bwd) bf16 N=8K d=128 as % MFMA peak; decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal_bf16 forward+backward", "B": w.B, "H": w.Hq,
+                   "seq_len": w.Nq, "head_dim": w.d, "causal": True,
+                   "flops_per_step": step_flops, "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+                   "wall_s": round(wall, 3)},
+        "roofline": {"kernel": "bwd_bf16_kernel<128,causal> (fa_bwd_main)", "bound": "mfma",
+                     "achieved": round(main_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(main_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": w.bwd_flops(),
+                     "avg_launch_ms": round(main_ms, 4)},
+        "parts": parts,
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,231 @@
+// C ABI of the attention library: argument validation and dispatch to the
+// gfx950 kernels.  Every check runs before anything is enqueued, so an invalid
+// call leaves the stream untouched.
+
+#include "../../include/fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// Shape checks shared by the attention entry points.
+fa_status check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  // element offsets are formed in 64-bit, per-(b,h) row counts in 32-bit
+  if ((int64_t)B * Hq > (1 << 24) || (int64_t)B * Hkv > (1 << 24)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                 int Hkv, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  return hip_status(
+      fa::launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream));
+}
+
+fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                     hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  return hip_status(
+      fa::launch_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, scale, causal != 0, stream));
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || d <= 0) return 0;
+  const size_t rows = (size_t)B * Hq * Nq;
+  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+static fa_status bwd_common(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, const void* dq, const void* dk,
+                            const void* dv, void* ws, size_t ws_bytes, int B, int Hq, int Hkv,
+                            int Nq, int Nk, int d, float scale, int causal) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  if (ws == nullptr || !aligned16(ws)) return FA_ERR_WORKSPACE;
+  if (ws_bytes < fa_bwd_workspace_size(B, Hq, Nq, d)) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+static float* ws_delta(void* ws, int B, int Hq, int Nq, int d) {
+  const size_t rows = (size_t)B * Hq * Nq;
+  return reinterpret_cast<float*>(static_cast<char*>(ws) + round256(rows * d * sizeof(float)));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, hipStream_t stream) {
+  if (fa_status s = bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
+                               Hq, Hkv, Nq, Nk, d, scale, causal))
+    return s;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  float* dq_accum = static_cast<float*>(workspace);
+  float* delta = ws_delta(workspace, B, Hq, Nq, d);
+  hipError_t e = fa::launch_bwd_pre(o, dout, dq_accum, delta, B, Hq, Nq, d, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_main(q, k, v, dout, lse, delta, dq_accum, dk, dv, B, Hq, Hkv, Nq, Nk, d,
+                            scale, causal != 0, stream);
+  if (e == hipSuccess) e = fa::launch_bwd_post(dq_accum, dq, B, Hq, Nq, d, stream);
+  return hip_status(e);
+}
+
+fa_status fa_bwd_pre(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
+                     int B, int Hq, int Nq, int d, hipStream_t stream) {
+  if (!aligned16(o) || !aligned16(dout)) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < fa_bwd_workspace_size(B, Hq, Nq, d)) return FA_ERR_WORKSPACE;
+  return hip_status(fa::launch_bwd_pre(o, dout, static_cast<float*>(workspace),
+                                       ws_delta(workspace, B, Hq, Nq, d), B, Hq, Nq, d, stream));
+}
+
+fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      float scale, int causal, hipStream_t stream) {
+  // o and dq are not touched by this stage; q stands in for them in the checks
+  if (fa_status s = bwd_common(q, k, v, q, dout, lse, q, dk, dv, workspace, workspace_bytes, B,
+                               Hq, Hkv, Nq, Nk, d, scale, causal))
+    return s;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_bwd_main(q, k, v, dout, lse, ws_delta(workspace, B, Hq, Nq, d),
+                                        static_cast<float*>(workspace), dk, dv, B, Hq, Hkv, Nq,
+                                        Nk, d, scale, causal != 0, stream));
+}
+
+fa_status fa_bwd_post(const void* workspace, size_t workspace_bytes, void* dq, int B, int Hq,
+                      int Nq, int d, hipStream_t stream) {
+  if (!aligned16(dq)) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < fa_bwd_workspace_size(B, Hq, Nq, d)) return FA_ERR_WORKSPACE;
+  return hip_status(
+      fa::launch_bwd_post(static_cast<const float*>(workspace), dq, B, Hq, Nq, d, stream));
+}
+
+fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                     const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                     int Nk, int d, float scale, int causal, hipStream_t stream) {
+  if (fa_status s = bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
+                               Hq, Hkv, Nq, Nk, d, scale, causal))
+    return s;
+  if (d != 64) return FA_ERR_UNSUPPORTED;
+  float* delta = ws_delta(workspace, B, Hq, Nq, d);
+  return hip_status(fa::launch_bwd_f32(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq,
+                                       Nk, scale, causal != 0, stream));
+}
+
+size_t fa_decode_workspace_size(int B, int Hq, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)B * Hq * num_splits;
+  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* o_part,
+                            float* lse_part, int B, int Hq, int Hkv, int Nk, int d, float scale,
+                            int num_splits, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) ||
+      !aligned16(lse_part))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, 1, Nk, d)) return s;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (num_splits <= 0 || num_splits > Nk || Nk % num_splits != 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 32) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv * num_splits > (int64_t)1 << 30) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_decode_split(q, k, v, o_part, lse_part, B, Hq, Hkv, Nk, d, scale,
+                                            num_splits, stream));
+}
+
+fa_status fa_decode_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                            int B, int Hq, int d, int num_splits, hipStream_t stream) {
+  if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 0) return FA_ERR_INVALID_ARG;
+  if (d > 256) return FA_ERR_UNSUPPORTED;
+  return hip_status(
+      fa::launch_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream));
+}
+
+fa_status fa_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float* scales, int B,
+                          int H, int N, int d, hipStream_t stream) {
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(scales)) return FA_ERR_INVALID_ARG;
+  if (signs != nullptr && !aligned16(signs)) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_quantize_fp8(x, signs, x8, scales, B, H, N, d, stream));
+}
+
+fa_status fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                     const float* q_scale, const float* k_scale, const float* v_scale, void* o,
+                     float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                     int causal, hipStream_t stream) {
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(q_scale) ||
+      !aligned16(k_scale) || !aligned16(v_scale) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv,
+                                       Nq, Nk, d, scale, causal != 0, stream));
+}
+
+int fa_fwd_schedule(int B, int Hq, int Nq, int Nk, int d, int causal, int* bh_out,
+                    int* qtile_out, int* cost_out, int capacity) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return -1;
+  if (causal && Nq != Nk) return -1;
+  return fa::fwd_schedule(B, Hq, Nq, Nk, causal != 0, bh_out, qtile_out, cost_out, capacity);
+}
+
+}  // extern "C"

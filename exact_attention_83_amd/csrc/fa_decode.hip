@@ -1,0 +1,277 @@
+// Split-KV decode and its combine step for gfx950.
+//
+// Method: [CH18] "第 18 章 FlashAttention" §18.8.2 (Flash-Decoding: cut the KV
+// length into chunks handled in parallel, then merge the partial softmax
+// statistics with the online-softmax formula) and [L21] "CMU 11-868 L21
+// FlashAttention" slides 57-60 (GQA packing: the query heads that share one KV
+// head fill the rows of one tile, so K and V are streamed once per group).
+//
+// Split kernel, one workgroup (4 waves) per (b, KV head, chunk):
+//   * the G = Hq/Hkv query heads of the group are the n axis of S^T = K Q^T on
+//     the 32x32x16 MFMA (n = 32 >= G; columns past G hold zero queries).
+//   * each wave streams 32-key blocks of the chunk (blocks w, w+4, ...): K
+//     goes from global memory straight into A-operand registers (each lane
+//     reads 128 contiguous bytes of one key row; the head-dim order inside a
+//     k-step is permuted identically in Q), V goes through a per-wave LDS
+//     region where it is stored transposed for O^T += V^T P^T.
+//   * the next block's loads are issued before the current block's math.
+//   * the 4 waves' (max, sum, O) are merged in LDS and the chunk's normalised
+//     output and logsumexp are written.
+// The work is bound by HBM reads of K and V (about 4 FLOP per byte); MFMA
+// waste on the padded n axis costs nothing that matters.
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+constexpr int kDecWaves = 4;
+constexpr int kDecBlk = 32;  // keys per wave iteration
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, float* __restrict__ o_part, float* __restrict__ lse_part,
+    int Hq, int Hkv, int Nk, int num_splits, float scale, float scale_log2) {
+  constexpr int KS = D / 16;      // k-steps over the head dim
+  constexpr int DBLK = D / 32;
+  constexpr int DCH = D / 8;      // 16-byte chunks per row
+  constexpr int HALF = D / 2;     // head dims per lane half for K loads
+  constexpr int VP = kDecBlk * 2 + 8;           // V^T pitch (bytes)
+  constexpr int VREG = kDecBlk * D / 8 / 64;    // 16-byte V chunks per lane
+  constexpr int KREG = KS;                      // 16-byte K chunks per lane
+  __shared__ __attribute__((aligned(16))) char vt_all[kDecWaves * D * VP];
+  __shared__ float red_m[kDecWaves][32];
+  __shared__ float red_l[kDecWaves][32];
+  __shared__ float red_o[32][D + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int G = Hq / Hkv;
+
+  const int c = blockIdx.x % num_splits;
+  const int bhk = blockIdx.x / num_splits;
+  const int b = bhk / Hkv;
+  const int hk = bhk - b * Hkv;
+  const int L = Nk / num_splits;
+  const int key_begin = c * L;
+  const int key_end = key_begin + L;
+
+  const uint16_t* Kp = K + (size_t)bhk * Nk * D;
+  const uint16_t* Vp = V + (size_t)bhk * Nk * D;
+  char* vt = vt_all + wave * D * VP;
+
+  // Q^T B operand: column n = l32 is query head hk*G + l32 (zero past G).
+  // k-step ks, element i of lane half hf is head dim hf*HALF + ks*8 + i.
+  u32x4 qf[KS];
+  {
+    const bool valid = l32 < G;
+    const uint16_t* qp = Q + ((size_t)b * Hq + hk * G + (valid ? l32 : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 x = ldg<u32x4>(qp + hf * HALF + ks * 8);
+      qf[ks] = valid ? x : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  const int nblk = (L + kDecBlk - 1) / kDecBlk;
+  u32x4 kreg[KREG], vreg[VREG];
+  // V staging: lane -> 4 consecutive keys (group l/DCH) x 8 head dims.
+  const int v_grp = lane / DCH;
+  const int v_col = lane - v_grp * DCH;
+  constexpr int VGRP_PER_ROUND = 64 / DCH;  // key groups covered per round
+
+  auto load_blk = [&](int blk) {
+    const int k0 = key_begin + blk * kDecBlk;
+    int key = k0 + l32;
+    key = key < key_end ? key : key_end - 1;
+    const uint16_t* kr = Kp + (size_t)key * D + hf * HALF;
+#pragma unroll
+    for (int i = 0; i < KREG; ++i) kreg[i] = ldg<u32x4>(kr + i * 8);
+#pragma unroll
+    for (int i = 0; i < VREG; ++i) {
+      const int round = i / 4;
+      int vk = k0 + (round * VGRP_PER_ROUND + v_grp) * 4 + (i & 3);
+      vk = vk < key_end ? vk : key_end - 1;
+      vreg[i] = ldg<u32x4>(Vp + (size_t)vk * D + v_col * 8);
+    }
+  };
+
+  f32x16 o[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{0};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  int blk = wave;
+  if (blk < nblk) load_blk(blk);
+  for (; blk < nblk; blk += kDecWaves) {
+    // V block -> LDS transposed ([d][key]) as 8-byte runs of 4 keys.
+#pragma unroll
+    for (int rd = 0; rd < VREG / 4; ++rd)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const u32x4* r = vreg + rd * 4;
+        uint32_t lo = (e & 1) ? pack_hi16(r[0][w], r[1][w]) : pack_lo16(r[0][w], r[1][w]);
+        uint32_t hi = (e & 1) ? pack_hi16(r[2][w], r[3][w]) : pack_lo16(r[2][w], r[3][w]);
+        lds_write<u32x2>(vt, (v_col * 8 + e) * VP + ((rd * VGRP_PER_ROUND + v_grp) * 4) * 2,
+                         u32x2{lo, hi});
+      }
+    f32x16 s = f32x16{0};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = mfma_32x32x16_bf16(kreg[ks], qf[ks], s);
+
+    const int k0 = key_begin + blk * kDecBlk;
+    if (blk + kDecWaves < nblk) load_blk(blk + kDecWaves);
+
+    if (k0 + kDecBlk > key_end) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k0 + 8 * (r >> 2) + 4 * hf + (r & 3) >= key_end) s[r] = -INFINITY;
+    }
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    mt = fmaxf(mt, xor32(mt));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2((m_run - m_ref) * scale_log2);
+    const float mb = m_ref * scale_log2;
+    m_run = m_new;
+    float p[16], psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = fast_exp2(fmaf(s[r], scale_log2, -mb));
+      psum += p[r];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+    u32x4 pb[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      pb[st] = u32x4{pack_bf16(p[8 * st + 0], p[8 * st + 1]), pack_bf16(p[8 * st + 2], p[8 * st + 3]),
+                     pack_bf16(p[8 * st + 4], p[8 * st + 5]), pack_bf16(p[8 * st + 6], p[8 * st + 7])};
+
+    // The V^T region was written by other lanes of this wave.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int off = (db * 32 + l32) * VP + (st * 16 + hf * 4) * 2;
+        u32x2 a0 = lds_read<u32x2>(vt, off);
+        u32x2 a1 = lds_read<u32x2>(vt, off + 16);
+        o[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[st], o[db]);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // Merge the four waves.  Lane (l32, hf) holds head column l32 and head dims
+  // 32*db + 8*(r/4) + 4*hf + r%4.  Each wave rescales its partial output to
+  // the merged max and sum, then the waves add into one LDS buffer in a fixed
+  // order (deterministic).
+  const float l_tot = l_run + xor32(l_run);
+  if (l32 < G && hf == 0) {
+    red_m[wave][l32] = m_run;
+    red_l[wave][l32] = l_tot;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  float Lsum = 0.f;
+  if (l32 < G) {
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_m[w][l32]);
+    const float Mr = M == -INFINITY ? 0.f : M;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w)
+      Lsum += red_l[w][l32] * fast_exp2((red_m[w][l32] - Mr) * scale_log2);
+    const float f = fast_exp2((m_run - Mr) * scale_log2) / Lsum;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[db] *= f;
+  }
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    if (wave == w && l32 < G) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float* dst = &red_o[l32][db * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)];
+          *dst = (w == 0) ? o[db][r] : *dst + o[db][r];
+        }
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int g = idx / D, dd = idx - (idx / D) * D;
+    const size_t row = ((size_t)b * Hq + hk * G + g) * num_splits + c;
+    o_part[row * D + dd] = red_o[g][dd];
+  }
+  if (wave == 0 && hf == 0 && l32 < G) {
+    const size_t row = ((size_t)b * Hq + hk * G + l32) * num_splits + c;
+    lse_part[row] = M * scale + __logf(Lsum);
+  }
+}
+
+// Combine: one wave per (b, hq); lane handles head dims lane, lane+64, ...
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ o_part,
+                                                            const float* __restrict__ lse_part,
+                                                            uint16_t* __restrict__ O,
+                                                            float* __restrict__ LSE, int d,
+                                                            int S) {
+  const int row = blockIdx.x;  // b*Hq + hq
+  const int lane = threadIdx.x;
+  const float* lp = lse_part + (size_t)row * S;
+  float M = -INFINITY;
+  for (int c = lane; c < S; c += 64) M = fmaxf(M, lp[c]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  const float Mr = M == -INFINITY ? 0.f : M;
+  float z = 0.f;
+  for (int c = lane; c < S; c += 64) z += __expf(lp[c] - Mr);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
+  const float lse = Mr + __logf(z);
+  for (int dd = lane; dd < d; dd += 64) {
+    float acc = 0.f;
+    for (int c = 0; c < S; ++c) acc += __expf(lp[c] - lse) * o_part[((size_t)row * S + c) * d + dd];
+    O[(size_t)row * d + dd] = (uint16_t)(pack_bf16(acc, 0.f) & 0xffff);
+  }
+  if (lane == 0) LSE[row] = lse;
+}
+
+hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
+                               float* lse_part, int B, int Hq, int Hkv, int Nk, int d,
+                               float scale, int num_splits, hipStream_t stream) {
+  dim3 grid(B * Hkv * num_splits), block(256);
+  const float sl2 = scale * kLog2e;
+  if (d == 128)
+    hipLaunchKernelGGL((decode_split_kernel<128>), grid, block, 0, stream, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, Hq, Hkv, Nk,
+                       num_splits, scale, sl2);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<64>), grid, block, 0, stream, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, Hq, Hkv, Nk,
+                       num_splits, scale, sl2);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o,
+                                 float* lse, int B, int Hq, int d, int num_splits,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(64), 0, stream, o_part, lse_part,
+                     (uint16_t*)o, lse, d, num_splits);
+  return hipGetLastError();
+}
+
+}  // namespace fa

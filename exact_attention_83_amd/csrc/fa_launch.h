@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).  Each
+// returns the HIP status of its launches; arguments are validated by the C ABI
+// layer before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                           bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int Hq, int Hkv, int Nq, int Nk, float scale, bool causal,
+                          hipStream_t stream);
+int fwd_schedule(int B, int Hq, int Nq, int Nk, bool causal, int* bh_out, int* qt_out,
+                 int* cost_out, int capacity);
+
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                          float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
+                          bool causal, hipStream_t stream);
+hipError_t launch_bwd_pre(const void* o, const void* dout, float* dq_accum, float* delta, int B,
+                          int Hq, int Nq, int d, hipStream_t stream);
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                           const float* lse, const float* delta, float* dq_accum, void* dk,
+                           void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                           bool causal, hipStream_t stream);
+hipError_t launch_bwd_post(const float* dq_accum, void* dq, int B, int Hq, int Nq, int d,
+                           hipStream_t stream);
+
+hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
+                               float* lse_part, int B, int Hq, int Hkv, int Nk, int d,
+                               float scale, int num_splits, hipStream_t stream);
+hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o,
+                                 float* lse, int B, int Hq, int d, int num_splits,
+                                 hipStream_t stream);
+
+hipError_t launch_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float* scales,
+                               int B, int H, int N, int d, hipStream_t stream);
+hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                          const float* qs, const float* ks, const float* vs, void* o,
+                          float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                          float scale, bool causal, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,217 @@
+/*
+ * fa.h -- C ABI of the exact-attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T + M) V
+ * the FlashAttention way: Q and K/V are split into tiles, a running row max and
+ * row sum rescale the partial output (online softmax), and the N x N score
+ * matrix never reaches device memory.  The forward stores only the per-row
+ * logsumexp; the backward recomputes the scores from it.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [CH18] "第 18 章 FlashAttention" (AI algorithm guide, theaiera.top)
+ *   [L21]  "CMU 11-868 L21 FlashAttention" lecture digest (quidproquo.cc)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are device pointers to contiguous row-major [B][H][N][d] arrays
+ *     ("BHSD"): element (b,h,n,c) sits at ((b*H + h)*N + n)*d + c.
+ *   - bf16 tensors are IEEE bfloat16 stored as 16-bit words; fp32 tensors are
+ *     float.  Every tensor pointer must be 16-byte aligned.
+ *   - Grouped-query attention: Hq must be a multiple of Hkv and query head hq
+ *     reads KV head hq / (Hq / Hkv)  ([CH18] §18.2.2).
+ *   - scale multiplies Q K^T; it must be finite and > 0 (the usual value is
+ *     1/sqrt(d)).
+ *   - causal: key j is visible to query i iff j <= i ([CH18] §18.2.2 item 3);
+ *     it requires Nq == Nk.
+ *   - lse is fp32 [B][Hq][Nq]: lse_i = ln sum_j exp(scale * q_i . k_j) over the
+ *     visible keys (natural log).
+ *   - Ownership: the caller allocates and owns every buffer, workspaces
+ *     included.  The library allocates no device memory and keeps no mutable
+ *     global state, so concurrent calls on different streams are safe.
+ *   - Calls are asynchronous on `stream`.  Argument errors are detected before
+ *     anything is enqueued and return FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or
+ *     FA_ERR_WORKSPACE; a failed kernel launch returns FA_ERR_HIP.  Faults in a
+ *     running kernel surface at the caller's next synchronisation.
+ *   - Outputs are overwritten, never accumulated into.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, bad scale */
+  FA_ERR_UNSUPPORTED = 2, /* valid but not implemented: head dim, causal Nq != Nk */
+  FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size */
+  FA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} fa_status;
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+/*
+ * Forward, bf16.  [CH18] §18.4.3 (tiled forward with online softmax, Fig.
+ * 18-16), §18.5.2 (causal tile skipping); [L21] slides 9-12.
+ *   q [B][Hq][Nq][d], k,v [B][Hkv][Nk][d], o [B][Hq][Nq][d]: bf16.
+ *   lse [B][Hq][Nq]: fp32.
+ *   d in {64, 128}.  Softmax and accumulation are fp32; O is rounded to
+ *   bf16 (nearest-even).
+ * Query tiles are launched longest-first (causal) so the hardware dispatcher
+ * hands the largest remaining work to the next free compute unit ([L21]
+ * slides 27-46).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, hipStream_t stream);
+
+/*
+ * Forward, fp32 in and out (same layout and meaning as fa_fwd).  d == 64.
+ * Query and key tiles are 64 rows, so Nk = 256 exercises four rounds of
+ * online rescaling.
+ */
+fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, hipStream_t stream);
+
+/*
+ * Bytes of workspace fa_bwd / fa_bwd_f32 need: an fp32 dQ accumulator
+ * [B][Hq][Nq][d] and the fp32 row term delta [B][Hq][Nq], each rounded up to
+ * 256 bytes.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
+
+/*
+ * Backward, bf16.  [CH18] §18.2.4 (gradients of attention), §18.4.4
+ * (recomputation: P is rebuilt from the saved logsumexp, no rescaling).
+ *   q,k,v,o,dout: bf16, o and lse as written by fa_fwd for the same inputs.
+ *   dq [B][Hq][Nq][d], dk,dv [B][Hkv][Nk][d]: bf16 outputs.  A KV head's
+ *   gradient is summed over the query heads of its group.
+ *   workspace: at least fa_bwd_workspace_size(B,Hq,Nq,d) bytes, 16-byte
+ *   aligned; its contents on entry do not matter.
+ * Three launches on `stream`: delta_i = dO_i . O_i (equal to rowsum(P * dP),
+ * [CH18] §18.4.4) together with zeroing of the dQ accumulator; the main
+ * kernel, one work unit per KV tile, which accumulates dK, dV on chip and adds
+ * dQ into the fp32 accumulator with atomics; and the dQ conversion to bf16.
+ * dQ is therefore reproducible only up to fp32 rounding order.
+ *   d == 128 (and 64).
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, hipStream_t stream);
+
+/*
+ * The three stages of fa_bwd as separate calls, for callers that schedule or
+ * time them individually.  Same arguments and workspace as fa_bwd; running
+ * fa_bwd_pre, fa_bwd_main and fa_bwd_post in that order on one stream is
+ * exactly fa_bwd.
+ *   fa_bwd_pre:  delta_i = dO_i . O_i into the workspace and zeroing of the
+ *                fp32 dQ accumulator ([CH18] §18.4.4: the row term of the
+ *                softmax backward, rowsum(P * dP), equals dO_i . O_i).
+ *   fa_bwd_main: dK, dV written; dQ accumulated (fp32) into the workspace.
+ *   fa_bwd_post: dQ accumulator -> dq (bf16, nearest-even).
+ */
+fa_status fa_bwd_pre(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
+                     int B, int Hq, int Nq, int d, hipStream_t stream);
+fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      float scale, int causal, hipStream_t stream);
+fa_status fa_bwd_post(const void* workspace, size_t workspace_bytes, void* dq, int B, int Hq,
+                      int Nq, int d, hipStream_t stream);
+
+/* Backward, fp32 tensors, d == 64.  Same meaning as fa_bwd; deterministic. */
+fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                     const float* dout, const float* lse,
+                     float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, hipStream_t stream);
+
+/*
+ * Split-KV decode ([CH18] §18.8.2, Flash-Decoding; [L21] slides 57-60, GQA
+ * packing).  One query position per (b, hq) attends all Nk keys, non-causal.
+ * The key range is cut into num_splits equal chunks; each work unit handles
+ * one chunk for one (b, KV head) and packs the Hq/Hkv query heads that share
+ * the KV head into the rows of one tile, so K and V are read once per group.
+ *   q [B][Hq][1][d] bf16; k,v [B][Hkv][Nk][d] bf16.
+ *   o_part [B][Hq][num_splits][d] fp32: each chunk's softmax-normalised
+ *   partial output.  lse_part [B][Hq][num_splits] fp32: each chunk's
+ *   logsumexp.
+ * Requirements: num_splits >= 1 divides Nk; d == 128 (and 64);
+ * Hq/Hkv <= 32.
+ */
+fa_status fa_decode_splitkv(const void* q, const void* k, const void* v,
+                            float* o_part, float* lse_part,
+                            int B, int Hq, int Hkv, int Nk, int d,
+                            float scale, int num_splits, hipStream_t stream);
+
+/*
+ * Merge of the split partials ([CH18] §18.8.2 (2), reduction step):
+ *   lse = M + ln sum_c exp(lse_c - M) with M = max_c lse_c,
+ *   O   = sum_c exp(lse_c - lse) * O_c.
+ *   o [B][Hq][1][d] bf16, lse [B][Hq][1] fp32.  d <= 256.
+ */
+fa_status fa_decode_combine(const float* o_part, const float* lse_part,
+                            void* o, float* lse,
+                            int B, int Hq, int d, int num_splits, hipStream_t stream);
+
+/* Bytes the caller must provide for o_part and lse_part together (one
+ * allocation: o_part first, lse_part at the next 256-byte boundary). */
+size_t fa_decode_workspace_size(int B, int Hq, int d, int num_splits);
+
+/*
+ * FP8 quantisation pre-pass ([CH18] §18.6.2 (1)(2); [L21] slide 24).
+ *   x [B][H][N][d] bf16 in; x8 [B][H][N][d] e4m3fn codes out (1 byte each);
+ *   scales [B][H][ceil(N/128)] fp32 out.
+ *   signs: device int8[d] of +-1, or NULL.  When given, every row is first
+ *   rotated by J = diag(signs) * Hadamard(d) / sqrt(d) (incoherent
+ *   processing: applied to Q and K with the same signs, (QJ)(KJ)^T = QK^T).
+ *   Each (b, h, 128-row block) gets amax = max |x|, r = fp32(448 / amax),
+ *   codes = e4m3(fp32(x * r)) rounded to nearest-even and saturated to +-448,
+ *   scale = fp32(amax / 448) (1 for an all-zero block).
+ *   d == 128.
+ */
+fa_status fa_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float* scales,
+                          int B, int H, int N, int d, hipStream_t stream);
+
+/*
+ * FP8 forward: fa_fwd on e4m3 operands with per-128-row-block fp32 scales
+ * (from fa_quantize_fp8).  S = (Q8 K8^T) * s_q * s_k * scale; softmax in
+ * fp32; P is rounded to e4m3 for the P V product; O is bf16, lse fp32.
+ *   q8 [B][Hq][Nq][d], k8,v8 [B][Hkv][Nk][d]; q_scale [B][Hq][ceil(Nq/128)],
+ *   k_scale, v_scale [B][Hkv][ceil(Nk/128)].  d == 128.
+ */
+fa_status fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                     const float* q_scale, const float* k_scale, const float* v_scale,
+                     void* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, hipStream_t stream);
+
+/*
+ * Host-side view of the forward's work order ([L21] slides 27-46: longest
+ * processing time first).  Writes, for each of the n work units the forward
+ * launches in dispatch order, its (b*Hq + h) index, its query-tile index and
+ * its cost in KV tiles.  Returns the number of work units, or -1 on bad
+ * arguments; with NULL outputs only the count is returned.  No GPU is needed.
+ */
+int fa_fwd_schedule(int B, int Hq, int Nq, int Nk, int d, int causal,
+                    int* bh_out, int* qtile_out, int* cost_out, int capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,311 @@
+"""Parity of the HIP path against the fp64 oracle, element by element, on the
+same seeded inputs.  Every call goes through the C ABI (ctypes binding).
+
+Tolerances (from the benchmark spec of the problem):
+  bf16, fp32 accumulation: O max-abs <= 1e-2, LSE max-abs <= 1e-3,
+                           dQ/dK/dV relative L2 <= 1e-2
+  fp32 tiny configuration: all of the above <= 1e-5
+  fp8 forward:             relative L2 of O <= 5e-2 against the oracle fed the
+                           dequantised operands the kernel receives
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import fp8 as F8
+from tests.conftest import say
+from workloads import WORKLOADS, make_inputs, to_f64
+
+pytestmark = pytest.mark.gpu
+
+BF16_O, BF16_LSE, BF16_GRAD = 1e-2, 1e-3, 1e-2
+F32_TOL = 1e-5
+FP8_REL = 5e-2
+
+
+def maxabs(a, b):
+    return float(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).max())
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def gen(B, Hq, Hkv, Nq, Nk, d, dtype, seed, grad=False):
+    g = torch.Generator("cpu").manual_seed(seed)
+    t = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = torch.randn(B, Hq, Nq, d, generator=g).to(t)
+    k = torch.randn(B, Hkv, Nk, d, generator=g).to(t)
+    v = torch.randn(B, Hkv, Nk, d, generator=g).to(t)
+    out = {"q": q.cuda(), "k": k.cuda(), "v": v.cuda()}
+    if grad:
+        out["do"] = torch.randn(B, Hq, Nq, d, generator=g).to(t).cuda()
+    return out
+
+
+# ------------------------------------------------------------------ forward
+
+def check_forward(fa, x, causal, o_tol, lse_tol, label):
+    q, k, v = x["q"], x["k"], x["v"]
+    d = q.shape[-1]
+    say(f"forward {label} shape={tuple(q.shape)} kv={tuple(k.shape)} causal={causal}")
+    o, lse = fa.forward(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.forward(to_f64(q), to_f64(k), to_f64(v), 1 / math.sqrt(d), causal)
+    eo, el = maxabs(to_f64(o), o_ref), maxabs(to_f64(lse), lse_ref)
+    assert eo <= o_tol and el <= lse_tol, (label, eo, el)
+    return o, lse
+
+
+def test_tiny_f32_config(fa_gpu):
+    """fp32 B=1 H=1 N=256 d=64: 64-row tiles, four KV blocks of rescaling."""
+    w = WORKLOADS["tiny_f32"]
+    x = make_inputs(w)
+    x = {n: t.cuda() for n, t in x.items()}
+    o, lse = check_forward(fa_gpu, x, False, F32_TOL, F32_TOL, "tiny_f32")
+    say("backward tiny_f32")
+    dq, dk, dv = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=False)
+    torch.cuda.synchronize()
+    ref = A.backward(*(to_f64(x[n]) for n in ("q", "k", "v", "do")), w.scale, False)
+    for got, want in zip((dq, dk, dv), ref):
+        assert rel_l2(to_f64(got), want) <= F32_TOL
+
+
+@pytest.mark.parametrize("shape,causal", [
+    ((1, 2, 1, 200, 200), True), ((2, 4, 2, 130, 70), False), ((1, 1, 1, 64, 64), True)])
+def test_f32_variants(fa_gpu, shape, causal):
+    B, Hq, Hkv, Nq, Nk = shape
+    x = gen(B, Hq, Hkv, Nq, Nk, 64, "f32", 11, grad=True)
+    o, lse = check_forward(fa_gpu, x, causal, F32_TOL, F32_TOL, f"f32 {shape}")
+    say(f"backward f32 {shape} causal={causal}")
+    grads = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal)
+    torch.cuda.synchronize()
+    ref = A.backward(*(to_f64(x[n]) for n in ("q", "k", "v", "do")), 1 / 8, causal)
+    for got, want in zip(grads, ref):
+        assert rel_l2(to_f64(got), want) <= F32_TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 4, 2, 333, 333), (2, 2, 2, 256, 256), (1, 3, 1, 129, 129)])
+def test_bf16_forward_small(fa_gpu, d, causal, shape):
+    B, Hq, Hkv, Nq, Nk = shape
+    x = gen(B, Hq, Hkv, Nq, Nk, d, "bf16", 21)
+    check_forward(fa_gpu, x, causal, BF16_O, BF16_LSE, f"bf16 d={d}")
+
+
+def test_bf16_forward_cross_lengths(fa_gpu):
+    """Non-causal with Nq != Nk and ragged tails on both sides."""
+    x = gen(1, 2, 1, 77, 1000, 128, "bf16", 22)
+    check_forward(fa_gpu, x, False, BF16_O, BF16_LSE, "Nq=77 Nk=1000")
+
+
+def test_prefill_config(fa_gpu):
+    """bf16 B=4 H=16 N=2048 d=64 non-causal, every output compared."""
+    w = WORKLOADS["prefill_bf16"]
+    x = {n: t.cuda() for n, t in make_inputs(w).items()}
+    check_forward(fa_gpu, x, False, BF16_O, BF16_LSE, "prefill_bf16")
+
+
+# ----------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 2, 256, 256), (1, 4, 2, 300, 300), (2, 1, 1, 129, 129)])
+def test_bf16_backward_small(fa_gpu, d, causal, shape):
+    B, Hq, Hkv, Nq, Nk = shape
+    x = gen(B, Hq, Hkv, Nq, Nk, d, "bf16", 31, grad=True)
+    o, lse = check_forward(fa_gpu, x, causal, BF16_O, BF16_LSE, f"bwd-prep d={d}")
+    say(f"backward bf16 d={d} shape={shape} causal={causal}")
+    grads = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal)
+    torch.cuda.synchronize()
+    ref = A.backward(*(to_f64(x[n]) for n in ("q", "k", "v", "do")), 1 / math.sqrt(d), causal)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        e = rel_l2(to_f64(got), want)
+        assert e <= BF16_GRAD, (name, e)
+
+
+def test_causal_config_sampled(fa_gpu):
+    """bf16 B=2 H=16 N=8192 d=128 causal at full size, in the launch
+    configuration the benchmark times.  Forward: 24 rows of every head
+    (tile edges, the diagonal, first and last rows).  Backward: dQ rows of
+    every head plus complete dK/dV of two heads, from the oracle's per-head
+    materialising backward."""
+    w = WORKLOADS["causal_bf16"]
+    x = {n: t.cuda() for n, t in make_inputs(w).items()}
+    say("forward causal_bf16 full size")
+    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 127, 128, 129, 255, 256, 1000, 2047, 2048, 4095, 4096,
+                     5000, 6143, 6144, 7000, 8000, 8127, 8128, 8190, 8191, 3333])
+    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
+    o_ref, lse_ref = A.forward(q, k, v, w.scale, True, rows=rows)
+    assert maxabs(to_f64(o)[:, :, rows], o_ref) <= BF16_O
+    assert maxabs(to_f64(lse)[:, :, rows], lse_ref) <= BF16_LSE
+
+    say("backward causal_bf16 full size")
+    dq, dk, dv = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=True)
+    torch.cuda.synchronize()
+    do = to_f64(x["do"])
+    dq, dk, dv = to_f64(dq), to_f64(dk), to_f64(dv)
+    for (b, h) in ((0, 0), (1, 15)):
+        rq, rk, rv, _ = A.head_backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, True)
+        for name, got, want in (("dq", dq[b, h], rq), ("dk", dk[b, h], rk), ("dv", dv[b, h], rv)):
+            e = rel_l2(got, want)
+            assert e <= BF16_GRAD, (b, h, name, e)
+
+
+# ------------------------------------------------------------------- decode
+
+def check_decode(fa, B, Hq, Hkv, Nk, d, splits, seed):
+    x = gen(B, Hq, Hkv, 1, Nk, d, "bf16", seed)
+    say(f"decode B={B} Hq={Hq} Hkv={Hkv} Nk={Nk} d={d} splits={splits}")
+    o, lse, op, lp = fa.decode(x["q"], x["k"], x["v"], splits, return_partials=True)
+    torch.cuda.synchronize()
+    ref = A.decode_split(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), 1 / math.sqrt(d), splits)
+    assert maxabs(to_f64(o), ref[0]) <= BF16_O
+    assert maxabs(to_f64(lse), ref[1]) <= BF16_LSE
+    assert maxabs(to_f64(op), ref[2]) <= BF16_O
+    assert maxabs(to_f64(lp), ref[3]) <= BF16_LSE
+    return x, o, lse
+
+
+@pytest.mark.parametrize("cfg", [
+    (2, 8, 2, 4096, 128, 8), (1, 4, 4, 1000, 128, 8), (2, 16, 2, 2048, 64, 4),
+    (1, 32, 1, 640, 128, 5), (3, 6, 2, 96, 128, 3)])
+def test_decode_small(fa_gpu, cfg):
+    check_decode(fa_gpu, *cfg, seed=41)
+
+
+def test_decode_split_count_invariance(fa_gpu):
+    x = gen(2, 8, 2, 1, 8192, 128, "bf16", 42)
+    outs = []
+    for s in (1, 2, 64, 128):
+        say(f"decode invariance splits={s}")
+        o, lse = fa_gpu.decode(x["q"], x["k"], x["v"], s)
+        torch.cuda.synchronize()
+        outs.append((to_f64(o), to_f64(lse)))
+    ref = A.forward(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), 1 / math.sqrt(128))
+    for o, lse in outs:
+        assert maxabs(o, ref[0]) <= BF16_O and maxabs(lse, ref[1]) <= BF16_LSE
+
+
+def test_decode_config_full(fa_gpu):
+    """B=8 Hq=32 Hkv=8 Nk=131072 d=128, 64 splits: every output and partial,
+    the oracle widening one (b, KV head) slab at a time."""
+    w = WORKLOADS["decode_gqa"]
+    say("decode_gqa inputs")
+    x = make_inputs(w, device="cuda")
+    say("decode_gqa full size")
+    o, lse, op, lp = fa_gpu.decode(x["q"], x["k"], x["v"], w.num_splits, return_partials=True)
+    torch.cuda.synchronize()
+    o, lse, op, lp = (to_f64(t) for t in (o, lse, op, lp))
+    qh = to_f64(x["q"])
+    G = w.Hq // w.Hkv
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            kk = x["k"][b:b + 1, hk:hk + 1].float().cpu().numpy()
+            vv = x["v"][b:b + 1, hk:hk + 1].float().cpu().numpy()
+            qq = qh[b:b + 1, hk * G:(hk + 1) * G]
+            ro, rl, rop, rlp = A.decode_split(qq, np.repeat(kk, 1, 1), vv, w.scale, w.num_splits)
+            sl = slice(hk * G, (hk + 1) * G)
+            assert maxabs(o[b, sl], ro[0]) <= BF16_O
+            assert maxabs(lse[b, sl], rl[0]) <= BF16_LSE
+            assert maxabs(op[b, sl], rop[0]) <= BF16_O
+            assert maxabs(lp[b, sl], rlp[0]) <= BF16_LSE
+
+
+# ---------------------------------------------------------------------- fp8
+
+def test_quantizer_codes_match_oracle_bytes(fa_gpu):
+    """Without rotation the codes are a pure function of the fp32 inputs: they
+    must equal the oracle's e4m3 codes byte for byte, scales exactly."""
+    x = gen(2, 3, 3, 300, 300, 128, "bf16", 51)["q"]
+    x[0, 0, 5, 7] = 50.0
+    x[1, 2, 299, :] = 0.0
+    say("quantize_fp8 no rotation")
+    codes, scales = fa_gpu.quantize_fp8(x)
+    torch.cuda.synchronize()
+    ref_c, ref_s = F8.quantize(x.float().cpu().numpy())
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    assert np.array_equal(codes.cpu().numpy(), ref_c)
+
+
+def test_quantizer_all_zero_block(fa_gpu):
+    x = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16, device="cuda")
+    say("quantize_fp8 zero block")
+    codes, scales = fa_gpu.quantize_fp8(x)
+    torch.cuda.synchronize()
+    assert float(scales[0, 0, 0]) == 1.0 and int(codes.abs().max() if False else codes.max()) == 0
+
+
+def test_quantizer_rotation(fa_gpu):
+    """With the Hadamard rotation the fp32 pre-quantisation values differ from
+    the oracle's fp64 rotation by rounding only, so a code may move by one
+    e4m3 step where the value sits on a rounding boundary."""
+    x = gen(1, 2, 2, 256, 256, 128, "bf16", 52)["q"]
+    signs = (torch.randint(0, 2, (128,), generator=torch.Generator().manual_seed(5)) * 2 - 1).to(torch.int8)
+    say("quantize_fp8 rotation")
+    codes, scales = fa_gpu.quantize_fp8(x, signs.cuda())
+    torch.cuda.synchronize()
+    rot = F8.rotate(x.float().cpu().numpy(), signs.numpy()).astype(np.float32)
+    ref_c, ref_s = F8.quantize(rot)
+    assert np.allclose(scales.cpu().numpy(), ref_s, rtol=1e-6)
+    got = F8.dequantize(codes.cpu().numpy(), scales.cpu().numpy())
+    want = F8.dequantize(ref_c, ref_s)
+    mismatch = (codes.cpu().numpy() != ref_c)
+    assert mismatch.mean() < 1e-3
+    step = np.abs(want) * 2.0 ** -3 + ref_s.max() * 2.0 ** -9
+    assert np.all(np.abs(got - want) <= step + 1e-12)
+
+
+def fp8_pipeline(fa, x, signs, causal=False):
+    q8, qs = fa.quantize_fp8(x["q"], signs)
+    k8, ks = fa.quantize_fp8(x["k"], signs)
+    v8, vs = fa.quantize_fp8(x["v"], None)
+    o, lse = fa.forward_fp8(q8, k8, v8, qs, ks, vs, causal=causal)
+    return o, lse, (q8, qs, k8, ks, v8, vs)
+
+
+def dequant_inputs(parts):
+    q8, qs, k8, ks, v8, vs = (t.cpu().numpy() for t in parts)
+    return F8.dequantize(q8, qs), F8.dequantize(k8, ks), F8.dequantize(v8, vs)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_forward_small(fa_gpu, causal):
+    x = gen(1, 4, 2, 384, 384, 128, "bf16", 61)
+    signs = (torch.randint(0, 2, (128,), generator=torch.Generator().manual_seed(6)) * 2 - 1).to(torch.int8).cuda()
+    say(f"fp8 forward small causal={causal}")
+    o, lse, parts = fp8_pipeline(fa_gpu, x, signs, causal)
+    torch.cuda.synchronize()
+    dq, dk, dv = dequant_inputs(parts)
+    ro, rl = A.forward(dq, dk, dv, 1 / math.sqrt(128), causal)
+    assert rel_l2(to_f64(o), ro) <= FP8_REL
+    assert maxabs(to_f64(lse), rl) <= 5e-2
+
+
+def test_fp8_config_sampled(fa_gpu):
+    """B=2 H=16 N=8192 d=128 with 0.1% outliers of magnitude 50 in Q and K,
+    rotated: sampled rows of every head against the oracle on the dequantised
+    operands; the error against exact attention on the unquantised inputs is
+    printed (it is dominated by e4m3 rounding of Q and K, not by the kernel)."""
+    w = WORKLOADS["fp8_fwd"]
+    x = {n: t.cuda() for n, t in make_inputs(w).items()}
+    say("fp8 forward full size")
+    o, lse, parts = fp8_pipeline(fa_gpu, x, x["signs"])
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 4095, 4096, 8191, 777])
+    dq, dk, dv = dequant_inputs(parts)
+    # dequantised Q/K are rotated; the oracle forward on them is the kernel's problem
+    ro, rl = A.forward(dq, dk, dv, w.scale, False, rows=rows)
+    og = to_f64(o)[:, :, rows]
+    assert rel_l2(og, ro) <= FP8_REL
+    exact, _ = A.forward(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), w.scale, False, rows=rows)
+    print(f"fp8 config: rel-L2 vs dequantised oracle {rel_l2(og, ro):.4f}, "
+          f"vs exact unquantised {rel_l2(og, exact):.4f}")
