@@ -82,6 +82,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of parts to time (default all)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one plain 256 MiB fp32 read+write kernel first (a known-size "
+                         "reference for hardware byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py: --gpus {a.gpus} is not supported; this library and its benchmark "
@@ -97,6 +100,13 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     parts = {}
     only = set(x for x in a.only.split(",") if x)
+    if a.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)   # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        log("calibration copy: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
 
     # ------------------------------------------------ headline: causal fwd+bwd
     w = WORKLOADS["causal_bf16"]

@@ -2,7 +2,7 @@
 // gfx950 kernels.  Every check runs before anything is enqueued, so an invalid
 // call leaves the stream untouched.
 
-#include "../../include/fa.h"
+#include "fa.h"
 
 #include <cmath>
 #include <cstdint>

@@ -53,6 +53,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max / sum of x over lanes l and l^32, in every lane (v_permlane32_swap:
+// one result holds the lower half's values, the other the upper half's).
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename T>
 __device__ __forceinline__ T ldg(const void* p) {
   return *reinterpret_cast<const T*>(p);
@@ -68,6 +79,42 @@ __device__ __forceinline__ T lds_read(const char* base, int off) {
 template <typename T>
 __device__ __forceinline__ void lds_write(char* base, int off, T v) {
   *reinterpret_cast<T*>(base + off) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads and transposing LDS reads (gfx950).
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// One wave copies 64 x 16 bytes: lane i reads rsrc[voff_i + soff] and writes
+// LDS bytes [lds + 16*i, lds + 16*i + 16).  `lds` must be wave-uniform.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char* lds, int voff,
+                                                  int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+
+// Wait for this wave's outstanding vector-memory loads (including the
+// direct-to-LDS ones, which the compiler does not track as LDS writes).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane i element e
+// is element (i % 4) of the 8-byte chunk addressed by lane 4*e + i/4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float fdot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 }  // namespace fa

@@ -6,7 +6,7 @@
 // FlashAttention" slide 12.
 //
 // bf16 kernel layout (one workgroup = 4 waves = 128 query rows, KV tiles of 64
-// keys):
+// keys, two workgroups per compute unit):
 //   * each wave owns 32 query rows.  It computes S^T = K Q^T with the keys on
 //     the MFMA m axis and its queries on the n axis, so every lane owns one
 //     query column: the row max is an in-register reduction plus one exchange
@@ -14,9 +14,11 @@
 //   * Q stays in registers for the whole tile as the B operand.
 //   * P^T (the S^T accumulator rounded to bf16) is directly the B operand of
 //     O^T += V^T P^T: the keys of the accumulator become the k index of the
-//     next product.  V^T comes from LDS, where V is stored transposed.
-//   * K and V^T tiles are double-buffered in LDS; the next tile's global loads
-//     are issued before the current tile's math so their latency is hidden.
+//     next product.  The V^T fragments are read from the row-major V tile with
+//     the transposing LDS read (ds_read_b64_tr_b16).
+//   * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
+//     destination bit), double-buffered: the next tile's loads are issued
+//     right after the barrier and land while the current tile is computed.
 //   * exp is exp2 with scale*log2(e) folded into one FMA; O is divided by the
 //     row sum once at the end ([CH18] §18.4.3 step 9).
 
@@ -54,15 +56,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Nq, int Nk, float scale, float scale_log2, int BH, int nqt) {
   constexpr int BC = kFwdBc;
-  constexpr int KP = D * 2 + 16;   // K row pitch in LDS (bytes): conflict-free b128 reads
-  constexpr int VP = BC * 2 + 8;   // V^T row pitch in LDS (bytes): conflict-free b64 reads
-  constexpr int KSLOT = BC * KP;
-  constexpr int VSLOT = D * VP;
-  constexpr int KCH = BC * D / 8 / 256;  // 16-byte K chunks per thread per tile
-  constexpr int DCH = D / 8;             // 16-byte chunks per row
-  constexpr int KSTEPS = D / 16;         // MFMA k-steps over the head dim
-  constexpr int DBLK = D / 32;           // 32-wide blocks of the head dim
-  __shared__ __attribute__((aligned(16))) char smem[2 * (KSLOT + VSLOT)];
+  constexpr int ROWB = D * 2;               // bytes per K/V row in LDS (no padding)
+  constexpr int NCH = D / 8;                // 16-byte chunks per row
+  constexpr int TILE = BC * ROWB;           // bytes of one K or V tile
+  constexpr int LPW = TILE / 1024 / 4;      // 1 KB direct loads per wave per tile
+  constexpr int RPL = 1024 / ROWB;          // rows per 1 KB load
+  constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
+  constexpr int DBLK = D / 32;              // 32-wide blocks of the head dim
+  // LDS: [slot 0: K | V][slot 1: K | V].  Rows are stored unpadded with the
+  // 16-byte chunks XOR-swizzled per row, so that both the b128 reads of K and
+  // the transposing b64 reads of V hit distinct banks:
+  //   K: chunk c of row r sits at position c ^ (r & 7)
+  //   V: chunk c of row r sits at position c ^ ((2 r) & (NCH - 1))
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,8 +82,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int h = bh - b * Hq;
   const int hk = h / (Hq / Hkv);
   const uint16_t* Qp = Q + (size_t)bh * Nq * D;
-  const uint16_t* Kp = K + (size_t)(b * Hkv + hk) * Nk * D;
-  const uint16_t* Vp = V + (size_t)(b * Hkv + hk) * Nk * D;
+  const size_t kv_off = (size_t)(b * Hkv + hk) * Nk * D;
+  // rows past Nk read as zero (and are masked below)
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kv_off, (uint32_t)Nk * ROWB);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * ROWB);
 
   const int q0 = qt * kFwdBr;
   const int qrow = q0 + wave * 32 + l32;
@@ -93,76 +101,65 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int kv_end = CAUSAL ? min(Nk, q0 + kFwdBr) : Nk;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  // Global -> register staging for one K/V tile.
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-  // V is read in groups of 4 consecutive keys x 8 head dims per thread so that
-  // it can be written transposed as 8-byte runs of keys.
-  const int v_rg = tid / DCH;          // key group (4 keys)
-  const int v_col = tid - v_rg * DCH;  // 16-byte column chunk
-  const bool v_active = v_rg < BC / 4;
+  // Per-lane source offsets of this wave's direct loads (same for every tile):
+  // LDS block (wave*LPW + i) holds tile rows r, lane -> position p.
+  int koff[LPW], voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int r = (wave * LPW + i) * RPL + lane / NCH;
+    const int p = lane % NCH;
+    koff[i] = r * ROWB + ((p ^ (r & 7)) << 4);
+    voff[i] = r * ROWB + ((p ^ ((2 * r) & (NCH - 1))) << 4);
+  }
+  auto issue_tile = [&](int j, int slot) {
+    char* kd = smem + slot * 2 * TILE + wave * LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      buffer_load_lds16(rK, kd + i * 1024, koff[i], j * TILE);
+      buffer_load_lds16(rV, kd + TILE + i * 1024, voff[i], j * TILE);
+    }
+  };
 
-  auto load_tile = [&](int j) {
-    const int kv0 = j * BC;
+  // Per-lane LDS read offsets.  K (A operand, row kb*32 + l32, chunk 2*kk + hf):
+  int krd[KSTEPS];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      int c = tid + 256 * i;
-      int row = c / DCH, col = c - row * DCH;
-      int key = kv0 + row;
-      key = key < Nk ? key : Nk - 1;
-      kreg[i] = ldg<u32x4>(Kp + (size_t)key * D + col * 8);
-    }
-    if (v_active) {
+  for (int kk = 0; kk < KSTEPS; ++kk) krd[kk] = l32 * ROWB + (((2 * kk + hf) ^ (l32 & 7)) << 4);
+  // V^T via ds_read_b64_tr_b16.  In each 16-lane group g (= lane/16), source
+  // lane j addresses key row 4*(g/2) + j/4 (+ 16*st + 32*kb, + 8 for the
+  // second read) at head dims dbase + 4*(j%4) with dbase = 32*db + 16*(g%2);
+  // the group's output lane i then holds V[row(e)][dbase + i] for e = 0..3.
+  const int g16 = lane >> 4;
+  const int j16 = lane & 15;
+  const int vrow = 4 * (g16 >> 1) + (j16 >> 2);
+  const int vsw = (2 * vrow) & (NCH - 1);
+  int vrd[DBLK];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int key = kv0 + v_rg * 4 + i;
-        key = key < Nk ? key : Nk - 1;
-        vreg[i] = ldg<u32x4>(Vp + (size_t)key * D + v_col * 8);
-      }
-    }
-  };
-  auto store_tile = [&](int slot) {
-    char* ks = smem + slot * (KSLOT + VSLOT);
-    char* vs = ks + KSLOT;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      int c = tid + 256 * i;
-      int row = c / DCH, col = c - row * DCH;
-      lds_write<u32x4>(ks, row * KP + col * 16, kreg[i]);
-    }
-    if (v_active) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = pack_hi16(vreg[0][w], vreg[1][w]);
-          hi = pack_hi16(vreg[2][w], vreg[3][w]);
-        } else {
-          lo = pack_lo16(vreg[0][w], vreg[1][w]);
-          hi = pack_lo16(vreg[2][w], vreg[3][w]);
-        }
-        lds_write<u32x2>(vs, (v_col * 8 + e) * VP + v_rg * 8, u32x2{lo, hi});
-      }
-    }
-  };
+  for (int db = 0; db < DBLK; ++db) {
+    const int c = 4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    vrd[db] = vrow * ROWB + ((c ^ vsw) << 4) + (j16 & 1) * 8;
+  }
 
   f32x16 o[DBLK];
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) o[i] = f32x16{0};
-  float m_run = -INFINITY;  // running max of raw q.k (unscaled)
-  float l_run = 0.f;        // this lane's share of the running row sum
+  // Running reference max in log2 units (scale*log2e folded in).  It is only
+  // raised when some row's max grows by more than 2^8, so O and l are rescaled
+  // rarely; probabilities are then at most 2^8, which fp32 and bf16 hold with
+  // unchanged relative precision.  The final O/l and LSE do not depend on the
+  // reference.  A finite start keeps (-inf) - (-inf) from ever forming.
+  float M = -1e30f;
+  float l_run = 0.f;  // this lane's share of the row sum
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
+  issue_tile(0, 0);
   for (int j = 0; j < ntiles; ++j) {
     const int slot = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-    const char* ks = smem + slot * (KSLOT + VSLOT);
-    const char* vs = ks + KSLOT;
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < ntiles) issue_tile(j + 1, slot ^ 1);
     const int kv0 = j * BC;
+    if (CAUSAL && kv0 > q0 + wave * 32 + 31) continue;  // every key after every row
+    const char* ks = smem + slot * 2 * TILE;
+    const char* vs = ks + TILE;
 
     // S^T for the wave: two 32-key blocks x 32 queries.
     f32x16 s[2];
@@ -170,10 +167,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{0};
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        u32x4 a = lds_read<u32x4>(ks, (kb * 32 + l32) * KP + (kk * 16 + hf * 8) * 2);
-        s[kb] = mfma_32x32x16_bf16(a, qf[kk], s[kb]);
-      }
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        s[kb] = mfma_32x32x16_bf16(lds_read<u32x4>(ks, kb * 32 * ROWB + krd[kk]), qf[kk], s[kb]);
     }
 
     // Mask keys past the end (ragged tail) and, on diagonal tiles, keys after
@@ -184,9 +179,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          bool dead = key >= Nk || (CAUSAL && key > qrow);
-          if (dead) s[kb][r] = -INFINITY;
+          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= Nk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
         }
     }
 
@@ -195,24 +189,24 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, xor32(mt));
-    // A row with no visible key so far keeps m = -inf; use 0 as its reference
-    // so that no (-inf) - (-inf) is ever formed.
-    const float m_new = fmaxf(m_run, mt);
-    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_ref) * scale_log2);
-    const float mb = m_ref * scale_log2;
-    m_run = m_new;
+    const float mts = max_halves(mt) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mts > M + 8.f)) {
+      const float Mn = fmaxf(M, mts);
+      const float alpha = fast_exp2(M - Mn);
+      M = Mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+    }
 
-    float psum = 0.f;
     u32x4 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(s[kb][r], scale_log2, -mb));
-        psum += p[r];
+        p[r] = fast_exp2(fmaf(s[kb][r], scale_log2, -M));
+        l_run += p[r];  // fp32 sum of the unrounded p: LSE stays exact to fp32
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -221,9 +215,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
                            pack_bf16(p[8 * st + 4], p[8 * st + 5]),
                            pack_bf16(p[8 * st + 6], p[8 * st + 7])};
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
 
     // O^T += V^T P^T.  B element e of lane half hf in k-step (kb, st) is key
     // kb*32 + 16*st + 8*(e/4) + 4*hf + e%4 (the accumulator's row order).
@@ -233,18 +224,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          int off = (db * 32 + l32) * VP + (kb * 32 + st * 16 + hf * 4) * 2;
-          u32x2 a0 = lds_read<u32x2>(vs, off);
-          u32x2 a1 = lds_read<u32x2>(vs, off + 16);
+          const char* vp = vs + (kb * 32 + st * 16) * ROWB + vrd[db];
+          const u32x2 a0 = lds_read_tr16(vp);
+          const u32x2 a1 = lds_read_tr16(vp + 8 * ROWB);
           o[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[kb][st], o[db]);
         }
-
-    if (j + 1 < ntiles) store_tile(slot ^ 1);
-    __syncthreads();
   }
 
-  // Epilogue: O = O^T / l, LSE = m*scale + ln l.
-  const float l_tot = l_run + xor32(l_run);
+  // Epilogue: O = O^T / l, LSE = (M + log2 l) ln 2.
+  const float l_tot = sum_halves(l_run);
   const float inv = 1.f / l_tot;
   if (qrow < Nq) {
     uint16_t* Op = O + ((size_t)bh * Nq + qrow) * D;
@@ -256,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         stg<u32x2>(Op + d0, u32x2{pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
                                   pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)});
       }
-    if (hf == 0) LSE[(size_t)bh * Nq + qrow] = m_run * scale + __logf(l_tot);
+    if (hf == 0) LSE[(size_t)bh * Nq + qrow] = (M + __log2f(l_tot)) * kLn2;
   }
 }
 
