@@ -104,6 +104,17 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char
 // Wait for this wave's outstanding vector-memory loads (including the
 // direct-to-LDS ones, which the compiler does not track as LDS writes).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (loads complete in issue order for this counter).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier for LDS tiles: this wave's LDS reads have returned, then
+// s_barrier.  Outstanding direct-to-LDS loads are waited for separately.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, output lane i element e
 // is element (i % 4) of the 8-byte chunk addressed by lane 4*e + i/4.

@@ -17,8 +17,9 @@
 //     next product.  The V^T fragments are read from the row-major V tile with
 //     the transposing LDS read (ds_read_b64_tr_b16).
 //   * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
-//     destination bit), double-buffered: the next tile's loads are issued
-//     right after the barrier and land while the current tile is computed.
+//     destination bit), double-buffered, with K one tile ahead of V so that
+//     the QK^T MFMAs of the next tile run while the exponentials of the
+//     current tile are computed (one barrier per tile).
 //   * exp is exp2 with scale*log2(e) folded into one FMA; O is divided by the
 //     row sum once at the end ([CH18] §18.4.3 step 9).
 
@@ -29,9 +30,10 @@ namespace fa {
 
 namespace {
 
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;
 constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;              // keys per KV tile
+constexpr int kFwdStages = 3;           // K/V tiles in flight
 
 }  // namespace
 
@@ -50,8 +52,24 @@ int fwd_kv_tiles(int qt, int Nk, bool causal, int br, int bc) {
   return (last + bc - 1) / bc;
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+template <int N>
+struct IntConst {
+  static constexpr int value = N;
+};
+
+// Chunk swizzles of the K and V tiles (see fwd_bf16_kernel).  K: rows r..r+15
+// read one chunk each; V: rows 4i..4i+3 read four consecutive chunks each.
+template <int D>
+__device__ __forceinline__ int fwd_swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int fwd_swz_v(int r) {
+  return D == 128 ? (4 * (r & 3)) : (4 * ((r >> 1) & 1));
+}
+
+template <int D, bool CAUSAL, int NW, int NS>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Nq, int Nk, float scale, float scale_log2, int BH, int nqt) {
@@ -59,20 +77,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   constexpr int ROWB = D * 2;               // bytes per K/V row in LDS (no padding)
   constexpr int NCH = D / 8;                // 16-byte chunks per row
   constexpr int TILE = BC * ROWB;           // bytes of one K or V tile
-  constexpr int LPW = TILE / 1024 / 4;      // 1 KB direct loads per wave per tile
+  constexpr int BR = 32 * NW;               // query rows per workgroup
+  constexpr int LPW = TILE / 1024 / NW;     // 1 KB direct loads per wave per tile
   constexpr int RPL = 1024 / ROWB;          // rows per 1 KB load
   constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
   constexpr int DBLK = D / 32;              // 32-wide blocks of the head dim
-  // LDS: [slot 0: K | V][slot 1: K | V].  Rows are stored unpadded with the
-  // 16-byte chunks XOR-swizzled per row, so that both the b128 reads of K and
-  // the transposing b64 reads of V hit distinct banks:
-  //   K: chunk c of row r sits at position c ^ (r & 7)
-  //   V: chunk c of row r sits at position c ^ ((2 r) & (NCH - 1))
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  // LDS: NS K slots, then NS V slots.  Rows are stored unpadded
+  // with the 16-byte chunks XOR-swizzled per row (chunk c of row r at position
+  // c ^ sw(r)), so that the b128 reads of K (16 consecutive rows, one chunk)
+  // and the transposing b64 reads of V (4 consecutive rows x 4 chunks) hit
+  // distinct banks of the 64-bank LDS.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -87,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kv_off, (uint32_t)Nk * ROWB);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * ROWB);
 
-  const int q0 = qt * kFwdBr;
+  const int q0 = qt * BR;
   const int qrow = q0 + wave * 32 + l32;
   const int qrow_c = qrow < Nq ? qrow : Nq - 1;
 
@@ -98,32 +117,35 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   for (int ks = 0; ks < KSTEPS; ++ks)
     qf[ks] = ldg<u32x4>(Qp + (size_t)qrow_c * D + ks * 16 + hf * 8);
 
-  const int kv_end = CAUSAL ? min(Nk, q0 + kFwdBr) : Nk;
+  const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
   const int ntiles = (kv_end + BC - 1) / BC;
 
   // Per-lane source offsets of this wave's direct loads (same for every tile):
-  // LDS block (wave*LPW + i) holds tile rows r, lane -> position p.
+  // LDS block (wave*LPW + i) of a tile holds rows r, lane -> position p.
   int koff[LPW], voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int r = (wave * LPW + i) * RPL + lane / NCH;
     const int p = lane % NCH;
-    koff[i] = r * ROWB + ((p ^ (r & 7)) << 4);
-    voff[i] = r * ROWB + ((p ^ ((2 * r) & (NCH - 1))) << 4);
+    koff[i] = r * ROWB + ((p ^ fwd_swz_k<D>(r)) << 4);
+    voff[i] = r * ROWB + ((p ^ fwd_swz_v<D>(r)) << 4);
   }
-  auto issue_tile = [&](int j, int slot) {
-    char* kd = smem + slot * 2 * TILE + wave * LPW * 1024;
+  auto issue_k = [&](int j, int slot) {
+    char* d = smem + slot * TILE + wave * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      buffer_load_lds16(rK, kd + i * 1024, koff[i], j * TILE);
-      buffer_load_lds16(rV, kd + TILE + i * 1024, voff[i], j * TILE);
-    }
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rK, d + i * 1024, koff[i], j * TILE);
+  };
+  auto issue_v = [&](int j, int slot) {
+    char* d = smem + (NS + slot) * TILE + wave * LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rV, d + i * 1024, voff[i], j * TILE);
   };
 
   // Per-lane LDS read offsets.  K (A operand, row kb*32 + l32, chunk 2*kk + hf):
   int krd[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) krd[kk] = l32 * ROWB + (((2 * kk + hf) ^ (l32 & 7)) << 4);
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    krd[kk] = l32 * ROWB + (((2 * kk + hf) ^ fwd_swz_k<D>(l32)) << 4);
   // V^T via ds_read_b64_tr_b16.  In each 16-lane group g (= lane/16), source
   // lane j addresses key row 4*(g/2) + j/4 (+ 16*st + 32*kb, + 8 for the
   // second read) at head dims dbase + 4*(j%4) with dbase = 32*db + 16*(g%2);
@@ -131,13 +153,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int g16 = lane >> 4;
   const int j16 = lane & 15;
   const int vrow = 4 * (g16 >> 1) + (j16 >> 2);
-  const int vsw = (2 * vrow) & (NCH - 1);
+  const int vsw = fwd_swz_v<D>(vrow);  // rows vrow + 8, +16, ... share it
   int vrd[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) {
     const int c = 4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1);
     vrd[db] = vrow * ROWB + ((c ^ vsw) << 4) + (j16 & 1) * 8;
   }
+
+  // S^T = K Q^T for one K slot: two 32-key blocks x this wave's 32 queries.
+  auto qk = [&](int slot, f32x16* s) {
+    const char* ks = smem + slot * TILE;
+    s[0] = f32x16{0};
+    s[1] = f32x16{0};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma_32x32x16_bf16(lds_read<u32x4>(ks, kb * 32 * ROWB + krd[kk]), qf[kk], s[kb]);
+  };
 
   f32x16 o[DBLK];
 #pragma unroll
@@ -150,29 +184,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   float M = -1e30f;
   float l_run = 0.f;  // this lane's share of the row sum
 
-  issue_tile(0, 0);
-  for (int j = 0; j < ntiles; ++j) {
-    const int slot = j & 1;
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < ntiles) issue_tile(j + 1, slot ^ 1);
+  // Mask one S^T tile and fold its row max into M (rescaling O and l when M
+  // must move).  Keys past the end (ragged tail) and, on tiles crossing the
+  // diagonal, keys after the query are masked ([CH18] §18.5.2).
+  auto row_max = [&](int j, f32x16* s) {
     const int kv0 = j * BC;
-    if (CAUSAL && kv0 > q0 + wave * 32 + 31) continue;  // every key after every row
-    const char* ks = smem + slot * 2 * TILE;
-    const char* vs = ks + TILE;
-
-    // S^T for the wave: two 32-key blocks x 32 queries.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{0};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        s[kb] = mfma_32x32x16_bf16(lds_read<u32x4>(ks, kb * 32 * ROWB + krd[kk]), qf[kk], s[kb]);
-    }
-
-    // Mask keys past the end (ragged tail) and, on diagonal tiles, keys after
-    // the query ([CH18] §18.5.2: only tiles crossing the diagonal need it).
     const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
     if (need_mask) {
 #pragma unroll
@@ -183,7 +199,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
           if (key >= Nk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
         }
     }
-
     float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -198,37 +213,112 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
     }
+  };
 
+  // Software pipeline, one barrier per tile.  Iteration i reads K_{i+1} (for
+  // S_{i+1}) and V_i; the loads issued at its start fetch K_{i+NS} and
+  // V_{i+NS-1} into the slots freed by iteration i-1, so every tile has NS-1
+  // iterations to arrive.  The MFMAs of S_{i+1} = K_{i+1} Q^T overlap the
+  // exp/convert work of tile i, whose row max was taken at the end of the
+  // previous iteration.
+  f32x16 s_cur[2], s_nxt[2];
+  // prologue: K_0, V_0, K_1, then V_1, K_2, ... (the first three are needed first)
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (ntiles > 1) issue_k(1, 1);
+#pragma unroll
+  for (int t = 1; t + 1 < NS; ++t) {
+    if (t < ntiles) issue_v(t, t);
+    if (t + 1 < ntiles) issue_k(t + 1, t + 1);
+  }
+  if (NS == 3) wait_vmem_le<2 * LPW>();  // V_1 and K_2 may still be in flight
+  else wait_vmem();
+  __syncthreads();
+  qk(0, s_cur);
+  row_max(0, s_cur);
+  lds_barrier();  // K slot 0 is refilled below
+
+  // One pipeline step; U = i % NS makes every slot a compile-time constant, so
+  // the LDS fragment addresses are a per-lane register plus an immediate.
+  auto step = [&](int i, auto U) {
+    constexpr int u = decltype(U)::value;
+    const bool more_k = i + NS < ntiles;
+    const bool more_v = i + NS - 1 < ntiles;
+    if (more_k) issue_k(i + NS, u);                   // slot (i+NS) % NS
+    if (more_v) issue_v(i + NS - 1, (u + NS - 1) % NS);
+    // S_{i+1} = K_{i+1} Q^T on the matrix pipe, interleaved op by op with the
+    // exponentials of tile i (the last iteration computes an unused product of
+    // a stale slot).  Group g issues one MFMA and then the fma/exp/sum/convert
+    // of two elements of S_i; sched_barrier pins that order so the MFMAs run
+    // while this wave does VALU work.  K fragments are read 2 groups ahead.
+    constexpr int NG = 2 * KSTEPS;            // MFMAs of one QK^T tile
+    constexpr int EPG = 32 / NG;              // S_i elements per group (per lane)
+    constexpr int AHEAD = 2;
     u32x4 pb[2][2];
+    {
+      const char* ks = smem + ((u + 1) % NS) * TILE;
+      s_nxt[0] = f32x16{0};
+      s_nxt[1] = f32x16{0};
+      u32x4 afr[AHEAD];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
+      for (int g = 0; g < AHEAD; ++g)
+        afr[g] = lds_read<u32x4>(ks, (g & 1) * 32 * ROWB + krd[g >> 1]);
+      float p[32];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(s[kb][r], scale_log2, -M));
-        l_run += p[r];  // fp32 sum of the unrounded p: LSE stays exact to fp32
+      for (int g = 0; g < NG; ++g) {
+        const int kb = g & 1, kk = g >> 1;
+        s_nxt[kb] = mfma_32x32x16_bf16(afr[g % AHEAD], qf[kk], s_nxt[kb]);
+        if (g + AHEAD < NG)
+          afr[g % AHEAD] =
+              lds_read<u32x4>(ks, ((g + AHEAD) & 1) * 32 * ROWB + krd[(g + AHEAD) >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = g * EPG; e < (g + 1) * EPG; ++e) {
+          p[e] = fast_exp2(fmaf(s_cur[e >> 4][e & 15], scale_log2, -M));
+          l_run += p[e];  // fp32 sum of the unrounded p: LSE stays exact to fp32
+          if (e & 1) {
+            const int kb2 = e >> 4, r = e & 15;
+            pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16(p[e - 1], p[e]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        pb[kb][st] = u32x4{pack_bf16(p[8 * st + 0], p[8 * st + 1]),
-                           pack_bf16(p[8 * st + 2], p[8 * st + 3]),
-                           pack_bf16(p[8 * st + 4], p[8 * st + 5]),
-                           pack_bf16(p[8 * st + 6], p[8 * st + 7])};
     }
 
     // O^T += V^T P^T.  B element e of lane half hf in k-step (kb, st) is key
     // kb*32 + 16*st + 8*(e/4) + 4*hf + e%4 (the accumulator's row order).
+    __builtin_amdgcn_s_setprio(1);
+    const char* vs = smem + (NS + u) * TILE;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int db = 0; db < DBLK; ++db) {
           const char* vp = vs + (kb * 32 + st * 16) * ROWB + vrd[db];
           const u32x2 a0 = lds_read_tr16(vp);
           const u32x2 a1 = lds_read_tr16(vp + 8 * ROWB);
           o[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[kb][st], o[db]);
         }
+    __builtin_amdgcn_s_setprio(0);
+
+    if (i + 1 < ntiles) {
+      row_max(i + 1, s_nxt);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+    }
+    // K_{i+2} and V_{i+1} must have landed; this iteration's loads may not.
+    if (NS == 3 && more_k) wait_vmem_le<2 * LPW>();
+    else if (NS == 3 && more_v) wait_vmem_le<LPW>();
+    else wait_vmem();
+    lds_barrier();
+  };
+  for (int i0 = 0; i0 < ntiles; i0 += NS) {
+    step(i0, IntConst<0>{});
+    if (i0 + 1 < ntiles) step(i0 + 1, IntConst<1>{});
+    if constexpr (NS == 3) {
+      if (i0 + 2 < ntiles) step(i0 + 2, IntConst<2>{});
+    }
   }
 
   // Epilogue: O = O^T / l, LSE = (M + log2 l) ln 2.
@@ -319,9 +409,10 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                            bool causal, hipStream_t stream) {
+  constexpr int NW = kFwdWaves, NS = kFwdStages;
   const int BH = B * Hq;
   const int nqt = (Nq + kFwdBr - 1) / kFwdBr;
-  dim3 grid(BH * nqt), block(256);
+  dim3 grid(BH * nqt), block(NW * 64);
   const float sl2 = scale * kLog2e;
   auto Qp = (const uint16_t*)q;
   auto Kp = (const uint16_t*)k;
@@ -329,18 +420,18 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   auto Op = (uint16_t*)o;
   if (d == 128) {
     if (causal)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, Qp, Kp, Vp, Op,
-                         lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, true, NW, NS>), grid, block, 0, stream, Qp, Kp,
+                         Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, Qp, Kp, Vp, Op,
-                         lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, false, NW, NS>), grid, block, 0, stream, Qp, Kp,
+                         Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
   } else {
     if (causal)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, Qp, Kp, Vp, Op,
-                         lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, true, NW, NS>), grid, block, 0, stream, Qp, Kp,
+                         Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, Qp, Kp, Vp, Op,
-                         lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, false, NW, NS>), grid, block, 0, stream, Qp, Kp,
+                         Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
   }
   return hipGetLastError();
 }
