@@ -3,7 +3,7 @@
 
 One step = the headline workload's whole training pass: bf16 causal forward
 plus backward at B=2, H=16, N=8192, d=128 (fa_fwd, then fa_bwd's three
-stages), inputs resident in HBM.  The value is its aggregate throughput in
+stages: delta pre-pass, dK/dV kernel, dQ kernel), inputs resident in HBM.  The value is its aggregate throughput in
 TFLOP/s, counting 4*B*H*N*N*d/2 for the causal forward and 2.5x that for the
 backward.  The remaining rows of the path are timed after the steps, each on
 its own workload, and reported under "parts": the non-causal forward at the
@@ -127,51 +127,61 @@ def main(argv=None):
     def bwd_pre():
         fa.fa_bwd_pre(o, do, ws, ws_bytes, w.B, w.Hq, w.Nq, w.d, sh)
 
-    def bwd_main():
-        fa.fa_bwd_main(q, k, v, do, lse, dk, dv, ws, ws_bytes, *args, w.scale, True, sh)
+    def bwd_dkdv():
+        fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, ws_bytes, *args, w.scale, True, sh)
 
-    def bwd_post():
-        fa.fa_bwd_post(ws, ws_bytes, dq, w.B, w.Hq, w.Nq, w.d, sh)
+    def bwd_dq():
+        fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, ws_bytes, *args, w.scale, True, sh)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     log("warmup")
     for _ in range(a.warmup):
-        fwd(); bwd_pre(); bwd_main(); bwd_post()
+        fwd(); bwd_pre(); bwd_dkdv(); bwd_dq()
     torch.cuda.synchronize()
-    marks = [(ev(), ev(), ev(), ev()) for _ in range(a.steps)]
+    marks = [tuple(ev() for _ in range(6)) for _ in range(a.steps)]
     t_start, t_end = ev(), ev()
     log(f"timing {a.steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for f0, f1, m0, m1 in marks:
+    for f0, f1, k0, k1, q0_, q1_ in marks:
         f0.record(stream)
         fwd()
         f1.record(stream)
         bwd_pre()
-        m0.record(stream)
-        bwd_main()
-        m1.record(stream)
-        bwd_post()
+        k0.record(stream)
+        bwd_dkdv()
+        k1.record(stream)
+        q0_.record(stream)
+        bwd_dq()
+        q1_.record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / a.steps
-    fwd_ms = sum(f0.elapsed_time(f1) for f0, f1, _, _ in marks) / a.steps
-    main_ms = sum(m0.elapsed_time(m1) for _, _, m0, m1 in marks) / a.steps
+    avg = lambda i, j: sum(m[i].elapsed_time(m[j]) for m in marks) / a.steps
+    fwd_ms, dkdv_ms, dq_ms = avg(0, 1), avg(2, 3), avg(4, 5)
     step_flops = w.fwd_flops() + w.bwd_flops()
     value = step_flops / (ms_step * 1e-3) / 1e12
-    fwd_tf = w.fwd_flops() / (fwd_ms * 1e-3) / 1e12
-    main_tf = w.bwd_flops() / (main_ms * 1e-3) / 1e12
+    rate = lambda flops, ms: flops / (ms * 1e-3) / 1e12
+    # executed products: the forward is 2 GEMM units (QK^T, PV); the dK/dV
+    # kernel 4 (S, dP, dV, dK); the dQ kernel 3 (S, dP, dQ)
+    unit = w.fwd_flops() / 2
+    kern = {"fwd_bf16_kernel<128,causal> (fa_fwd)": (w.fwd_flops(), fwd_ms),
+            "bwd_dkdv_kernel<128,causal> (fa_bwd_dkdv)": (4 * unit, dkdv_ms),
+            "bwd_dq_kernel<128,causal> (fa_bwd_dq)": (3 * unit, dq_ms)}
+    dom = max(kern, key=lambda n: kern[n][1])
     bwd_ms = ms_step - fwd_ms
-    parts["fwd_causal"] = {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 1),
-                           "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)}
-    parts["bwd_causal"] = {"ms": round(bwd_ms, 4), "main_kernel_ms": round(main_ms, 4),
-                           "tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
-                           "frac_peak": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12
-                                              / PEAK_BF16_TFLOPS, 4)}
-    log(f"step {ms_step:.3f} ms: fwd {fwd_ms:.3f} ms ({fwd_tf:.0f} TF), bwd main {main_ms:.3f} ms "
-        f"({main_tf:.0f} TF)")
+    parts["fwd_causal"] = {"ms": round(fwd_ms, 4), "tflops": round(rate(w.fwd_flops(), fwd_ms), 1),
+                           "frac_peak": round(rate(w.fwd_flops(), fwd_ms) / PEAK_BF16_TFLOPS, 4)}
+    parts["bwd_causal"] = {"ms": round(bwd_ms, 4), "dkdv_ms": round(dkdv_ms, 4),
+                           "dq_ms": round(dq_ms, 4),
+                           "tflops": round(rate(w.bwd_flops(), bwd_ms), 1),
+                           "frac_peak": round(rate(w.bwd_flops(), bwd_ms) / PEAK_BF16_TFLOPS, 4),
+                           "dkdv_executed_tflops": round(rate(4 * unit, dkdv_ms), 1),
+                           "dq_executed_tflops": round(rate(3 * unit, dq_ms), 1)}
+    log(f"step {ms_step:.3f} ms: fwd {fwd_ms:.3f} ms ({rate(w.fwd_flops(), fwd_ms):.0f} TF), "
+        f"dkdv {dkdv_ms:.3f} ms, dq {dq_ms:.3f} ms, bwd {rate(w.bwd_flops(), bwd_ms):.0f} TF")
 
     iters = max(5, a.steps)
     if not only or "fwd" in only:
@@ -277,11 +287,11 @@ def main(argv=None):
                    "seq_len": w.Nq, "head_dim": w.d, "causal": True,
                    "flops_per_step": step_flops, "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
                    "wall_s": round(wall, 3)},
-        "roofline": {"kernel": "bwd_bf16_kernel<128,causal> (fa_bwd_main)", "bound": "mfma",
-                     "achieved": round(main_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(main_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flops_per_launch": w.bwd_flops(),
-                     "avg_launch_ms": round(main_ms, 4)},
+        "roofline": {"kernel": dom, "bound": "mfma",
+                     "achieved": round(rate(*kern[dom]), 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(rate(*kern[dom]) / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": kern[dom][0],
+                     "avg_launch_ms": round(kern[dom][1], 4)},
         "parts": parts,
     }
     if not a.no_cpu_baseline:

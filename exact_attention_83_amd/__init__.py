@@ -35,9 +35,10 @@ _SIGS = {
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                     _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_pre": (_I, [_P, _P, _P, _Z, _I, _I, _I, _I, _P]),
-    "fa_bwd_main": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z,
+    "fa_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z,
                          _I, _I, _I, _I, _I, _I, _F, _I, _P]),
-    "fa_bwd_post": (_I, [_P, _Z, _P, _I, _I, _I, _I, _P]),
+    "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _Z,
+                       _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                         _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -136,15 +137,17 @@ def fa_bwd_pre(o, dout, workspace, workspace_bytes, B, Hq, Nq, d, stream=None):
           _stream(stream))
 
 
-def fa_bwd_main(q, k, v, dout, lse, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+def fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
                 scale, causal, stream=None):
-    _call("fa_bwd_main", _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dk), _ptr(dv),
+    _call("fa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dk), _ptr(dv),
           _ptr(workspace), workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
           _stream(stream))
 
 
-def fa_bwd_post(workspace, workspace_bytes, dq, B, Hq, Nq, d, stream=None):
-    _call("fa_bwd_post", _ptr(workspace), workspace_bytes, _ptr(dq), B, Hq, Nq, d,
+def fa_bwd_dq(q, k, v, dout, lse, dq, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale,
+              causal, stream=None):
+    _call("fa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq),
+          _ptr(workspace), workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
           _stream(stream))
 
 

@@ -23,6 +23,11 @@ LIB = os.path.join(PKG, "libfa.so")
 
 ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fp8.hip"]
+# Per-file code generation options.  The backward kernel keeps more live
+# values than the 256 architectural VGPRs; with MFMA results in VGPR form the
+# overflow is spilled to AGPRs (cheap) instead of the register allocator
+# bouncing MFMA accumulators between AGPRs and VGPRs around every product.
+EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU ops.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
@@ -39,7 +44,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

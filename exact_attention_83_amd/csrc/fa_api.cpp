@@ -74,8 +74,7 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d) {
   if (B <= 0 || Hq <= 0 || Nq <= 0 || d <= 0) return 0;
-  const size_t rows = (size_t)B * Hq * Nq;
-  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+  return round256((size_t)B * Hq * Nq * sizeof(float));
 }
 
 static fa_status bwd_common(const void* q, const void* k, const void* v, const void* o,
@@ -93,11 +92,6 @@ static fa_status bwd_common(const void* q, const void* k, const void* v, const v
   return FA_OK;
 }
 
-static float* ws_delta(void* ws, int B, int Hq, int Nq, int d) {
-  const size_t rows = (size_t)B * Hq * Nq;
-  return reinterpret_cast<float*>(static_cast<char*>(ws) + round256(rows * d * sizeof(float)));
-}
-
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -106,13 +100,14 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                                Hq, Hkv, Nq, Nk, d, scale, causal))
     return s;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  float* dq_accum = static_cast<float*>(workspace);
-  float* delta = ws_delta(workspace, B, Hq, Nq, d);
-  hipError_t e = fa::launch_bwd_pre(o, dout, dq_accum, delta, B, Hq, Nq, d, stream);
+  float* delta = static_cast<float*>(workspace);
+  hipError_t e = fa::launch_bwd_pre(o, dout, delta, B, Hq, Nq, d, stream);
   if (e == hipSuccess)
-    e = fa::launch_bwd_main(q, k, v, dout, lse, delta, dq_accum, dk, dv, B, Hq, Hkv, Nq, Nk, d,
-                            scale, causal != 0, stream);
-  if (e == hipSuccess) e = fa::launch_bwd_post(dq_accum, dq, B, Hq, Nq, d, stream);
+    e = fa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                            causal != 0, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Nq, Nk, d, scale,
+                          causal != 0, stream);
   return hip_status(e);
 }
 
@@ -123,33 +118,35 @@ fa_status fa_bwd_pre(const void* o, const void* dout, void* workspace, size_t wo
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (workspace == nullptr || !aligned16(workspace)) return FA_ERR_WORKSPACE;
   if (workspace_bytes < fa_bwd_workspace_size(B, Hq, Nq, d)) return FA_ERR_WORKSPACE;
-  return hip_status(fa::launch_bwd_pre(o, dout, static_cast<float*>(workspace),
-                                       ws_delta(workspace, B, Hq, Nq, d), B, Hq, Nq, d, stream));
+  return hip_status(
+      fa::launch_bwd_pre(o, dout, static_cast<float*>(workspace), B, Hq, Nq, d, stream));
 }
 
-fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                      const float* lse, void* dk, void* dv, void* workspace,
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv, const void* workspace,
                       size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                       float scale, int causal, hipStream_t stream) {
   // o and dq are not touched by this stage; q stands in for them in the checks
-  if (fa_status s = bwd_common(q, k, v, q, dout, lse, q, dk, dv, workspace, workspace_bytes, B,
-                               Hq, Hkv, Nq, Nk, d, scale, causal))
+  if (fa_status s = bwd_common(q, k, v, q, dout, lse, q, dk, dv, const_cast<void*>(workspace),
+                               workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, causal))
     return s;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  return hip_status(fa::launch_bwd_main(q, k, v, dout, lse, ws_delta(workspace, B, Hq, Nq, d),
-                                        static_cast<float*>(workspace), dk, dv, B, Hq, Hkv, Nq,
-                                        Nk, d, scale, causal != 0, stream));
+  return hip_status(fa::launch_bwd_dkdv(q, k, v, dout, lse, static_cast<const float*>(workspace),
+                                        dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0,
+                                        stream));
 }
 
-fa_status fa_bwd_post(const void* workspace, size_t workspace_bytes, void* dq, int B, int Hq,
-                      int Nq, int d, hipStream_t stream) {
-  if (!aligned16(dq)) return FA_ERR_INVALID_ARG;
-  if (B <= 0 || Hq <= 0 || Nq <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, void* dq, const void* workspace, size_t workspace_bytes,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                    hipStream_t stream) {
+  // o, dk and dv are not touched by this stage; q stands in for them
+  if (fa_status s = bwd_common(q, k, v, q, dout, lse, dq, q, q, const_cast<void*>(workspace),
+                               workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, causal))
+    return s;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (workspace == nullptr || !aligned16(workspace)) return FA_ERR_WORKSPACE;
-  if (workspace_bytes < fa_bwd_workspace_size(B, Hq, Nq, d)) return FA_ERR_WORKSPACE;
-  return hip_status(
-      fa::launch_bwd_post(static_cast<const float*>(workspace), dq, B, Hq, Nq, d, stream));
+  return hip_status(fa::launch_bwd_dq(q, k, v, dout, lse, static_cast<const float*>(workspace),
+                                      dq, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream));
 }
 
 fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
@@ -160,7 +157,7 @@ fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float
                                Hq, Hkv, Nq, Nk, d, scale, causal))
     return s;
   if (d != 64) return FA_ERR_UNSUPPORTED;
-  float* delta = ws_delta(workspace, B, Hq, Nq, d);
+  float* delta = static_cast<float*>(workspace);
   return hip_status(fa::launch_bwd_f32(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Nq,
                                        Nk, scale, causal != 0, stream));
 }

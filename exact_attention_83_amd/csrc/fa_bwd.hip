@@ -7,25 +7,12 @@
 // row statistics are kept from the forward).  The row term rowsum(P * dP)
 // equals dO_i . O_i, which a pre-pass computes from O and dO.
 //
-// bf16 main kernel, one workgroup per (b, KV head, 128-key tile):
-//   * wave w owns keys kv0 + 32w .. +32.  Its K and V rows stay in registers
-//     as MFMA B operands for S = Q K^T and dP = dO V^T (queries on the MFMA m
-//     axis, keys on n), and it accumulates dK and dV for those keys in
-//     registers over every query tile of every query head of the group.
-//   * the S and dP accumulators (query rows in registers, one key per lane)
-//     are directly the A operands of dV += P^T dO and dK += dS^T Q: their
-//     query index becomes the contraction index.  The other operands, dO^T and
-//     Q^T, are read from LDS where the query tile is also stored transposed.
-//   * dQ needs the contraction over all 128 keys, so each wave writes its dS
-//     block to LDS; after a barrier the waves split the 64 x d dQ tile, compute
-//     it from dS and K^T (resident in LDS) and add it into the fp32
-//     accumulator with atomics.
-//   * the next query tile is fetched into registers while the current one is
-//     processed.
-// Causal: KV tile j only visits query tiles that reach its keys, and only the
-// tiles crossing the diagonal are masked ([CH18] §18.5.2 (4): the skipped
-// gradients are structurally zero).  Work units are launched in ascending KV
-// tile order, i.e. longest first.
+// The bf16 path runs the delta pre-pass and then two kernels (see the
+// comment above bwd_dkdv_kernel).  Causal: a KV tile only visits the query
+// tiles that reach its keys, a query tile only the key tiles up to its last
+// row, and only tiles crossing the diagonal are masked ([CH18] §18.5.2 (4):
+// the skipped gradients are structurally zero).  Work units are launched
+// longest first.
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -33,13 +20,11 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// delta_i = sum_c dO_ic * O_ic; also zeroes the fp32 dQ accumulator row.
+// delta_i = sum_c dO_ic * O_ic.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ O,
                                                         const T* __restrict__ dO,
-                                                        float* __restrict__ delta,
-                                                        float* __restrict__ dq_accum,
-                                                        int rows) {
+                                                        float* __restrict__ delta, int rows) {
   // 16 threads per row, each owns D/16 consecutive elements.
   constexpr int E = D / 16;
   const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -50,27 +35,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ O,
     const T* gp = dO + (size_t)row * D + sub * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc = fmaf((float)op[e], (float)gp[e], acc);
-    if (dq_accum) {
-      float* zp = dq_accum + (size_t)row * D + sub * E;
-#pragma unroll
-      for (int e = 0; e < E; e += 4) stg<f32x4>(zp + e, f32x4{0.f, 0.f, 0.f, 0.f});
-    }
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
   if (row < rows && sub == 0) delta[row] = acc;
-}
-
-// dq_accum (fp32) -> dq (bf16), 8 elements per thread.
-__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ acc,
-                                                             uint16_t* __restrict__ dq,
-                                                             size_t n8) {
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  f32x4 a = ldg<f32x4>(acc + i * 8);
-  f32x4 b = ldg<f32x4>(acc + i * 8 + 4);
-  stg<u32x4>(dq + i * 8, u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]),
-                               pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3])});
 }
 
 // ---------------------------------------------------------------------------
@@ -197,41 +165,85 @@ __global__ __launch_bounds__(64) void bwd_f32_dkv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 main backward kernel.
+// bf16 backward: two kernels, no atomics.
+//   bwd_dkdv_kernel: one workgroup per (b, KV head, 128-key tile); dK and dV
+//     are accumulated on chip over every query tile of every query head of the
+//     group (4 products per tile pair: S, dP, dV, dK).
+//   bwd_dq_kernel: one workgroup per (b, query head, 256-row tile); dQ is
+//     accumulated on chip over the key tiles, exactly like O in the forward
+//     (3 products per tile pair: S, dP, dQ).
+// Recomputing S and dP in the dQ kernel costs 7 products per tile pair instead
+// of the 5 of a single kernel, but removes the fp32 dQ atomics (whose traffic,
+// B*H*(#tile pairs)*BQ*d*4 bytes, goes to memory on this multi-XCD device)
+// and the dS round trip through LDS.
 namespace {
-constexpr int kBwdBkv = 128;  // keys per workgroup (4 waves x 32)
-constexpr int kBwdBq = 64;    // query rows per inner tile
+constexpr int kKvWaves = 4;
+constexpr int kKvBkv = 32 * kKvWaves;  // keys per dK/dV work unit
+constexpr int kKvBq = 32;              // query rows per inner tile
+constexpr int kDqWaves = 8;
+constexpr int kDqBr = 32 * kDqWaves;   // query rows per dQ work unit
+constexpr int kDqBc = 64;              // keys per KV tile
 }  // namespace
 
+// Chunk swizzle of an LDS tile with ROWB-byte rows: chunk c of row r sits at
+// position c ^ bwd_swz<ROWB>(r).  Both b128 reads of 16 consecutive rows (one
+// chunk) and transposing reads of 4 consecutive rows x 4 chunks are free of
+// bank conflicts on the 64-bank LDS.
+template <int ROWB>
+__device__ __forceinline__ int bwd_swz(int r) {
+  return ROWB == 256 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                     : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Byte offset, within a row-major tile, that lane `lane` passes to the
+// transposing read (ds_read_b64_tr_b16) so that output lane i of its 16-lane
+// group receives elements (row r0 + e, col c0 + 16*((lane>>4)&1) + i), e=0..3,
+// with r0 = rb + 4*(lane>>5) (the lane half) and c0 a multiple of 32.
+template <int ROWB>
+__device__ __forceinline__ int tr_offset(int lane, int rb, int c0) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = rb + 4 * (g >> 1) + (j >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (j & 3);  // elements (bf16)
+  return row * ROWB + (((col >> 3) ^ bwd_swz<ROWB>(row)) << 4) + (col & 7) * 2;
+}
+
+// Source offset of direct-load block `blk` (1 KB) of a row-major tile with
+// ROWB-byte rows, for this lane: LDS position p of row r receives source
+// chunk p ^ swz(r).
+template <int ROWB>
+__device__ __forceinline__ int swz_src_offset(int lane, int blk) {
+  const int r = blk * (1024 / ROWB) + lane / (ROWB / 16);
+  const int p = lane % (ROWB / 16);
+  return r * ROWB + ((p ^ bwd_swz<ROWB>(r)) << 4);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  Wave w owns keys kv0 + 32w .. +32, whose K and V rows stay in
+// registers as MFMA B operands of S = Q K^T and dP = dO V^T (queries on the m
+// axis, keys on n).  The S and dP accumulators (query rows in registers, one
+// key per lane) are directly the A operands of dV += P^T dO and dK += dS^T Q;
+// their B operands are transposing reads of the row-major dO and Q tiles.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
+__global__ __launch_bounds__(kKvWaves * 64, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta,
-    float* __restrict__ dq_accum, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    int Hq, int Hkv, int Nq, int Nk, float scale, float scale_log2, int BHkv) {
-  constexpr int BQ = kBwdBq;
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk,
+    float scale, float scale_log2, int BHkv) {
+  constexpr int NW = kKvWaves;
+  constexpr int BQ = kKvBq;
+  constexpr int BKV = kKvBkv;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  constexpr int DCH = D / 8;                // 16-byte chunks per row
-  constexpr int RP = D * 2 + 16;            // row-major tile pitch (Q, dO)
-  constexpr int TP = BQ * 2 + 8;            // transposed tile pitch (Q^T, dO^T)
-  constexpr int SP = kBwdBkv * 2 + 16;      // dS pitch [q][key]
-  constexpr int KTP = kBwdBkv * 2 + 16;     // K^T pitch [d][key]
-  constexpr int OFF_Q = 0;
-  constexpr int OFF_QT = OFF_Q + BQ * RP;
-  constexpr int OFF_G = OFF_QT + D * TP;
-  constexpr int OFF_GT = OFF_G + BQ * RP;
-  constexpr int OFF_L = OFF_GT + D * TP;    // lse * log2(e)
-  constexpr int OFF_DL = OFF_L + BQ * 4;    // delta
-  constexpr int OFF_S = OFF_DL + BQ * 4;
-  constexpr int OFF_KT = OFF_S + BQ * SP;
-  constexpr int SMEM = OFF_KT + D * KTP;
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  constexpr int ROWB = D * 2;
+  constexpr int QTILE = BQ * ROWB;
+  constexpr int LPW = QTILE / 1024 / NW;  // direct loads per wave per Q (or dO) tile
+  constexpr int OFF_L = 4 * QTILE;        // 2 slots x (lse, delta) [BQ] fp32
+  __shared__ __attribute__((aligned(1024))) char smem[4 * QTILE + 4 * BQ * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -241,40 +253,65 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   const int b = bhk / Hkv;
   const int hk = bhk - b * Hkv;
   const int G = Hq / Hkv;
-  const int kv0 = jt * kBwdBkv;
+  const int kv0 = jt * BKV;
   const int mykey = kv0 + wave * 32 + l32;
   const int mykey_c = mykey < Nk ? mykey : Nk - 1;
 
-  const uint16_t* Kp = K + (size_t)bhk * Nk * D;
-  const uint16_t* Vp = V + (size_t)bhk * Nk * D;
-
-  // Resident K, V fragments (B operands with n = key, k = head dim).
+  // This lane's K and V row: B operands with n = key, k = head dim.
   u32x4 kf[KSTEPS], vf[KSTEPS];
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    kf[ks] = ldg<u32x4>(Kp + (size_t)mykey_c * D + ks * 16 + hf * 8);
-    vf[ks] = ldg<u32x4>(Vp + (size_t)mykey_c * D + ks * 16 + hf * 8);
-  }
-  // K^T for the whole workgroup in LDS (B operand of dQ = dS K).
   {
-    // thread: 4 keys x 8 head dims, written as 8-byte runs of keys.
-    for (int gidx = tid; gidx < (kBwdBkv / 4) * DCH; gidx += 256) {
-      const int rg = gidx / DCH, col = gidx - (gidx / DCH) * DCH;
-      u32x4 r[4];
+    const uint16_t* kr = K + ((size_t)bhk * Nk + mykey_c) * D;
+    const uint16_t* vr = V + ((size_t)bhk * Nk + mykey_c) * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int key = kv0 + rg * 4 + i;
-        key = key < Nk ? key : Nk - 1;
-        r[i] = ldg<u32x4>(Kp + (size_t)key * D + col * 8);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint32_t lo = (e & 1) ? pack_hi16(r[0][w], r[1][w]) : pack_lo16(r[0][w], r[1][w]);
-        uint32_t hi = (e & 1) ? pack_hi16(r[2][w], r[3][w]) : pack_lo16(r[2][w], r[3][w]);
-        lds_write<u32x2>(smem + OFF_KT, (col * 8 + e) * KTP + rg * 8, u32x2{lo, hi});
-      }
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      kf[ks] = ldg<u32x4>(kr + ks * 16 + hf * 8);
+      vf[ks] = ldg<u32x4>(vr + ks * 16 + hf * 8);
     }
+  }
+
+  const int nqt = (Nq + BQ - 1) / BQ;
+  const int qt_begin = CAUSAL ? kv0 / BQ : 0;
+  const int per_head = nqt - qt_begin;
+  const int total = per_head * G;
+  auto tile_head = [&](int it, int* bh, int* q0) {
+    const int gi = it / per_head;
+    *bh = b * Hq + hk * G + gi;
+    *q0 = (qt_begin + (it - gi * per_head)) * BQ;
+  };
+  int qoff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) qoff[i] = swz_src_offset<ROWB>(lane, wave * LPW + i);
+  auto issue = [&](int it, int slot) {
+    int bh, q0;
+    tile_head(it, &bh, &q0);
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * ROWB);
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc(dO + (size_t)bh * Nq * D, (uint32_t)Nq * ROWB);
+    char* qd = smem + slot * 2 * QTILE + wave * LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      buffer_load_lds16(rQ, qd + i * 1024, qoff[i], q0 * ROWB);
+      buffer_load_lds16(rG, qd + QTILE + i * 1024, qoff[i], q0 * ROWB);
+    }
+    if (wave < 2 && lane < BQ) {  // wave 0: lse, wave 1: delta
+      const float* src = (wave == 0 ? LSE : Delta) + (size_t)bh * Nq;
+      const __amdgpu_buffer_rsrc_t rL = make_rsrc(src, (uint32_t)Nq * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rL, (lds_void_t*)(smem + OFF_L + (slot * 2 + wave) * BQ * 4), 4, lane * 4, q0 * 4, 0, 0);
+    }
+  };
+
+  // A-operand rows of S / dP (b128): query l32, chunk 2*ks + hf.
+  int ard[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    ard[ks] = l32 * ROWB + (((2 * ks + hf) ^ bwd_swz<ROWB>(l32)) << 4);
+  // B operands of dV / dK (transposing reads of dO / Q), k-step st: query rows
+  // 16*st + 8*(e/4) + 4*hf + e%4, head dims 32*db + lane.
+  int trd0[DBLK], trd1[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    trd0[db] = tr_offset<ROWB>(lane, 0, 32 * db);
+    trd1[db] = tr_offset<ROWB>(lane, 8, 32 * db);
   }
 
   f32x16 dk[DBLK], dv[DBLK];
@@ -284,195 +321,65 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     dv[i] = f32x16{0};
   }
 
-  const int nqt = (Nq + BQ - 1) / BQ;
-  const int qt_begin = CAUSAL ? kv0 / BQ : 0;
-  const int per_head = nqt - qt_begin;
-  const int total = per_head * G;
-
-  // Query-tile staging: thread owns 4 consecutive rows x 8 head dims of Q and dO.
-  const int st_rg = tid / DCH;                 // row group
-  const int st_col = tid - st_rg * DCH;
-  const bool st_active = st_rg < BQ / 4;
-  u32x4 qreg[4], greg[4];
-  float lreg = 0.f;
-
-  auto tile_head = [&](int it, int* bh, int* q0) {
-    const int gi = it / per_head;
-    *bh = b * Hq + hk * G + gi;
-    *q0 = (qt_begin + (it - gi * per_head)) * BQ;
-  };
-  auto load_q = [&](int it) {
-    int bh, q0;
-    tile_head(it, &bh, &q0);
-    if (st_active) {
-      const uint16_t* qp = Q + (size_t)bh * Nq * D;
-      const uint16_t* gp = dO + (size_t)bh * Nq * D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int r = q0 + st_rg * 4 + i;
-        r = r < Nq ? r : Nq - 1;
-        qreg[i] = ldg<u32x4>(qp + (size_t)r * D + st_col * 8);
-        greg[i] = ldg<u32x4>(gp + (size_t)r * D + st_col * 8);
-      }
-    }
-    if (tid < 2 * BQ) {
-      int r = q0 + (tid & (BQ - 1));
-      r = r < Nq ? r : Nq - 1;
-      lreg = tid < BQ ? LSE[(size_t)bh * Nq + r] * kLog2e : Delta[(size_t)bh * Nq + r];
-    }
-  };
-  auto store_q = [&]() {
-    if (st_active) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lds_write<u32x4>(smem + OFF_Q, (st_rg * 4 + i) * RP + st_col * 16, qreg[i]);
-        lds_write<u32x4>(smem + OFF_G, (st_rg * 4 + i) * RP + st_col * 16, greg[i]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint32_t lo = (e & 1) ? pack_hi16(qreg[0][w], qreg[1][w]) : pack_lo16(qreg[0][w], qreg[1][w]);
-        uint32_t hi = (e & 1) ? pack_hi16(qreg[2][w], qreg[3][w]) : pack_lo16(qreg[2][w], qreg[3][w]);
-        lds_write<u32x2>(smem + OFF_QT, (st_col * 8 + e) * TP + st_rg * 8, u32x2{lo, hi});
-        lo = (e & 1) ? pack_hi16(greg[0][w], greg[1][w]) : pack_lo16(greg[0][w], greg[1][w]);
-        hi = (e & 1) ? pack_hi16(greg[2][w], greg[3][w]) : pack_lo16(greg[2][w], greg[3][w]);
-        lds_write<u32x2>(smem + OFF_GT, (st_col * 8 + e) * TP + st_rg * 8, u32x2{lo, hi});
-      }
-    }
-    if (tid < 2 * BQ) lds_write<float>(smem, OFF_L + tid * 4, lreg);
-  };
-
-  if (total > 0) {
-    load_q(0);
-    store_q();
-  }
-  __syncthreads();
-
+  if (total > 0) issue(0, 0);
   for (int it = 0; it < total; ++it) {
+    const int slot = it & 1;
     int bh, q0;
     tile_head(it, &bh, &q0);
-    if (it + 1 < total) load_q(it + 1);
+    wait_vmem();
+    lds_barrier();
+    if (it + 1 < total) issue(it + 1, slot ^ 1);
+    const char* qs = smem + slot * 2 * QTILE;
+    const char* gs = qs + QTILE;
+    const char* ls = smem + OFF_L + slot * 2 * BQ * 4;
 
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys: two 32-row blocks.
-    f32x16 s[2], dp[2];
+    f32x16 sb = f32x16{0}, dpb = f32x16{0};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = f32x16{0};
-      dp[qb] = f32x16{0};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int off = (qb * 32 + l32) * RP + (ks * 16 + hf * 8) * 2;
-        s[qb] = mfma_32x32x16_bf16(lds_read<u32x4>(smem + OFF_Q, off), kf[ks], s[qb]);
-        dp[qb] = mfma_32x32x16_bf16(lds_read<u32x4>(smem + OFF_G, off), vf[ks], dp[qb]);
-      }
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      sb = mfma_32x32x16_bf16(lds_read<u32x4>(qs, ard[ks]), kf[ks], sb);
+      dpb = mfma_32x32x16_bf16(lds_read<u32x4>(gs, ard[ks]), vf[ks], dpb);
     }
-
-    // P = exp(S*scale - lse) and dS = P (dP - delta).  Accumulator register r
-    // of block qb holds query row 32*qb + 8*(r/4) + 4*hf + r%4.
+    // P = exp(S*scale - lse), dS = P (dP - delta); register r holds query row
+    // 8*(r/4) + 4*hf + r%4 of the tile.
     const bool need_mask = (kv0 + wave * 32 + 32 > Nk) || (q0 + BQ > Nq) ||
                            (CAUSAL && kv0 + wave * 32 + 31 > q0);
-    u32x4 pa[2][2], dsa[2][2];
+    u32x4 pa[2], dsa[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float p[16], ds[16];
+    for (int g = 0; g < 4; ++g) {
+      const int qr = g * 8 + hf * 4;
+      const f32x4 lv = lds_read<f32x4>(ls, qr * 4);
+      const f32x4 dl = lds_read<f32x4>(ls, BQ * 4 + qr * 4);
+      float p[4], ds[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qr = qb * 32 + g * 8 + hf * 4;
-        f32x4 lv = lds_read<f32x4>(smem, OFF_L + qr * 4);
-        f32x4 dl = lds_read<f32x4>(smem, OFF_DL + qr * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = g * 4 + e;
-          float sv = s[qb][r];
-          if (need_mask) {
-            const int qi = q0 + qr + e;
-            if (mykey >= Nk || qi >= Nq || (CAUSAL && mykey > qi)) sv = -INFINITY;
-          }
-          p[r] = fast_exp2(fmaf(sv, scale_log2, -lv[e]));
-          ds[r] = p[r] * (dp[qb][r] - dl[e]);
+      for (int e = 0; e < 4; ++e) {
+        const int r = g * 4 + e;
+        float sv = sb[r];
+        if (need_mask) {
+          const int qi = q0 + qr + e;
+          sv = (mykey >= Nk || qi >= Nq || (CAUSAL && mykey > qi)) ? -INFINITY : sv;
         }
+        p[e] = fast_exp2(fmaf(sv, scale_log2, -lv[e] * kLog2e));
+        ds[e] = p[e] * (dpb[r] - dl[e]);
       }
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        pa[qb][st] = u32x4{pack_bf16(p[8 * st + 0], p[8 * st + 1]),
-                           pack_bf16(p[8 * st + 2], p[8 * st + 3]),
-                           pack_bf16(p[8 * st + 4], p[8 * st + 5]),
-                           pack_bf16(p[8 * st + 6], p[8 * st + 7])};
-        dsa[qb][st] = u32x4{pack_bf16(ds[8 * st + 0], ds[8 * st + 1]),
-                            pack_bf16(ds[8 * st + 2], ds[8 * st + 3]),
-                            pack_bf16(ds[8 * st + 4], ds[8 * st + 5]),
-                            pack_bf16(ds[8 * st + 6], ds[8 * st + 7])};
-      }
+      // register r = 4g + e is element e + 4*(g%2) of k-step g/2
+      pa[g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
+      pa[g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
+      dsa[g >> 1][2 * (g & 1)] = pack_bf16(ds[0], ds[1]);
+      dsa[g >> 1][2 * (g & 1) + 1] = pack_bf16(ds[2], ds[3]);
     }
-
-    // dV += P^T dO and dK += dS^T Q.  k-step (qb, st) element e of lane half
-    // hf is query row 32*qb + 16*st + 8*(e/4) + 4*hf + e%4.
+    // dV += P^T dO and dK += dS^T Q.
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int off = (db * 32 + l32) * TP + (qb * 32 + st * 16 + hf * 4) * 2;
-          u32x2 g0 = lds_read<u32x2>(smem + OFF_GT, off);
-          u32x2 g1 = lds_read<u32x2>(smem + OFF_GT, off + 16);
-          dv[db] = mfma_32x32x16_bf16(pa[qb][st], u32x4{g0[0], g0[1], g1[0], g1[1]}, dv[db]);
-          u32x2 q0v = lds_read<u32x2>(smem + OFF_QT, off);
-          u32x2 q1v = lds_read<u32x2>(smem + OFF_QT, off + 16);
-          dk[db] = mfma_32x32x16_bf16(dsa[qb][st], u32x4{q0v[0], q0v[1], q1v[0], q1v[1]}, dk[db]);
-        }
-
-    // dS -> LDS as [q][key] bf16 for the dQ product.  This wave's keys are
-    // columns 32*wave + l32; register r of block qb is query row
-    // 32*qb + 8*(r/4) + 4*hf + r%4.  The transposed register layout is
-    // recovered from the packed pairs: each packed word holds two query rows.
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t word = dsa[qb][st][w];
-          const int e0 = 2 * w;  // elements e0 and e0+1 of this k-step
-          const int r0 = qb * 32 + st * 16 + 8 * (e0 >> 2) + 4 * hf + (e0 & 3);
-          const int col = (wave * 32 + l32) * 2;
-          lds_write<uint16_t>(smem + OFF_S, r0 * SP + col, (uint16_t)(word & 0xffff));
-          lds_write<uint16_t>(smem + OFF_S, (r0 + 1) * SP + col, (uint16_t)(word >> 16));
-        }
-    __syncthreads();
-
-    // Next query tile into LDS (Q, dO regions are free now; dS and K^T are
-    // still being read below).
-    if (it + 1 < total) store_q();
-
-    // dQ = dS K over all 128 keys, then fp32 atomics.  The (query block,
-    // head-dim block) pairs of the 64 x D output are dealt to the 4 waves.
-    {
-      constexpr int PAIRS = 2 * DBLK;
-      constexpr int PPW = PAIRS / 4;
-#pragma unroll
-      for (int pi = 0; pi < PPW; ++pi) {
-        const int pr = wave * PPW + pi;
-        const int qb = pr / DBLK;
-        const int db = pr - qb * DBLK;
-        f32x16 dq = f32x16{0};
-#pragma unroll
-        for (int kk = 0; kk < kBwdBkv / 16; ++kk) {
-          const u32x4 bk =
-              lds_read<u32x4>(smem + OFF_KT, (db * 32 + l32) * KTP + (kk * 16 + hf * 8) * 2);
-          const u32x4 a =
-              lds_read<u32x4>(smem + OFF_S, (qb * 32 + l32) * SP + (kk * 16 + hf * 8) * 2);
-          dq = mfma_32x32x16_bf16(a, bk, dq);
-        }
-        float* dqp = dq_accum + (size_t)bh * Nq * D + db * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = q0 + qb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (qi < Nq) atomicAdd(dqp + (size_t)qi * D, dq[r] * scale);
-        }
+      for (int db = 0; db < DBLK; ++db) {
+        const int ro = st * 16 * ROWB;
+        const u32x2 g0 = lds_read_tr16(gs + ro + trd0[db]);
+        const u32x2 g1 = lds_read_tr16(gs + ro + trd1[db]);
+        dv[db] = mfma_32x32x16_bf16(pa[st], u32x4{g0[0], g0[1], g1[0], g1[1]}, dv[db]);
+        const u32x2 q0v = lds_read_tr16(qs + ro + trd0[db]);
+        const u32x2 q1v = lds_read_tr16(qs + ro + trd1[db]);
+        dk[db] = mfma_32x32x16_bf16(dsa[st], u32x4{q0v[0], q0v[1], q1v[0], q1v[1]}, dk[db]);
       }
-    }
-    __syncthreads();
   }
 
   // dK = scale * sum dS^T Q, dV = sum P^T dO.  Accumulator register r of block
@@ -493,6 +400,164 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dQ.  The forward's structure with keys on the MFMA m axis: S^T = K Q^T and
+// dP^T = V dO^T with this wave's 32 queries on n (Q and dO rows in registers),
+// so lse and delta are per-lane scalars; dS^T (rounded to bf16) is the B
+// operand of dQ^T += K^T dS^T, whose A operand is a transposing read of the
+// row-major K tile.  K/V tiles of 64 keys are double-buffered in LDS.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta,
+    uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, float scale, float scale_log2,
+    int BH, int nqt) {
+  constexpr int NW = kDqWaves;
+  constexpr int BR = kDqBr;
+  constexpr int BC = kDqBc;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int TILE = BC * ROWB;
+  constexpr int LPW = TILE / 1024 / NW;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // 2 slots x (K, V)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  int bh, qt;
+  query_tile_of(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
+  const int b = bh / Hq;
+  const int h = bh - b * Hq;
+  const int hk = h / (Hq / Hkv);
+  const size_t kv_off = (size_t)(b * Hkv + hk) * Nk * D;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kv_off, (uint32_t)Nk * ROWB);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * ROWB);
+
+  const int q0 = qt * BR;
+  const int qrow = q0 + wave * 32 + l32;
+  const int qrow_c = qrow < Nq ? qrow : Nq - 1;
+  u32x4 qf[KSTEPS], gf[KSTEPS];
+  {
+    const uint16_t* qr = Q + ((size_t)bh * Nq + qrow_c) * D;
+    const uint16_t* gr = dO + ((size_t)bh * Nq + qrow_c) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      qf[ks] = ldg<u32x4>(qr + ks * 16 + hf * 8);
+      gf[ks] = ldg<u32x4>(gr + ks * 16 + hf * 8);
+    }
+  }
+  const float lse2 = LSE[(size_t)bh * Nq + qrow_c] * kLog2e;
+  const float dlt = Delta[(size_t)bh * Nq + qrow_c];
+
+  const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  int ldo[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) ldo[i] = swz_src_offset<ROWB>(lane, wave * LPW + i);
+  auto issue = [&](int j, int slot) {
+    char* d = smem + slot * 2 * TILE + wave * LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      buffer_load_lds16(rK, d + i * 1024, ldo[i], j * TILE);
+      buffer_load_lds16(rV, d + TILE + i * 1024, ldo[i], j * TILE);
+    }
+  };
+  // A operands of S^T / dP^T (b128): key row kb*32 + l32, chunk 2*ks + hf.
+  int ard[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    ard[ks] = l32 * ROWB + (((2 * ks + hf) ^ bwd_swz<ROWB>(l32)) << 4);
+  // A operand of dQ^T (transposing read of K): k-step (kb, st) element e of
+  // lane half hf is key kb*32 + 16*st + 8*(e/4) + 4*hf + e%4.
+  int trd0[DBLK], trd1[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    trd0[db] = tr_offset<ROWB>(lane, 0, 32 * db);
+    trd1[db] = tr_offset<ROWB>(lane, 8, 32 * db);
+  }
+
+  f32x16 dq[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) dq[i] = f32x16{0};
+
+  issue(0, 0);
+  for (int j = 0; j < ntiles; ++j) {
+    const int slot = j & 1;
+    wait_vmem();
+    lds_barrier();
+    if (j + 1 < ntiles) issue(j + 1, slot ^ 1);
+    const char* ks_ = smem + slot * 2 * TILE;
+    const char* vs_ = ks_ + TILE;
+    const int kv0 = j * BC;
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{0};
+      dp[kb] = f32x16{0};
+    }
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma_32x32x16_bf16(lds_read<u32x4>(ks_, kb * 32 * ROWB + ard[kk]), qf[kk], s[kb]);
+        dp[kb] = mfma_32x32x16_bf16(lds_read<u32x4>(vs_, kb * 32 * ROWB + ard[kk]), gf[kk], dp[kb]);
+      }
+    const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
+    u32x4 dsb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float sv = s[kb][r];
+        if (need_mask) {
+          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          sv = (key >= Nk || (CAUSAL && key > qrow)) ? -INFINITY : sv;
+        }
+        const float p = fast_exp2(fmaf(sv, scale_log2, -lse2));
+        ds[r] = p * (dp[kb][r] - dlt);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        dsb[kb][st] = u32x4{pack_bf16(ds[8 * st + 0], ds[8 * st + 1]),
+                            pack_bf16(ds[8 * st + 2], ds[8 * st + 3]),
+                            pack_bf16(ds[8 * st + 4], ds[8 * st + 5]),
+                            pack_bf16(ds[8 * st + 6], ds[8 * st + 7])};
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const char* kp = ks_ + (kb * 32 + st * 16) * ROWB;
+          const u32x2 a0 = lds_read_tr16(kp + trd0[db]);
+          const u32x2 a1 = lds_read_tr16(kp + trd1[db]);
+          dq[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, dsb[kb][st], dq[db]);
+        }
+  }
+
+  // dQ = scale * dQ^T, written as bf16 rows.
+  if (qrow < Nq) {
+    uint16_t* op = dQ + ((size_t)bh * Nq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + g * 8 + hf * 4;
+        stg<u32x2>(op + d0, u32x2{pack_bf16(dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale),
+                                  pack_bf16(dq[db][4 * g + 2] * scale, dq[db][4 * g + 3] * scale)});
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                           const float* dout, const float* lse, float* dq, float* dk, float* dv,
@@ -500,7 +565,7 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
                           bool causal, hipStream_t stream) {
   const int rows = B * Hq * Nq;
   hipLaunchKernelGGL((bwd_delta_kernel<float, 64>), dim3((rows + 15) / 16), dim3(256), 0,
-                     stream, o, dout, delta, (float*)nullptr, rows);
+                     stream, o, dout, delta, rows);
   hipLaunchKernelGGL(bwd_f32_dq_kernel, dim3((Nq + kBF32T - 1) / kBF32T, B * Hq), dim3(64), 0,
                      stream, q, k, v, dout, lse, delta, dq, Hq, Hkv, Nq, Nk, scale,
                      causal ? 1 : 0);
@@ -509,26 +574,26 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_pre(const void* o, const void* dout, float* dq_accum, float* delta, int B,
-                          int Hq, int Nq, int d, hipStream_t stream) {
+hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int B, int Hq, int Nq,
+                          int d, hipStream_t stream) {
   const int rows = B * Hq * Nq;
   const __bf16* ob = (const __bf16*)o;
   const __bf16* gb = (const __bf16*)dout;
   if (d == 128)
     hipLaunchKernelGGL((bwd_delta_kernel<__bf16, 128>), dim3((rows + 15) / 16), dim3(256), 0,
-                       stream, ob, gb, delta, dq_accum, rows);
+                       stream, ob, gb, delta, rows);
   else
     hipLaunchKernelGGL((bwd_delta_kernel<__bf16, 64>), dim3((rows + 15) / 16), dim3(256), 0,
-                       stream, ob, gb, delta, dq_accum, rows);
+                       stream, ob, gb, delta, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                           const float* lse, const float* delta, float* dq_accum, void* dk,
-                           void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                           bool causal, hipStream_t stream) {
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                           const float* lse, const float* delta, void* dk, void* dv, int B,
+                           int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal,
+                           hipStream_t stream) {
   const int BHkv = B * Hkv;
-  dim3 grid(BHkv * ((Nk + kBwdBkv - 1) / kBwdBkv)), block(256);
+  dim3 grid(BHkv * ((Nk + kKvBkv - 1) / kKvBkv)), block(kKvWaves * 64);
   auto Q = (const uint16_t*)q;
   auto K = (const uint16_t*)k;
   auto V = (const uint16_t*)v;
@@ -536,29 +601,43 @@ hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const vo
   auto dK = (uint16_t*)dk;
   auto dV = (uint16_t*)dv;
   const float sl2 = scale * kLog2e;
+#define FA_LAUNCH_DKDV(DD, CC)                                                                   \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, Q, K, V, G, lse, delta, \
+                     dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv)
   if (d == 128) {
-    if (causal)
-      hipLaunchKernelGGL((bwd_bf16_kernel<128, true>), grid, block, 0, stream, Q, K, V, G, lse,
-                         delta, dq_accum, dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv);
-    else
-      hipLaunchKernelGGL((bwd_bf16_kernel<128, false>), grid, block, 0, stream, Q, K, V, G, lse,
-                         delta, dq_accum, dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv);
+    if (causal) FA_LAUNCH_DKDV(128, true);
+    else FA_LAUNCH_DKDV(128, false);
   } else {
-    if (causal)
-      hipLaunchKernelGGL((bwd_bf16_kernel<64, true>), grid, block, 0, stream, Q, K, V, G, lse,
-                         delta, dq_accum, dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv);
-    else
-      hipLaunchKernelGGL((bwd_bf16_kernel<64, false>), grid, block, 0, stream, Q, K, V, G, lse,
-                         delta, dq_accum, dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv);
+    if (causal) FA_LAUNCH_DKDV(64, true);
+    else FA_LAUNCH_DKDV(64, false);
   }
+#undef FA_LAUNCH_DKDV
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_post(const float* dq_accum, void* dq, int B, int Hq, int Nq, int d,
-                           hipStream_t stream) {
-  const size_t n8 = (size_t)B * Hq * Nq * d / 8;
-  hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
-                     stream, dq_accum, (uint16_t*)dq, n8);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                         int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream) {
+  const int BH = B * Hq;
+  const int nqt = (Nq + kDqBr - 1) / kDqBr;
+  dim3 grid(BH * nqt), block(kDqWaves * 64);
+  auto Q = (const uint16_t*)q;
+  auto K = (const uint16_t*)k;
+  auto V = (const uint16_t*)v;
+  auto G = (const uint16_t*)dout;
+  auto dQ = (uint16_t*)dq;
+  const float sl2 = scale * kLog2e;
+#define FA_LAUNCH_DQ(DD, CC)                                                                   \
+  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, Q, K, V, G, lse, delta, \
+                     dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt)
+  if (d == 128) {
+    if (causal) FA_LAUNCH_DQ(128, true);
+    else FA_LAUNCH_DQ(128, false);
+  } else {
+    if (causal) FA_LAUNCH_DQ(64, true);
+    else FA_LAUNCH_DQ(64, false);
+  }
+#undef FA_LAUNCH_DQ
   return hipGetLastError();
 }
 

@@ -81,6 +81,21 @@ __device__ __forceinline__ void lds_write(char* base, int off, T v) {
   *reinterpret_cast<T*>(base + off) = v;
 }
 
+// Work order of query-tile work units: longest first under causal masking
+// ([L21] slides 27-46).  Consecutive units walk the (b,h) index fastest, so
+// units of one (b,h) land on the same XCD (workgroups are dealt round-robin
+// over the 8 XCDs) and share K/V in its L2.
+__host__ __device__ inline void query_tile_of(int t, int BH, int nqt, bool causal, int* bh,
+                                              int* qt) {
+  *bh = t % BH;
+  *qt = causal ? (nqt - 1 - t / BH) : (t / BH);
+}
+
+template <int N>
+struct IntConst {
+  static constexpr int value = N;
+};
+
 // ---------------------------------------------------------------------------
 // Direct global -> LDS loads and transposing LDS reads (gfx950).
 

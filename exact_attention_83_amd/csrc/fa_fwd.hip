@@ -37,25 +37,10 @@ constexpr int kFwdStages = 3;           // K/V tiles in flight
 
 }  // namespace
 
-// Dispatch order of the forward's work units: longest first for causal
-// ([L21] slides 27-46).  Consecutive units walk the (b,h) index fastest, so
-// units of one (b,h) land on the same XCD (workgroups are dealt round-robin
-// over the 8 XCDs) and share K/V in its L2.
-__host__ __device__ inline void fwd_tile_of(int t, int BH, int nqt, bool causal, int* bh,
-                                            int* qt) {
-  *bh = t % BH;
-  *qt = causal ? (nqt - 1 - t / BH) : (t / BH);
-}
-
 int fwd_kv_tiles(int qt, int Nk, bool causal, int br, int bc) {
   int last = causal ? ((qt + 1) * br < Nk ? (qt + 1) * br : Nk) : Nk;
   return (last + bc - 1) / bc;
 }
-
-template <int N>
-struct IntConst {
-  static constexpr int value = N;
-};
 
 // Chunk swizzles of the K and V tiles (see fwd_bf16_kernel).  K: rows r..r+15
 // read one chunk each; V: rows 4i..4i+3 read four consecutive chunks each.
@@ -96,7 +81,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   const int hf = lane >> 5;
 
   int bh, qt;
-  fwd_tile_of(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
+  query_tile_of(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int hk = h / (Hq / Hkv);
@@ -454,7 +439,7 @@ int fwd_schedule(int B, int Hq, int Nq, int Nk, bool causal, int* bh_out, int* q
     if (capacity < n) return -1;
     for (int t = 0; t < n; ++t) {
       int bh, qt;
-      fwd_tile_of(t, BH, nqt, causal, &bh, &qt);
+      query_tile_of(t, BH, nqt, causal, &bh, &qt);
       if (bh_out) bh_out[t] = bh;
       if (qt_out) qt_out[t] = qt;
       if (cost_out) cost_out[t] = fwd_kv_tiles(qt, Nk, causal, kFwdBr, kFwdBc);

@@ -22,14 +22,15 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
                           const float* dout, const float* lse, float* dq, float* dk, float* dv,
                           float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
                           bool causal, hipStream_t stream);
-hipError_t launch_bwd_pre(const void* o, const void* dout, float* dq_accum, float* delta, int B,
-                          int Hq, int Nq, int d, hipStream_t stream);
-hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                           const float* lse, const float* delta, float* dq_accum, void* dk,
-                           void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                           bool causal, hipStream_t stream);
-hipError_t launch_bwd_post(const float* dq_accum, void* dq, int B, int Hq, int Nq, int d,
+hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int B, int Hq, int Nq,
+                          int d, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                           const float* lse, const float* delta, void* dk, void* dv, int B,
+                           int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal,
                            hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                         int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream);
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
                                float* lse_part, int B, int Hq, int Hkv, int Nk, int d,

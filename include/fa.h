@@ -84,9 +84,8 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
                      float scale, int causal, hipStream_t stream);
 
 /*
- * Bytes of workspace fa_bwd / fa_bwd_f32 need: an fp32 dQ accumulator
- * [B][Hq][Nq][d] and the fp32 row term delta [B][Hq][Nq], each rounded up to
- * 256 bytes.
+ * Bytes of workspace fa_bwd / fa_bwd_f32 need: the fp32 row term delta
+ * [B][Hq][Nq], rounded up to 256 bytes.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
 
@@ -99,11 +98,10 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
  *   workspace: at least fa_bwd_workspace_size(B,Hq,Nq,d) bytes, 16-byte
  *   aligned; its contents on entry do not matter.
  * Three launches on `stream`: delta_i = dO_i . O_i (equal to rowsum(P * dP),
- * [CH18] §18.4.4) together with zeroing of the dQ accumulator; the main
- * kernel, one work unit per KV tile, which accumulates dK, dV on chip and adds
- * dQ into the fp32 accumulator with atomics; and the dQ conversion to bf16.
- * dQ is therefore reproducible only up to fp32 rounding order.
- *   d == 128 (and 64).
+ * [CH18] §18.4.4); dK and dV, one work unit per KV tile accumulating over the
+ * query tiles; dQ, one work unit per query tile accumulating over the KV
+ * tiles.  No atomics: results are deterministic.
+ *   d in {64, 128}.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse,
@@ -114,23 +112,26 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * The three stages of fa_bwd as separate calls, for callers that schedule or
- * time them individually.  Same arguments and workspace as fa_bwd; running
- * fa_bwd_pre, fa_bwd_main and fa_bwd_post in that order on one stream is
+ * time them individually.  Same arguments and workspace as fa_bwd; fa_bwd_pre
+ * must precede the other two on the stream (or be ordered before them), which
+ * are independent of each other.  fa_bwd_pre + fa_bwd_dkdv + fa_bwd_dq is
  * exactly fa_bwd.
- *   fa_bwd_pre:  delta_i = dO_i . O_i into the workspace and zeroing of the
- *                fp32 dQ accumulator ([CH18] §18.4.4: the row term of the
- *                softmax backward, rowsum(P * dP), equals dO_i . O_i).
- *   fa_bwd_main: dK, dV written; dQ accumulated (fp32) into the workspace.
- *   fa_bwd_post: dQ accumulator -> dq (bf16, nearest-even).
+ *   fa_bwd_pre:  delta_i = dO_i . O_i into the workspace ([CH18] §18.4.4: the
+ *                row term of the softmax backward, rowsum(P * dP), equals
+ *                dO_i . O_i).
+ *   fa_bwd_dkdv: dk and dv written.
+ *   fa_bwd_dq:   dq written.
  */
 fa_status fa_bwd_pre(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Nq, int d, hipStream_t stream);
-fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                      const float* lse, void* dk, void* dv, void* workspace,
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv, const void* workspace,
                       size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                       float scale, int causal, hipStream_t stream);
-fa_status fa_bwd_post(const void* workspace, size_t workspace_bytes, void* dq, int B, int Hq,
-                      int Nq, int d, hipStream_t stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, void* dq, const void* workspace, size_t workspace_bytes,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                    hipStream_t stream);
 
 /* Backward, fp32 tensors, d == 64.  Same meaning as fa_bwd; deterministic. */
 fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,

@@ -76,7 +76,7 @@ def test_bwd_validation_and_workspace(lib):
     B, Hq, Hkv, N, d = 2, 4, 2, 100, 128
     need = lib.fa_bwd_workspace_size(B, Hq, N, d)
     rows = B * Hq * N
-    assert need == ((rows * d * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert need == ((rows * 4 + 255) // 256) * 256
     assert lib.fa_bwd_workspace_size(0, Hq, N, d) == 0
 
     def call(ws=FAKE, ws_bytes=need, **kw):
@@ -140,9 +140,10 @@ def test_forward_schedule_is_lpt_permutation(lib, B, H, N, d, causal):
     assert sorted(zip(bh, qt)) == [(x, y) for x in range(B * H) for y in range(nqt)]
     assert all(a >= b for a, b in zip(cost, cost[1:])), "not longest-first"
     # costs agree with the oracle's count of KV tiles per causal query tile
-    br = N // nqt if N % nqt == 0 else None
+    # (query tiles are a power-of-two number of rows, KV tiles 64 keys)
+    br = 1 << math.ceil(math.log2(math.ceil(N / nqt)))
     if causal:
-        ref = SCH.causal_tile_costs(1, nqt, 128, 64)
+        ref = SCH.causal_tile_costs(1, nqt, br, 64)
         assert all(cost[i] == ref[qt[i]] for i in range(len(cost)))
 
 
