@@ -23,10 +23,9 @@ LIB = os.path.join(PKG, "libfa.so")
 
 ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fp8.hip"]
-# Per-file code generation options.  The backward kernel keeps more live
-# values than the 256 architectural VGPRs; with MFMA results in VGPR form the
-# overflow is spilled to AGPRs (cheap) instead of the register allocator
-# bouncing MFMA accumulators between AGPRs and VGPRs around every product.
+# Per-file code generation options.  In the backward kernels the products whose
+# results feed VALU work (S, dP) take VGPR accumulators; the long-lived dK/dV
+# accumulators are pinned to AGPRs in the source.
 EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU ops.

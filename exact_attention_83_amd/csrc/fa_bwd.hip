@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dkv_kernel(
 
 // ---------------------------------------------------------------------------
 // bf16 backward: two kernels, no atomics.
-//   bwd_dkdv_kernel: one workgroup per (b, KV head, 128-key tile); dK and dV
+//   bwd_dkdv_kernel: one workgroup per (b, KV head, 256-key tile); dK and dV
 //     are accumulated on chip over every query tile of every query head of the
 //     group (4 products per tile pair: S, dP, dV, dK).
 //   bwd_dq_kernel: one workgroup per (b, query head, 256-row tile); dQ is
@@ -178,7 +178,8 @@ __global__ __launch_bounds__(64) void bwd_f32_dkv_kernel(
 // and the dS round trip through LDS.
 namespace {
 constexpr int kKvWaves = 4;
-constexpr int kKvBkv = 32 * kKvWaves;  // keys per dK/dV work unit
+constexpr int kKvKb = 2;                         // 32-key blocks per wave
+constexpr int kKvBkv = 32 * kKvKb * kKvWaves;    // keys per dK/dV work unit
 constexpr int kKvBq = 32;              // query rows per inner tile
 constexpr int kDqWaves = 8;
 constexpr int kDqBr = 32 * kDqWaves;   // query rows per dQ work unit
@@ -217,20 +218,44 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk) {
   return r * ROWB + ((p ^ bwd_swz<ROWB>(r)) << 4);
 }
 
+// dK/dV accumulation with the accumulator pinned to the accumulation registers
+// (AGPRs).  The compiler's own register assignment cannot hold these 256
+// accumulators there next to the S/dP products, and shuffles them between
+// register files around every product instead.  The leading s_nop provides
+// the two wait states the hardware requires between a VALU write of an A/B
+// operand and its read by a matrix instruction, which the compiler cannot see
+// through inline assembly; LDS results are waited for by the compiler as for
+// any other use.
+__device__ __forceinline__ void mfma_acc_pinned(f32x16& c, u32x4 a, u32x4 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// Wait states between the last pinned product and any read of its result by
+// a non-matrix instruction (more than the 19 the longest product needs).
+__device__ __forceinline__ void mfma_acc_drain(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c));
+}
+
 // ---------------------------------------------------------------------------
-// dK, dV.  Wave w owns keys kv0 + 32w .. +32, whose K and V rows stay in
-// registers as MFMA B operands of S = Q K^T and dP = dO V^T (queries on the m
-// axis, keys on n).  The S and dP accumulators (query rows in registers, one
-// key per lane) are directly the A operands of dV += P^T dO and dK += dS^T Q;
-// their B operands are transposing reads of the row-major dO and Q tiles.
+// dK, dV.  Wave w owns KB blocks of 32 keys, kv0 + 32*KB*w + 32*kb + (0..31),
+// whose K and V rows stay in registers as MFMA B operands of S = Q K^T and
+// dP = dO V^T (queries on the m axis, keys on n).  Each A operand read from
+// LDS (a Q or dO row chunk) feeds one product per key block, which halves the
+// LDS read traffic per product at KB = 2: with one LDS operand per product
+// the LDS read bandwidth, not the matrix cores, bounds the kernel.  The S and
+// dP accumulators (query rows in registers, one key per lane) are directly the
+// A operands of dV += P^T dO and dK += dS^T Q; their B operands are
+// transposing reads of the row-major dO and Q tiles, again shared by the key
+// blocks.  The dK/dV accumulators (256 registers at d = 128) live in the
+// accumulation registers, so one wave runs per SIMD.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kKvWaves * 64, 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk,
     float scale, float scale_log2, int BHkv) {
   constexpr int NW = kKvWaves;
+  constexpr int KB = kKvKb;
   constexpr int BQ = kKvBq;
   constexpr int BKV = kKvBkv;
   constexpr int KSTEPS = D / 16;
@@ -238,8 +263,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 2) void bwd_dkdv_kernel(
   constexpr int ROWB = D * 2;
   constexpr int QTILE = BQ * ROWB;
   constexpr int LPW = QTILE / 1024 / NW;  // direct loads per wave per Q (or dO) tile
-  constexpr int OFF_L = 4 * QTILE;        // 2 slots x (lse, delta) [BQ] fp32
-  __shared__ __attribute__((aligned(1024))) char smem[4 * QTILE + 4 * BQ * 4];
+  constexpr int SLOT = 2 * QTILE + 2 * BQ * 4;  // Q, dO, lse, delta
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -254,18 +279,19 @@ __global__ __launch_bounds__(kKvWaves * 64, 2) void bwd_dkdv_kernel(
   const int hk = bhk - b * Hkv;
   const int G = Hq / Hkv;
   const int kv0 = jt * BKV;
-  const int mykey = kv0 + wave * 32 + l32;
-  const int mykey_c = mykey < Nk ? mykey : Nk - 1;
+  const int kbase = kv0 + wave * 32 * KB;
 
-  // This lane's K and V row: B operands with n = key, k = head dim.
-  u32x4 kf[KSTEPS], vf[KSTEPS];
-  {
-    const uint16_t* kr = K + ((size_t)bhk * Nk + mykey_c) * D;
-    const uint16_t* vr = V + ((size_t)bhk * Nk + mykey_c) * D;
+  // This lane's K and V rows: B operands with n = key, k = head dim.
+  u32x4 kf[KB][KSTEPS], vf[KB][KSTEPS];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = min(kbase + kb * 32 + l32, Nk - 1);
+    const uint16_t* kr = K + ((size_t)bhk * Nk + key) * D;
+    const uint16_t* vr = V + ((size_t)bhk * Nk + key) * D;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      kf[ks] = ldg<u32x4>(kr + ks * 16 + hf * 8);
-      vf[ks] = ldg<u32x4>(vr + ks * 16 + hf * 8);
+      kf[kb][ks] = ldg<u32x4>(kr + ks * 16 + hf * 8);
+      vf[kb][ks] = ldg<u32x4>(vr + ks * 16 + hf * 8);
     }
   }
 
@@ -286,7 +312,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 2) void bwd_dkdv_kernel(
     tile_head(it, &bh, &q0);
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * ROWB);
     const __amdgpu_buffer_rsrc_t rG = make_rsrc(dO + (size_t)bh * Nq * D, (uint32_t)Nq * ROWB);
-    char* qd = smem + slot * 2 * QTILE + wave * LPW * 1024;
+    char* qd = smem + slot * SLOT + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       buffer_load_lds16(rQ, qd + i * 1024, qoff[i], q0 * ROWB);
@@ -296,7 +322,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 2) void bwd_dkdv_kernel(
       const float* src = (wave == 0 ? LSE : Delta) + (size_t)bh * Nq;
       const __amdgpu_buffer_rsrc_t rL = make_rsrc(src, (uint32_t)Nq * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rL, (lds_void_t*)(smem + OFF_L + (slot * 2 + wave) * BQ * 4), 4, lane * 4, q0 * 4, 0, 0);
+          rL, (lds_void_t*)(smem + slot * SLOT + 2 * QTILE + wave * BQ * 4), 4, lane * 4, q0 * 4,
+          0, 0);
     }
   };
 
@@ -314,12 +341,14 @@ __global__ __launch_bounds__(kKvWaves * 64, 2) void bwd_dkdv_kernel(
     trd1[db] = tr_offset<ROWB>(lane, 8, 32 * db);
   }
 
-  f32x16 dk[DBLK], dv[DBLK];
+  f32x16 dk[KB][DBLK], dv[KB][DBLK];
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) {
-    dk[i] = f32x16{0};
-    dv[i] = f32x16{0};
-  }
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) {
+      dk[kb][i] = f32x16{0};
+      dv[kb][i] = f32x16{0};
+    }
 
   if (total > 0) issue(0, 0);
   for (int it = 0; it < total; ++it) {
@@ -329,74 +358,113 @@ __global__ __launch_bounds__(kKvWaves * 64, 2) void bwd_dkdv_kernel(
     wait_vmem();
     lds_barrier();
     if (it + 1 < total) issue(it + 1, slot ^ 1);
-    const char* qs = smem + slot * 2 * QTILE;
+    const char* qs = smem + slot * SLOT;
     const char* gs = qs + QTILE;
-    const char* ls = smem + OFF_L + slot * 2 * BQ * 4;
+    const char* ls = qs + 2 * QTILE;
 
-    f32x16 sb = f32x16{0}, dpb = f32x16{0};
+    f32x16 sb[KB], dpb[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sb[kb] = f32x16{0};
+      dpb[kb] = f32x16{0};
+    }
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      sb = mfma_32x32x16_bf16(lds_read<u32x4>(qs, ard[ks]), kf[ks], sb);
-      dpb = mfma_32x32x16_bf16(lds_read<u32x4>(gs, ard[ks]), vf[ks], dpb);
-    }
-    // P = exp(S*scale - lse), dS = P (dP - delta); register r holds query row
-    // 8*(r/4) + 4*hf + r%4 of the tile.
-    const bool need_mask = (kv0 + wave * 32 + 32 > Nk) || (q0 + BQ > Nq) ||
-                           (CAUSAL && kv0 + wave * 32 + 31 > q0);
-    u32x4 pa[2], dsa[2];
+      const u32x4 qa = lds_read<u32x4>(qs, ard[ks]);
+      const u32x4 ga = lds_read<u32x4>(gs, ard[ks]);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int qr = g * 8 + hf * 4;
-      const f32x4 lv = lds_read<f32x4>(ls, qr * 4);
-      const f32x4 dl = lds_read<f32x4>(ls, BQ * 4 + qr * 4);
-      float p[4], ds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = g * 4 + e;
-        float sv = sb[r];
-        if (need_mask) {
-          const int qi = q0 + qr + e;
-          sv = (mykey >= Nk || qi >= Nq || (CAUSAL && mykey > qi)) ? -INFINITY : sv;
-        }
-        p[e] = fast_exp2(fmaf(sv, scale_log2, -lv[e] * kLog2e));
-        ds[e] = p[e] * (dpb[r] - dl[e]);
+      for (int kb = 0; kb < KB; ++kb) {
+        sb[kb] = mfma_32x32x16_bf16(qa, kf[kb][ks], sb[kb]);
+        dpb[kb] = mfma_32x32x16_bf16(ga, vf[kb][ks], dpb[kb]);
       }
-      // register r = 4g + e is element e + 4*(g%2) of k-step g/2
-      pa[g >> 1][2 * (g & 1)] = pack_bf16(p[0], p[1]);
-      pa[g >> 1][2 * (g & 1) + 1] = pack_bf16(p[2], p[3]);
-      dsa[g >> 1][2 * (g & 1)] = pack_bf16(ds[0], ds[1]);
-      dsa[g >> 1][2 * (g & 1) + 1] = pack_bf16(ds[2], ds[3]);
     }
-    // dV += P^T dO and dK += dS^T Q.
+    // Mask keys past Nk, rows past Nq and (causal) keys after the query;
+    // register r of block kb holds query row 8*(r/4) + 4*hf + r%4 of the tile.
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int kb = 0; kb < KB; ++kb) {
+      const int key = kbase + kb * 32 + l32;
+      if ((kbase + kb * 32 + 32 > Nk) || (q0 + BQ > Nq) ||
+          (CAUSAL && kbase + kb * 32 + 31 > q0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = q0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= Nk || qi >= Nq || (CAUSAL && key > qi)) sb[kb][r] = -INFINITY;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // P = exp(S*scale - lse), dS = P (dP - delta) for query rows 16*st ..
+      // +16; register r holds query row 8*(r/4) + 4*hf + r%4 of the tile, and
+      // registers 8*st .. 8*st+7 form the A operand of k-step st.
+      u32x4 pa[KB], dsa[KB];
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * st + gg;
+        const int qr = g * 8 + hf * 4;
+        const f32x4 lv = lds_read<f32x4>(ls, qr * 4);
+        const f32x4 dl = lds_read<f32x4>(ls, BQ * 4 + qr * 4);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          float p[4], ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = g * 4 + e;
+            p[e] = fast_exp2(fmaf(sb[kb][r], scale_log2, -lv[e] * kLog2e));
+            ds[e] = p[e] * (dpb[kb][r] - dl[e]);
+          }
+          pa[kb][2 * gg] = pack_bf16(p[0], p[1]);
+          pa[kb][2 * gg + 1] = pack_bf16(p[2], p[3]);
+          dsa[kb][2 * gg] = pack_bf16(ds[0], ds[1]);
+          dsa[kb][2 * gg + 1] = pack_bf16(ds[2], ds[3]);
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q for this k-step.
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         const int ro = st * 16 * ROWB;
         const u32x2 g0 = lds_read_tr16(gs + ro + trd0[db]);
         const u32x2 g1 = lds_read_tr16(gs + ro + trd1[db]);
-        dv[db] = mfma_32x32x16_bf16(pa[st], u32x4{g0[0], g0[1], g1[0], g1[1]}, dv[db]);
+        const u32x4 gb = u32x4{g0[0], g0[1], g1[0], g1[1]};
         const u32x2 q0v = lds_read_tr16(qs + ro + trd0[db]);
         const u32x2 q1v = lds_read_tr16(qs + ro + trd1[db]);
-        dk[db] = mfma_32x32x16_bf16(dsa[st], u32x4{q0v[0], q0v[1], q1v[0], q1v[1]}, dk[db]);
+        const u32x4 qb = u32x4{q0v[0], q0v[1], q1v[0], q1v[1]};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          mfma_acc_pinned(dv[kb][db], pa[kb], gb);
+          mfma_acc_pinned(dk[kb][db], dsa[kb], qb);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // dK = scale * sum dS^T Q, dV = sum P^T dO.  Accumulator register r of block
-  // db holds key 32*wave + 8*(r/4) + 4*hf + r%4 at head dim 32*db + l32.
+  // dK = scale * sum dS^T Q, dV = sum P^T dO.  Accumulator register r of
+  // block (kb, db) holds key kbase + 32*kb + 8*(r/4) + 4*hf + r%4 at head dim
+  // 32*db + l32.
   uint16_t* dkp = dK + (size_t)bhk * Nk * D;
   uint16_t* dvp = dV + (size_t)bhk * Nk * D;
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kv0 + wave * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (key < Nk) {
-        const size_t off = (size_t)key * D + db * 32 + l32;
-        dkp[off] = (uint16_t)(pack_bf16(dk[db][r] * scale, 0.f) & 0xffff);
-        dvp[off] = (uint16_t)(pack_bf16(dv[db][r], 0.f) & 0xffff);
-      }
+    for (int db = 0; db < DBLK; ++db) {
+      mfma_acc_drain(dk[kb][db]);
+      mfma_acc_drain(dv[kb][db]);
     }
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key < Nk) {
+          const size_t off = (size_t)key * D + db * 32 + l32;
+          dkp[off] = (uint16_t)(pack_bf16(dk[kb][db][r] * scale, 0.f) & 0xffff);
+          dvp[off] = (uint16_t)(pack_bf16(dv[kb][db][r], 0.f) & 0xffff);
+        }
+      }
 }
 
 // ---------------------------------------------------------------------------
