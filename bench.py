@@ -47,9 +47,10 @@ def timed(fn, iters, stream):
     return s.elapsed_time(e) / iters
 
 
-def cpu_baseline(w):
-    """The fp64 oracle on the host cores: forward + backward of one (b, h) head
-    of the headline workload at full sequence length."""
+def cpu_baseline(w, min_seconds=10.0, max_heads=8):
+    """The fp64 oracle on the host cores: forward + backward of whole (b, h)
+    heads of the headline workload at full sequence length, head after head
+    until about `min_seconds` of CPU work (at most `max_heads` heads)."""
     import numpy as np
     import torch
     from oracle import attention as A
@@ -62,16 +63,19 @@ def cpu_baseline(w):
         threads = os.cpu_count() or 1
     g = torch.Generator("cpu").manual_seed(w.seed)
     mk = lambda: to_f64(torch.randn(w.Nq, w.d, generator=g).to(torch.bfloat16))
-    q, k, v, do = mk(), mk(), mk(), mk()
-    t0 = time.perf_counter()
-    A.head_forward(q, k, v, w.scale, w.causal)
-    A.head_backward(q, k, v, do, w.scale, w.causal)
-    dt = time.perf_counter() - t0
+    heads, dt = 0, 0.0
+    while heads < max_heads and (heads == 0 or dt < min_seconds):
+        q, k, v, do = mk(), mk(), mk(), mk()
+        t0 = time.perf_counter()
+        A.head_forward(q, k, v, w.scale, w.causal)
+        A.head_backward(q, k, v, do, w.scale, w.causal)
+        dt += time.perf_counter() - t0
+        heads += 1
     one = w.scaled(B=1, Hq=1, Hkv=1)
-    flops = one.fwd_flops() + one.bwd_flops()
+    flops = heads * (one.fwd_flops() + one.bwd_flops())
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"forward+backward of 1 of {w.B * w.Hq} heads "
+            "sample": f"forward+backward of {heads} of the {w.B * w.Hq} heads "
                       f"(N={w.Nq}, d={w.d}, causal), numpy fp64"}
 
 

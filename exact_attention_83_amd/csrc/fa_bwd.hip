@@ -218,23 +218,6 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk) {
   return r * ROWB + ((p ^ bwd_swz<ROWB>(r)) << 4);
 }
 
-// dK/dV accumulation with the accumulator pinned to the accumulation registers
-// (AGPRs).  The compiler's own register assignment cannot hold these 256
-// accumulators there next to the S/dP products, and shuffles them between
-// register files around every product instead.  The leading s_nop provides
-// the two wait states the hardware requires between a VALU write of an A/B
-// operand and its read by a matrix instruction, which the compiler cannot see
-// through inline assembly; LDS results are waited for by the compiler as for
-// any other use.
-__device__ __forceinline__ void mfma_acc_pinned(f32x16& c, u32x4 a, u32x4 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-// Wait states between the last pinned product and any read of its result by
-// a non-matrix instruction (more than the 19 the longest product needs).
-__device__ __forceinline__ void mfma_acc_drain(f32x16& c) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c));
-}
-
 // ---------------------------------------------------------------------------
 // dK, dV.  Wave w owns KB blocks of 32 keys, kv0 + 32*KB*w + 32*kb + (0..31),
 // whose K and V rows stay in registers as MFMA B operands of S = Q K^T and
@@ -350,6 +333,13 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       dv[kb][i] = f32x16{0};
     }
 
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      settle(kf[kb][ks]);
+      settle(vf[kb][ks]);
+    }
   if (total > 0) issue(0, 0);
   for (int it = 0; it < total; ++it) {
     const int slot = it & 1;
@@ -488,7 +478,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   constexpr int ROWB = D * 2;
   constexpr int TILE = BC * ROWB;
   constexpr int LPW = TILE / 1024 / NW;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // 2 slots x (K, V)
+  // Two slots of (K, V), one LDS variable each (see bwd_dkdv_kernel).
+  __shared__ __attribute__((aligned(1024))) char k0s[TILE], v0s[TILE], k1s[TILE], v1s[TILE];
+  auto kslot = [&](int sl) -> char* { return sl == 0 ? k0s : k1s; };
+  auto vslot = [&](int sl) -> char* { return sl == 0 ? v0s : v1s; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -528,11 +521,12 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
 #pragma unroll
   for (int i = 0; i < LPW; ++i) ldo[i] = swz_src_offset<ROWB>(lane, wave * LPW + i);
   auto issue = [&](int j, int slot) {
-    char* d = smem + slot * 2 * TILE + wave * LPW * 1024;
+    char* dk_ = kslot(slot) + wave * LPW * 1024;
+    char* dv_ = vslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      buffer_load_lds16(rK, d + i * 1024, ldo[i], j * TILE);
-      buffer_load_lds16(rV, d + TILE + i * 1024, ldo[i], j * TILE);
+      buffer_load_lds16(rK, dk_ + i * 1024, ldo[i], j * TILE);
+      buffer_load_lds16(rV, dv_ + i * 1024, ldo[i], j * TILE);
     }
   };
   // A operands of S^T / dP^T (b128): key row kb*32 + l32, chunk 2*ks + hf.
@@ -553,14 +547,21 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) dq[i] = f32x16{0};
 
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    settle(qf[ks]);
+    settle(gf[ks]);
+  }
+  settle(lse2);
+  settle(dlt);
   issue(0, 0);
-  for (int j = 0; j < ntiles; ++j) {
-    const int slot = j & 1;
+  // One iteration per KV tile; S = slot (a compile-time constant).
+  auto body = [&](int j, auto S) {
+    constexpr int slot = decltype(S)::value;
     wait_vmem();
     lds_barrier();
-    if (j + 1 < ntiles) issue(j + 1, slot ^ 1);
-    const char* ks_ = smem + slot * 2 * TILE;
-    const char* vs_ = ks_ + TILE;
+    const char* ks_ = kslot(slot);
+    const char* vs_ = vslot(slot);
     const int kv0 = j * BC;
 
     f32x16 s[2], dp[2];
@@ -573,8 +574,15 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma_32x32x16_bf16(lds_read<u32x4>(ks_, kb * 32 * ROWB + ard[kk]), qf[kk], s[kb]);
-        dp[kb] = mfma_32x32x16_bf16(lds_read<u32x4>(vs_, kb * 32 * ROWB + ard[kk]), gf[kk], dp[kb]);
+        const u32x4 ka = lds_read<u32x4>(ks_, kb * 32 * ROWB + ard[kk]);
+        const u32x4 va = lds_read<u32x4>(vs_, kb * 32 * ROWB + ard[kk]);
+        if (kk == 0 && kb == 0) {
+          // next tile's loads after this tile's first LDS reads
+          asm volatile("" ::: "memory");
+          if (j + 1 < ntiles) issue(j + 1, slot ^ 1);
+        }
+        s[kb] = mfma_32x32x16_bf16(ka, qf[kk], s[kb]);
+        dp[kb] = mfma_32x32x16_bf16(va, gf[kk], dp[kb]);
       }
     const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
     u32x4 dsb[2][2];
@@ -609,6 +617,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
           const u32x2 a1 = lds_read_tr16(kp + trd1[db]);
           dq[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, dsb[kb][st], dq[db]);
         }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    body(j, IntConst<0>{});
+    if (j + 1 < ntiles) body(j + 1, IntConst<1>{});
   }
 
   // dQ = scale * dQ^T, written as bf16 rows.

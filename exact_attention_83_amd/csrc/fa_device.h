@@ -31,6 +31,25 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c)
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Accumulating product with the accumulator pinned to the accumulation
+// registers (AGPRs), for long-lived accumulators (O in the forward, dK/dV in
+// the backward).  Left to itself the compiler assigns MFMA results to one
+// register file for the whole kernel and, when the short-lived products
+// (whose results feed VALU work) compete for it, shuffles the long-lived
+// accumulators between files around every product.  The leading s_nop gives
+// the two wait states the hardware requires between a VALU write of an
+// operand and its read by a matrix instruction, which the compiler cannot see
+// through inline assembly; LDS and memory results are waited for by the
+// compiler as for any other use.
+__device__ __forceinline__ void mfma_acc_pinned(f32x16& c, u32x4 a, u32x4 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// Wait states between the last pinned product into c and any read of c by a
+// non-matrix instruction (more than the 19 the longest product needs).
+__device__ __forceinline__ void mfma_acc_drain(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c));
+}
+
 // fp32 pair -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2_t v = {(__bf16)lo, (__bf16)hi};
@@ -116,14 +135,28 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
 
-// Wait for this wave's outstanding vector-memory loads (including the
-// direct-to-LDS ones, which the compiler does not track as LDS writes).
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Wait until at most N of this wave's vector-memory loads are outstanding
-// (loads complete in issue order for this counter).
+// Waits for this wave's vector-memory loads, issued through the builtin so
+// that the compiler's own wait bookkeeping knows about them (it then does not
+// re-wait for loads these calls have already covered).  The empty asm
+// statements pin each wait between the loads around it.
+constexpr int vmcnt_wait_bits(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  // at most N loads outstanding (they complete in issue order for this counter)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait_bits(N));
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
+// Make the compiler wait for a register loaded from memory here.  Placed
+// before a main loop for the loads issued ahead of it (register operands),
+// so that the compiler does not carry them as pending across the loop
+// back-edge and wait for them inside the loop, where that wait would also
+// wait for the prefetches.
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" ::"v"(x));
 }
 // Workgroup barrier for LDS tiles: this wave's LDS reads have returned, then
 // s_barrier.  Outstanding direct-to-LDS loads are waited for separately.

@@ -67,12 +67,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   constexpr int RPL = 1024 / ROWB;          // rows per 1 KB load
   constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
   constexpr int DBLK = D / 32;              // 32-wide blocks of the head dim
-  // LDS: NS K slots, then NS V slots.  Rows are stored unpadded
+  // LDS: NS K slots and NS V slots.  Rows are stored unpadded
   // with the 16-byte chunks XOR-swizzled per row (chunk c of row r at position
   // c ^ sw(r)), so that the b128 reads of K (16 consecutive rows, one chunk)
   // and the transposing b64 reads of V (4 consecutive rows x 4 chunks) hit
   // distinct banks of the 64-bank LDS.
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TILE];
+  //
+  // Every K and V slot is an LDS variable of its own: the compiler then knows
+  // which slot a direct load writes and does not make the reads of the other
+  // slots wait for it (with one array it would wait for every outstanding
+  // load before any LDS read).  Slot indices are compile-time constants.
+  static_assert(NS >= 2 && NS <= 4, "stages");
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE], kb1[TILE], kb2[TILE], kb3[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE], vb1[TILE], vb2[TILE], vb3[TILE];
+  auto kslot = [&](int s) -> char* { return s == 0 ? kb0 : s == 1 ? kb1 : s == 2 ? kb2 : kb3; };
+  auto vslot = [&](int s) -> char* { return s == 0 ? vb0 : s == 1 ? vb1 : s == 2 ? vb2 : vb3; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,12 +125,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     voff[i] = r * ROWB + ((p ^ fwd_swz_v<D>(r)) << 4);
   }
   auto issue_k = [&](int j, int slot) {
-    char* d = smem + slot * TILE + wave * LPW * 1024;
+    char* d = kslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) buffer_load_lds16(rK, d + i * 1024, koff[i], j * TILE);
   };
   auto issue_v = [&](int j, int slot) {
-    char* d = smem + (NS + slot) * TILE + wave * LPW * 1024;
+    char* d = vslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) buffer_load_lds16(rV, d + i * 1024, voff[i], j * TILE);
   };
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
 
   // S^T = K Q^T for one K slot: two 32-key blocks x this wave's 32 queries.
   auto qk = [&](int slot, f32x16* s) {
-    const char* ks = smem + slot * TILE;
+    const char* ks = kslot(slot);
     s[0] = f32x16{0};
     s[1] = f32x16{0};
 #pragma unroll
@@ -229,8 +238,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     constexpr int u = decltype(U)::value;
     const bool more_k = i + NS < ntiles;
     const bool more_v = i + NS - 1 < ntiles;
-    if (more_k) issue_k(i + NS, u);                   // slot (i+NS) % NS
-    if (more_v) issue_v(i + NS - 1, (u + NS - 1) % NS);
     // S_{i+1} = K_{i+1} Q^T on the matrix pipe, interleaved op by op with the
     // exponentials of tile i (the last iteration computes an unused product of
     // a stale slot).  Group g issues one MFMA and then the fma/exp/sum/convert
@@ -241,13 +248,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     constexpr int AHEAD = 2;
     u32x4 pb[2][2];
     {
-      const char* ks = smem + ((u + 1) % NS) * TILE;
+      const char* ks = kslot((u + 1) % NS);
       s_nxt[0] = f32x16{0};
       s_nxt[1] = f32x16{0};
       u32x4 afr[AHEAD];
 #pragma unroll
       for (int g = 0; g < AHEAD; ++g)
         afr[g] = lds_read<u32x4>(ks, (g & 1) * 32 * ROWB + krd[g >> 1]);
+      // This step's loads go out after its first LDS reads: where the
+      // compiler cannot tell the slots apart (at the loop head) its wait then
+      // covers only the previous step's loads.
+      asm volatile("" ::: "memory");
+      if (more_k) issue_k(i + NS, u);                   // slot (i+NS) % NS
+      if (more_v) issue_v(i + NS - 1, (u + NS - 1) % NS);
       float p[32];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     // O^T += V^T P^T.  B element e of lane half hf in k-step (kb, st) is key
     // kb*32 + 16*st + 8*(e/4) + 4*hf + e%4 (the accumulator's row order).
     __builtin_amdgcn_s_setprio(1);
-    const char* vs = smem + (NS + u) * TILE;
+    const char* vs = vslot(u);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
