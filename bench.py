@@ -47,6 +47,31 @@ def timed(fn, iters, stream):
     return s.elapsed_time(e) / iters
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "bwd_dkdv_kernel_causal_bf16_traffic.md")
+
+
+def measured_traffic(path=TRAFFIC_PROFILE):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE/WRITE_SIZE, calibrated), or None when that summary is
+    missing or the kernel sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    vals = dict(line.split(": ", 1) for line in text.splitlines()
+                if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+    files = ["exact_attention_83_amd/csrc/fa_bwd.hip", "exact_attention_83_amd/csrc/fa_device.h",
+             "exact_attention_83_amd/csrc/fa_launch.h", "exact_attention_83_amd/build.py"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
+
+
 def cpu_baseline(w, min_seconds=10.0, max_heads=8):
     """The fp64 oracle on the host cores: forward + backward of whole (b, h)
     heads of the headline workload at full sequence length, head after head
@@ -294,7 +319,8 @@ def main(argv=None):
         "roofline": {"kernel": dom, "bound": "mfma",
                      "achieved": round(rate(*kern[dom]), 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(rate(*kern[dom]) / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": kern[dom][0],
+                     "traffic": measured_traffic() if dom.startswith("bwd_dkdv") else None,
+                     "algorithmic_flops_per_launch": kern[dom][0],
                      "avg_launch_ms": round(kern[dom][1], 4)},
         "parts": parts,
     }
