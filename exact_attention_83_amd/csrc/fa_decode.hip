@@ -223,31 +223,71 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   }
 }
 
-// Combine: one wave per (b, hq); lane handles head dims lane, lane+64, ...
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ o_part,
-                                                            const float* __restrict__ lse_part,
-                                                            uint16_t* __restrict__ O,
-                                                            float* __restrict__ LSE, int d,
-                                                            int S) {
+// Combine of the split partials ([CH18] §18.8.2 (2), reduction step).
+template <int VW>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ o_part,
+                                                             const float* __restrict__ lse_part,
+                                                             uint16_t* __restrict__ O,
+                                                             float* __restrict__ LSE, int d,
+                                                             int S) {
+  // One workgroup per (b, hq) row.  lse = M + ln sum_c exp(lse_c - M) over the
+  // whole workgroup; then thread t sums VW consecutive output elements
+  // (vector j = t % NV) over the splits c = g, g + G, ... (g = t / NV), and
+  // the G partial sums meet in LDS.  Reads of o_part are VW*4-byte vectors,
+  // consecutive across the threads of a group.
+  __shared__ float red[1024];
+  __shared__ float wred[4];
   const int row = blockIdx.x;  // b*Hq + hq
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const float* lp = lse_part + (size_t)row * S;
-  float M = -INFINITY;
-  for (int c = lane; c < S; c += 64) M = fmaxf(M, lp[c]);
+
+  float m = -INFINITY;
+  for (int c = t; c < S; c += 256) m = fmaxf(m, lp[c]);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
+  if (lane == 0) wred[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
   const float Mr = M == -INFINITY ? 0.f : M;
+  __syncthreads();
   float z = 0.f;
-  for (int c = lane; c < S; c += 64) z += __expf(lp[c] - Mr);
+  for (int c = t; c < S; c += 256) z += __expf(lp[c] - Mr);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
-  const float lse = Mr + __logf(z);
-  for (int dd = lane; dd < d; dd += 64) {
-    float acc = 0.f;
-    for (int c = 0; c < S; ++c) acc += __expf(lp[c] - lse) * o_part[((size_t)row * S + c) * d + dd];
-    O[(size_t)row * d + dd] = (uint16_t)(pack_bf16(acc, 0.f) & 0xffff);
+  for (int k = 32; k >= 1; k >>= 1) z += __shfl_xor(z, k, 64);
+  if (lane == 0) wred[wave] = z;
+  __syncthreads();
+  const float lse = Mr + __logf(wred[0] + wred[1] + wred[2] + wred[3]);
+
+  const int NV = d / VW;          // vectors per output row (<= 256)
+  const int G = 256 / NV;         // split groups
+  const int j = t % NV, g = t / NV;
+  float acc[VW];
+#pragma unroll
+  for (int e = 0; e < VW; ++e) acc[e] = 0.f;
+  if (g < G) {
+    const float* op = o_part + (size_t)row * S * d + j * VW;
+#pragma unroll 4
+    for (int c = g; c < S; c += G) {
+      const float w = __expf(lp[c] - lse);
+      if constexpr (VW == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(op + (size_t)c * d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+      } else {
+        acc[0] = fmaf(w, op[(size_t)c * d], acc[0]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VW; ++e) red[g * d + j * VW + e] = acc[e];
   }
-  if (lane == 0) LSE[row] = lse;
+  __syncthreads();
+  for (int dd = t; dd < d; dd += 256) {
+    float sum = 0.f;
+    for (int gg = 0; gg < G; ++gg) sum += red[gg * d + dd];
+    O[(size_t)row * d + dd] = (uint16_t)(pack_bf16(sum, 0.f) & 0xffff);
+  }
+  if (t == 0) LSE[row] = lse;
 }
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
@@ -269,8 +309,13 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, floa
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o,
                                  float* lse, int B, int Hq, int d, int num_splits,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(64), 0, stream, o_part, lse_part,
-                     (uint16_t*)o, lse, d, num_splits);
+  // (d <= 256 is checked by the caller; G * d <= 1024 floats of LDS)
+  if (d % 4 == 0)
+    hipLaunchKernelGGL(decode_combine_kernel<4>, dim3(B * Hq), dim3(256), 0, stream, o_part,
+                       lse_part, (uint16_t*)o, lse, d, num_splits);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<1>, dim3(B * Hq), dim3(256), 0, stream, o_part,
+                       lse_part, (uint16_t*)o, lse, d, num_splits);
   return hipGetLastError();
 }
 

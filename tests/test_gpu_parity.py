@@ -195,6 +195,28 @@ def test_decode_split_count_invariance(fa_gpu):
         assert maxabs(o, ref[0]) <= BF16_O and maxabs(lse, ref[1]) <= BF16_LSE
 
 
+@pytest.mark.parametrize("B,Hq,S,d", [(2, 3, 7, 100), (1, 2, 300, 30), (1, 5, 64, 256),
+                                        (3, 1, 1, 128), (2, 4, 513, 64)])
+def test_decode_combine_direct(fa_gpu, B, Hq, S, d):
+    """The merge alone on arbitrary partials: odd d (vector and scalar paths),
+    more splits than threads, one split, and chunks whose lse is -inf (empty
+    chunks weigh nothing)."""
+    say(f"decode combine direct B={B} Hq={Hq} S={S} d={d}")
+    g = torch.Generator("cpu").manual_seed(1000 + S + d)
+    op = torch.randn(B, Hq, S, d, generator=g, dtype=torch.float32)
+    lp = 3 * torch.randn(B, Hq, S, generator=g, dtype=torch.float32)
+    if S > 1:
+        lp[..., 1] = -math.inf
+    o = torch.empty(B, Hq, 1, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, Hq, 1, dtype=torch.float32, device="cuda")
+    opc, lpc = op.cuda(), lp.cuda()
+    fa_gpu.fa_decode_combine(opc, lpc, o, lse, B, Hq, d, S)
+    torch.cuda.synchronize()
+    ro, rl = A.combine(op.double().numpy(), lp.double().numpy())
+    assert maxabs(to_f64(o)[:, :, 0], ro) <= BF16_O
+    assert maxabs(to_f64(lse)[:, :, 0], rl) <= 1e-5
+
+
 def test_decode_config_full(fa_gpu):
     """B=8 Hq=32 Hkv=8 Nk=131072 d=128, 64 splits: every output and partial,
     the oracle widening one (b, KV head) slab at a time."""
