@@ -33,7 +33,7 @@ namespace {
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;              // keys per KV tile
-constexpr int kFwdStages = 3;           // K/V tiles in flight
+constexpr int kFwdStages = 2;           // K/V tiles in flight (even)
 
 }  // namespace
 
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   // which slot a direct load writes and does not make the reads of the other
   // slots wait for it (with one array it would wait for every outstanding
   // load before any LDS read).  Slot indices are compile-time constants.
-  static_assert(NS >= 2 && NS <= 4, "stages");
+  static_assert(NS == 2 || NS == 4, "stages");
   __shared__ __attribute__((aligned(1024))) char kb0[TILE], kb1[TILE], kb2[TILE], kb3[TILE];
   __shared__ __attribute__((aligned(1024))) char vb0[TILE], vb1[TILE], vb2[TILE], vb3[TILE];
   auto kslot = [&](int s) -> char* { return s == 0 ? kb0 : s == 1 ? kb1 : s == 2 ? kb2 : kb3; };
@@ -170,18 +170,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   f32x16 o[DBLK];
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) o[i] = f32x16{0};
-  // Running reference max in log2 units (scale*log2e folded in).  It is only
-  // raised when some row's max grows by more than 2^8, so O and l are rescaled
-  // rarely; probabilities are then at most 2^8, which fp32 and bf16 hold with
-  // unchanged relative precision.  The final O/l and LSE do not depend on the
-  // reference.  A finite start keeps (-inf) - (-inf) from ever forming.
-  float M = -1e30f;
-  float l_run = 0.f;  // this lane's share of the row sum
+  // Reference max M in log2 units (scale*log2e folded in), per query row, and
+  // this lane's share of the row sum.  p = exp2(s*c - M) is computed against
+  // the current reference without taking each tile's max first; the tile's
+  // per-lane sum of p bounds every p it holds, and only when some lane's sum
+  // exceeds kLazyLimit (or is inf) is the tile's true max taken, O and l
+  // rescaled and the tile's p recomputed.  The final O/l and LSE do not depend
+  // on the reference ([L21] slide 12: any common shift cancels).
+  constexpr float kLazyLimit = 65536.f;
+  float M;
+  float l_run = 0.f;
 
-  // Mask one S^T tile and fold its row max into M (rescaling O and l when M
-  // must move).  Keys past the end (ragged tail) and, on tiles crossing the
-  // diagonal, keys after the query are masked ([CH18] §18.5.2).
-  auto row_max = [&](int j, f32x16* s) {
+  // Mask one S^T tile: keys past the end (ragged tail) and, on tiles crossing
+  // the diagonal, keys after the query ([CH18] §18.5.2).
+  auto mask = [&](int j, f32x16* s) {
     const int kv0 = j * BC;
     const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
     if (need_mask) {
@@ -193,29 +195,25 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
           if (key >= Nk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
         }
     }
+  };
+  // Row max of a masked tile in log2 units, the same in both lane halves.
+  auto tile_max = [&](const f32x16* s) {
     float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    const float mts = max_halves(mt) * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mts > M + 8.f)) {
-      const float Mn = fmaxf(M, mts);
-      const float alpha = fast_exp2(M - Mn);
-      M = Mn;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
-    }
+    return max_halves(mt) * scale_log2;
   };
 
   // Software pipeline, one barrier per tile.  Iteration i reads K_{i+1} (for
   // S_{i+1}) and V_i; the loads issued at its start fetch K_{i+NS} and
   // V_{i+NS-1} into the slots freed by iteration i-1, so every tile has NS-1
   // iterations to arrive.  The MFMAs of S_{i+1} = K_{i+1} Q^T overlap the
-  // exp/convert work of tile i, whose row max was taken at the end of the
-  // previous iteration.
-  f32x16 s_cur[2], s_nxt[2];
+  // exp/convert work of tile i.  The S^T tiles of consecutive iterations live
+  // in sbuf[i % 2] (NS is even, so the parity is a compile-time constant).
+  static_assert(NS % 2 == 0, "stages");
+  f32x16 sbuf[2][2];
   // prologue: K_0, V_0, K_1, then V_1, K_2, ... (the first three are needed first)
   issue_k(0, 0);
   issue_v(0, 0);
@@ -225,17 +223,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     if (t < ntiles) issue_v(t, t);
     if (t + 1 < ntiles) issue_k(t + 1, t + 1);
   }
-  if (NS == 3) wait_vmem_le<2 * LPW>();  // V_1 and K_2 may still be in flight
-  else wait_vmem();
+  wait_vmem();
   __syncthreads();
-  qk(0, s_cur);
-  row_max(0, s_cur);
+  qk(0, sbuf[0]);
+  mask(0, sbuf[0]);
+  // Start the reference at tile 0's max (finite: key 0 is visible to every
+  // row; the floor only guards rows past Nq).
+  M = fmaxf(tile_max(sbuf[0]), -1e30f);
   lds_barrier();  // K slot 0 is refilled below
 
   // One pipeline step; U = i % NS makes every slot a compile-time constant, so
   // the LDS fragment addresses are a per-lane register plus an immediate.
   auto step = [&](int i, auto U) {
     constexpr int u = decltype(U)::value;
+    f32x16* s_cur = sbuf[u & 1];
+    f32x16* s_nxt = sbuf[(u & 1) ^ 1];
     const bool more_k = i + NS < ntiles;
     const bool more_v = i + NS - 1 < ntiles;
     // S_{i+1} = K_{i+1} Q^T on the matrix pipe, interleaved op by op with the
@@ -247,6 +249,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     constexpr int EPG = 32 / NG;              // S_i elements per group (per lane)
     constexpr int AHEAD = 2;
     u32x4 pb[2][2];
+    float lt = 0.f;                           // this lane's sum of p over tile i
     {
       const char* ks = kslot((u + 1) % NS);
       s_nxt[0] = f32x16{0};
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
 #pragma unroll
         for (int e = g * EPG; e < (g + 1) * EPG; ++e) {
           p[e] = fast_exp2(fmaf(s_cur[e >> 4][e & 15], scale_log2, -M));
-          l_run += p[e];  // fp32 sum of the unrounded p: LSE stays exact to fp32
+          lt += p[e];  // fp32 sum of the unrounded p: LSE stays exact to fp32
           if (e & 1) {
             const int kb2 = e >> 4, r = e & 15;
             pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16(p[e - 1], p[e]);
@@ -282,6 +285,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // Rare: the reference is too low for this tile.  Move it to the tile's
+    // max, rescale O and l, and redo the tile's p.
+    if (__builtin_amdgcn_ballot_w64(lt > kLazyLimit)) {
+      const float Mn = fmaxf(M, tile_max(s_cur));
+      const float alpha = fast_exp2(M - Mn);
+      M = Mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int d4 = 0; d4 < DBLK; ++d4) o[d4] *= alpha;
+      lt = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; e += 2) {
+        const float p0 = fast_exp2(fmaf(s_cur[e >> 4][e & 15], scale_log2, -M));
+        const float p1 = fast_exp2(fmaf(s_cur[e >> 4][(e & 15) + 1], scale_log2, -M));
+        lt += p0 + p1;
+        const int r = e & 15;
+        pb[e >> 4][r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
+      }
+    }
+    l_run += lt;
 
     // O^T += V^T P^T.  B element e of lane half hf in k-step (kb, st) is key
     // kb*32 + 16*st + 8*(e/4) + 4*hf + e%4 (the accumulator's row order).
@@ -300,22 +323,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
         }
     __builtin_amdgcn_s_setprio(0);
 
-    if (i + 1 < ntiles) {
-      row_max(i + 1, s_nxt);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
-    }
-    // K_{i+2} and V_{i+1} must have landed; this iteration's loads may not.
-    if (NS == 3 && more_k) wait_vmem_le<2 * LPW>();
-    else if (NS == 3 && more_v) wait_vmem_le<LPW>();
+    if (i + 1 < ntiles) mask(i + 1, s_nxt);
+    // K_{i+2} and V_{i+1} (issued NS-2 iterations ago) must have landed; the
+    // loads of this and the NS-3 previous iterations may not (while more_k
+    // holds, each of those issued 2*LPW loads).
+    if (more_k) wait_vmem_le<2 * LPW * (NS - 2)>();
     else wait_vmem();
     lds_barrier();
   };
   for (int i0 = 0; i0 < ntiles; i0 += NS) {
     step(i0, IntConst<0>{});
     if (i0 + 1 < ntiles) step(i0 + 1, IntConst<1>{});
-    if constexpr (NS == 3) {
-      if (i0 + 2 < ntiles) step(i0 + 2, IntConst<2>{});
+    if constexpr (NS > 2) {
+      if (i0 + 2 < ntiles) step(i0 + 2, IntConst<2 % NS>{});
+      if (i0 + 3 < ntiles) step(i0 + 3, IntConst<3 % NS>{});
     }
   }
 
