@@ -33,7 +33,7 @@ namespace {
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;              // keys per KV tile
-constexpr int kFwdStages = 2;           // K/V tiles in flight (even)
+constexpr int kFwdStages = 2;           // K/V slots
 
 }  // namespace
 
@@ -206,22 +206,29 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     return max_halves(mt) * scale_log2;
   };
 
-  // Software pipeline, one barrier per tile.  Iteration i reads K_{i+1} (for
-  // S_{i+1}) and V_i; the loads issued at its start fetch K_{i+NS} and
-  // V_{i+NS-1} into the slots freed by iteration i-1, so every tile has NS-1
-  // iterations to arrive.  The MFMAs of S_{i+1} = K_{i+1} Q^T overlap the
-  // exp/convert work of tile i.  The S^T tiles of consecutive iterations live
-  // in sbuf[i % 2] (NS is even, so the parity is a compile-time constant).
-  static_assert(NS % 2 == 0, "stages");
+  // Software pipeline, one barrier per tile, two LDS slots each for K and V.
+  // Iteration i issues, op by op, the 16 products of S_{i+1} = K_{i+1} Q^T and
+  // the 16 products of O^T += V_{i-1}^T P_{i-1}^T (tile i-1's P, kept from the
+  // previous iteration), and after each product the fma/exp/sum/convert of one
+  // element of tile i's S; every product thus has about four VALU ops beside
+  // it, and the matrix pipe never waits for a VALU-only phase.  The loads
+  // issued at the start of iteration i fetch K_{i+2} (into the slot K_i left)
+  // and V_i (into the slot V_{i-2} left); both have one iteration to arrive.
+  // S^T tiles and P fragments alternate by iteration parity.
+  static_assert(NS == 2, "stages");
   f32x16 sbuf[2][2];
-  // prologue: K_0, V_0, K_1, then V_1, K_2, ... (the first three are needed first)
-  issue_k(0, 0);
-  issue_v(0, 0);
-  if (ntiles > 1) issue_k(1, 1);
+  u32x4 pbuf[2][2][2];  // [parity][kb][k-step]: P^T B operands
 #pragma unroll
-  for (int t = 1; t + 1 < NS; ++t) {
-    if (t < ntiles) issue_v(t, t);
-    if (t + 1 < ntiles) issue_k(t + 1, t + 1);
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) pbuf[1][kb][st] = u32x4{0, 0, 0, 0};
+  // prologue: K_0, K_1; V slot 1 is zeroed so that the first iteration's
+  // product with "tile -1" (P = 0) adds exactly zero.
+  issue_k(0, 0);
+  if (ntiles > 1) issue_k(1, 1);
+  {
+    char* z = vslot(1);
+    for (int off = tid * 16; off < TILE; off += NW * 64 * 16) lds_write<u32x4>(z, off, u32x4{0, 0, 0, 0});
   }
   wait_vmem();
   __syncthreads();
@@ -232,61 +239,80 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   M = fmaxf(tile_max(sbuf[0]), -1e30f);
   lds_barrier();  // K slot 0 is refilled below
 
-  // One pipeline step; U = i % NS makes every slot a compile-time constant, so
-  // the LDS fragment addresses are a per-lane register plus an immediate.
+  // Products per tile: NQK of S = K Q^T (h -> kb = h%2, kk = h/2) and NPV of
+  // O^T += V^T P^T (h -> kb = h/(2*DBLK), st = (h/DBLK)%2, db = h%DBLK).
+  constexpr int NQK = 2 * KSTEPS;
+  constexpr int NPV = 4 * DBLK;
+  static_assert(NQK == NPV && 32 % (2 * NQK) == 0, "product interleave");
+  constexpr int EPG = 32 / (2 * NQK);  // elements of S_i per product (per lane)
+  // V^T fragment of PV product h.
+  auto vfrag = [&](const char* vs, int h) {
+    const char* vp = vs + ((h / (2 * DBLK)) * 32 + ((h / DBLK) & 1) * 16) * ROWB + vrd[h % DBLK];
+    const u32x2 a0 = lds_read_tr16(vp);
+    const u32x2 a1 = lds_read_tr16(vp + 8 * ROWB);
+    return u32x4{a0[0], a0[1], a1[0], a1[1]};
+  };
+  // K fragment of S product h: kb = h%2, kk = h/2.
+  auto kfrag = [&](const char* ks, int h) {
+    return lds_read<u32x4>(ks, (h & 1) * 32 * ROWB + krd[h >> 1]);
+  };
+
+  // One pipeline step; U = i % 2 makes slots and buffers compile-time
+  // constants, so the LDS fragment addresses are a per-lane register plus an
+  // immediate.
   auto step = [&](int i, auto U) {
     constexpr int u = decltype(U)::value;
-    f32x16* s_cur = sbuf[u & 1];
-    f32x16* s_nxt = sbuf[(u & 1) ^ 1];
-    const bool more_k = i + NS < ntiles;
-    const bool more_v = i + NS - 1 < ntiles;
-    // S_{i+1} = K_{i+1} Q^T on the matrix pipe, interleaved op by op with the
-    // exponentials of tile i (the last iteration computes an unused product of
-    // a stale slot).  Group g issues one MFMA and then the fma/exp/sum/convert
-    // of two elements of S_i; sched_barrier pins that order so the MFMAs run
-    // while this wave does VALU work.  K fragments are read 2 groups ahead.
-    constexpr int NG = 2 * KSTEPS;            // MFMAs of one QK^T tile
-    constexpr int EPG = 32 / NG;              // S_i elements per group (per lane)
+    f32x16* s_cur = sbuf[u];
+    f32x16* s_nxt = sbuf[u ^ 1];
+    u32x4 (*pb_cur)[2] = pbuf[u];
+    u32x4 (*pb_prev)[2] = pbuf[u ^ 1];
+    const bool more_k = i + 2 < ntiles;
     constexpr int AHEAD = 2;
-    u32x4 pb[2][2];
-    float lt = 0.f;                           // this lane's sum of p over tile i
+    float lt = 0.f;  // this lane's sum of p over tile i
     {
-      const char* ks = kslot((u + 1) % NS);
+      const char* ks = kslot(u ^ 1);   // K_{i+1}
+      const char* vs = vslot(u ^ 1);   // V_{i-1}
       s_nxt[0] = f32x16{0};
       s_nxt[1] = f32x16{0};
-      u32x4 afr[AHEAD];
+      u32x4 kfr[AHEAD], vfr[AHEAD];
 #pragma unroll
-      for (int g = 0; g < AHEAD; ++g)
-        afr[g] = lds_read<u32x4>(ks, (g & 1) * 32 * ROWB + krd[g >> 1]);
+      for (int h = 0; h < AHEAD; ++h) {
+        kfr[h] = kfrag(ks, h);
+        vfr[h] = vfrag(vs, h);
+      }
       // This step's loads go out after its first LDS reads: where the
       // compiler cannot tell the slots apart (at the loop head) its wait then
       // covers only the previous step's loads.
       asm volatile("" ::: "memory");
-      if (more_k) issue_k(i + NS, u);                   // slot (i+NS) % NS
-      if (more_v) issue_v(i + NS - 1, (u + NS - 1) % NS);
+      if (more_k) issue_k(i + 2, u);
+      issue_v(i, u);
       float p[32];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int kb = g & 1, kk = g >> 1;
-        s_nxt[kb] = mfma_32x32x16_bf16(afr[g % AHEAD], qf[kk], s_nxt[kb]);
-        if (g + AHEAD < NG)
-          afr[g % AHEAD] =
-              lds_read<u32x4>(ks, ((g + AHEAD) & 1) * 32 * ROWB + krd[(g + AHEAD) >> 1]);
+      for (int g = 0; g < 2 * NQK; ++g) {
+        const int h = g >> 1;
+        if ((g & 1) == 0) {
+          s_nxt[h & 1] = mfma_32x32x16_bf16(kfr[h % AHEAD], qf[h >> 1], s_nxt[h & 1]);
+          if (h + AHEAD < NQK) kfr[h % AHEAD] = kfrag(ks, h + AHEAD);
+        } else {
+          o[h % DBLK] = mfma_32x32x16_bf16(vfr[h % AHEAD],
+                                           pb_prev[h / (2 * DBLK)][(h / DBLK) & 1], o[h % DBLK]);
+          if (h + AHEAD < NPV) vfr[h % AHEAD] = vfrag(vs, h + AHEAD);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int e = g * EPG; e < (g + 1) * EPG; ++e) {
           p[e] = fast_exp2(fmaf(s_cur[e >> 4][e & 15], scale_log2, -M));
           lt += p[e];  // fp32 sum of the unrounded p: LSE stays exact to fp32
           if (e & 1) {
-            const int kb2 = e >> 4, r = e & 15;
-            pb[kb2][r >> 3][(r & 7) >> 1] = pack_bf16(p[e - 1], p[e]);
+            const int r = e & 15;
+            pb_cur[e >> 4][r >> 3][(r & 7) >> 1] = pack_bf16(p[e - 1], p[e]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // Rare: the reference is too low for this tile.  Move it to the tile's
-    // max, rescale O and l, and redo the tile's p.
+    // Rare: the reference is too low for tile i.  Move it to the tile's max,
+    // rescale O (which now holds tiles up to i-1) and l, and redo tile i's p.
     if (__builtin_amdgcn_ballot_w64(lt > kLazyLimit)) {
       const float Mn = fmaxf(M, tile_max(s_cur));
       const float alpha = fast_exp2(M - Mn);
@@ -301,44 +327,30 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
         const float p1 = fast_exp2(fmaf(s_cur[e >> 4][(e & 15) + 1], scale_log2, -M));
         lt += p0 + p1;
         const int r = e & 15;
-        pb[e >> 4][r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
+        pb_cur[e >> 4][r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
       }
     }
     l_run += lt;
-
-    // O^T += V^T P^T.  B element e of lane half hf in k-step (kb, st) is key
-    // kb*32 + 16*st + 8*(e/4) + 4*hf + e%4 (the accumulator's row order).
-    __builtin_amdgcn_s_setprio(1);
-    const char* vs = vslot(u);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const char* vp = vs + (kb * 32 + st * 16) * ROWB + vrd[db];
-          const u32x2 a0 = lds_read_tr16(vp);
-          const u32x2 a1 = lds_read_tr16(vp + 8 * ROWB);
-          o[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[kb][st], o[db]);
-        }
-    __builtin_amdgcn_s_setprio(0);
-
     if (i + 1 < ntiles) mask(i + 1, s_nxt);
-    // K_{i+2} and V_{i+1} (issued NS-2 iterations ago) must have landed; the
-    // loads of this and the NS-3 previous iterations may not (while more_k
-    // holds, each of those issued 2*LPW loads).
-    if (more_k) wait_vmem_le<2 * LPW * (NS - 2)>();
-    else wait_vmem();
+    // K_{i+2} and V_i, issued above, are read in the next iteration.
+    wait_vmem();
     lds_barrier();
   };
-  for (int i0 = 0; i0 < ntiles; i0 += NS) {
+  for (int i0 = 0; i0 < ntiles; i0 += 2) {
     step(i0, IntConst<0>{});
     if (i0 + 1 < ntiles) step(i0 + 1, IntConst<1>{});
-    if constexpr (NS > 2) {
-      if (i0 + 2 < ntiles) step(i0 + 2, IntConst<2 % NS>{});
-      if (i0 + 3 < ntiles) step(i0 + 3, IntConst<3 % NS>{});
-    }
   }
+  // The last tile's O^T += V^T P^T.
+  auto pv_last = [&](auto U) {
+    constexpr int u = decltype(U)::value;
+    const char* vs = vslot(u);
+#pragma unroll
+    for (int h = 0; h < NPV; ++h)
+      o[h % DBLK] =
+          mfma_32x32x16_bf16(vfrag(vs, h), pbuf[u][h / (2 * DBLK)][(h / DBLK) & 1], o[h % DBLK]);
+  };
+  if ((ntiles - 1) & 1) pv_last(IntConst<1>{});
+  else pv_last(IntConst<0>{});
 
   // Epilogue: O = O^T / l, LSE = (M + log2 l) ln 2.
   const float l_tot = sum_halves(l_run);
