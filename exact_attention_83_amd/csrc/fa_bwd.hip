@@ -301,13 +301,18 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       buffer_load_lds16(rQ, qd + i * 1024, qoff[i], q0 * ROWB);
       buffer_load_lds16(rG, qd + QTILE + i * 1024, qoff[i], q0 * ROWB);
     }
-    if (wave < 2 && lane < BQ) {  // wave 0: lse, wave 1: delta
-      const float* src = (wave == 0 ? LSE : Delta) + (size_t)bh * Nq;
-      const __amdgpu_buffer_rsrc_t rL = make_rsrc(src, (uint32_t)Nq * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rL, (lds_void_t*)(smem + slot * SLOT + 2 * QTILE + wave * BQ * 4), 4, lane * 4, q0 * 4,
-          0, 0);
-    }
+    // wave 0: lse, wave 1: delta (each with its own uniform descriptor; a
+    // pointer chosen per wave would make the descriptor look divergent)
+    // (descriptors built outside the lane-divergent branches, so that they
+    // stay scalar)
+    char* ld = smem + slot * SLOT + 2 * QTILE;
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
+    const __amdgpu_buffer_rsrc_t rD = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
+    if (wave == 0 && lane < BQ)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (lds_void_t*)ld, 4, lane * 4, q0 * 4, 0, 0);
+    if (wave == 1 && lane < BQ)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (lds_void_t*)(ld + BQ * 4), 4, lane * 4, q0 * 4,
+                                               0, 0);
   };
 
   // A-operand rows of S / dP (b128): query l32, chunk 2*ks + hf.

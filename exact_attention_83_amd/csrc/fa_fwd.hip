@@ -286,9 +286,35 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
       asm volatile("" ::: "memory");
       if (more_k) issue_k(i + 2, u);
       issue_v(i, u);
+      // The elementwise chain of one element (fma -> exp -> sum/convert) is
+      // spread over three product groups: group g does the fma of group g+1's
+      // elements, the exp of its own and the sum/convert of group g-1's, so no
+      // result is consumed by the instruction right after it (an exp result
+      // read at once costs a wait state).
+      constexpr int NG = 2 * NQK;
       float p[32];
+      auto F = [&](int gg) {
 #pragma unroll
-      for (int g = 0; g < 2 * NQK; ++g) {
+        for (int e = gg * EPG; e < (gg + 1) * EPG; ++e)
+          p[e] = fmaf(s_cur[e >> 4][e & 15], scale_log2, -M);
+      };
+      auto X = [&](int gg) {
+#pragma unroll
+        for (int e = gg * EPG; e < (gg + 1) * EPG; ++e) p[e] = fast_exp2(p[e]);
+      };
+      auto A = [&](int gg) {
+#pragma unroll
+        for (int e = gg * EPG; e < (gg + 1) * EPG; ++e) {
+          lt += p[e];  // fp32 sum of the unrounded p: LSE stays exact to fp32
+          if (e & 1) {
+            const int r = e & 15;
+            pb_cur[e >> 4][r >> 3][(r & 7) >> 1] = pack_bf16(p[e - 1], p[e]);
+          }
+        }
+      };
+      F(0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
         const int h = g >> 1;
         if ((g & 1) == 0) {
           s_nxt[h & 1] = mfma_32x32x16_bf16(kfr[h % AHEAD], qf[h >> 1], s_nxt[h & 1]);
@@ -299,17 +325,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
           if (h + AHEAD < NPV) vfr[h % AHEAD] = vfrag(vs, h + AHEAD);
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int e = g * EPG; e < (g + 1) * EPG; ++e) {
-          p[e] = fast_exp2(fmaf(s_cur[e >> 4][e & 15], scale_log2, -M));
-          lt += p[e];  // fp32 sum of the unrounded p: LSE stays exact to fp32
-          if (e & 1) {
-            const int r = e & 15;
-            pb_cur[e >> 4][r >> 3][(r & 7) >> 1] = pack_bf16(p[e - 1], p[e]);
-          }
-        }
+        if (g + 1 < NG) F(g + 1);
+        X(g);
+        if (g > 0) A(g - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
+      A(NG - 1);
     }
     // Rare: the reference is too low for tile i.  Move it to the tile's max,
     // rescale O (which now holds tiles up to i-1) and l, and redo tile i's p.
