@@ -569,59 +569,94 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     const char* vs_ = vslot(slot);
     const int kv0 = j * BC;
 
+    // Three phases so that the elementwise work runs beside matrix products:
+    // (A) S^T = K Q^T; (B) dP^T = V dO^T with P = exp(S*scale - lse) of the
+    // finished S computed in place between its products; (C) dS = P (dP -
+    // delta) of key block 0, then dQ^T += K^T dS^T for block 0 with block 1's
+    // dS computed between its products, then block 1's products.
+    constexpr int NAB = 2 * KSTEPS;      // products of phase A (and B)
+    constexpr int EPB = 32 / NAB;        // elements per phase-B product
+    constexpr int NCB = 2 * DBLK;        // phase-C products per key block
+    constexpr int EPC = 16 / NCB;        // block-1 elements per block-0 product
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{0};
       dp[kb] = f32x16{0};
     }
+    // (A)
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 ka = lds_read<u32x4>(ks_, kb * 32 * ROWB + ard[kk]);
-        const u32x4 va = lds_read<u32x4>(vs_, kb * 32 * ROWB + ard[kk]);
-        if (kk == 0 && kb == 0) {
-          // next tile's loads after this tile's first LDS reads
-          asm volatile("" ::: "memory");
-          if (j + 1 < ntiles) issue(j + 1, slot ^ 1);
-        }
-        s[kb] = mfma_32x32x16_bf16(ka, qf[kk], s[kb]);
-        dp[kb] = mfma_32x32x16_bf16(va, gf[kk], dp[kb]);
+    for (int m = 0; m < NAB; ++m) {
+      const int kk = m >> 1, kb = m & 1;
+      const u32x4 ka = lds_read<u32x4>(ks_, kb * 32 * ROWB + ard[kk]);
+      if (m == 0) {
+        // next tile's loads after this tile's first LDS reads
+        asm volatile("" ::: "memory");
+        if (j + 1 < ntiles) issue(j + 1, slot ^ 1);
       }
-    const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
-    u32x4 dsb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = s[kb][r];
-        if (need_mask) {
-          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          sv = (key >= Nk || (CAUSAL && key > qrow)) ? -INFINITY : sv;
-        }
-        const float p = fast_exp2(fmaf(sv, scale_log2, -lse2));
-        ds[r] = p * (dp[kb][r] - dlt);
-      }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        dsb[kb][st] = u32x4{pack_bf16(ds[8 * st + 0], ds[8 * st + 1]),
-                            pack_bf16(ds[8 * st + 2], ds[8 * st + 3]),
-                            pack_bf16(ds[8 * st + 4], ds[8 * st + 5]),
-                            pack_bf16(ds[8 * st + 6], ds[8 * st + 7])};
+      s[kb] = mfma_32x32x16_bf16(ka, qf[kk], s[kb]);
     }
+    const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const char* kp = ks_ + (kb * 32 + st * 16) * ROWB;
-          const u32x2 a0 = lds_read_tr16(kp + trd0[db]);
-          const u32x2 a1 = lds_read_tr16(kp + trd1[db]);
-          dq[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, dsb[kb][st], dq[db]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= Nk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
         }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (B)
+    {
+      u32x4 va = lds_read<u32x4>(vs_, ard[0]);
+#pragma unroll
+      for (int m = 0; m < NAB; ++m) {
+        const int kk = m >> 1, kb = m & 1;
+        dp[kb] = mfma_32x32x16_bf16(va, gf[kk], dp[kb]);
+        if (m + 1 < NAB) va = lds_read<u32x4>(vs_, ((m + 1) & 1) * 32 * ROWB + ard[(m + 1) >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < EPB; ++t) {
+          const int x = EPB * m + t;
+          s[x >> 4][x & 15] = fast_exp2(fmaf(s[x >> 4][x & 15], scale_log2, -lse2));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // (C)
+    u32x4 dsb[2][2];
+    auto ds_elem = [&](int kb, int r) {
+      dp[kb][r] = s[kb][r] * (dp[kb][r] - dlt);
+      if (r & 1) {
+        const int st = r >> 3, w = (r & 7) >> 1;
+        dsb[kb][st][w] = pack_bf16(dp[kb][r - 1], dp[kb][r]);
+      }
+    };
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds_elem(0, r);
+    auto kfragT = [&](int kb, int st, int db) {
+      const char* kp = ks_ + (kb * 32 + st * 16) * ROWB;
+      const u32x2 a0 = lds_read_tr16(kp + trd0[db]);
+      const u32x2 a1 = lds_read_tr16(kp + trd1[db]);
+      return u32x4{a0[0], a0[1], a1[0], a1[1]};
+    };
+    {
+      u32x4 kt = kfragT(0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < 2 * NCB; ++m) {
+        const int kb = m / NCB, st = (m / DBLK) & 1, db = m % DBLK;
+        dq[db] = mfma_32x32x16_bf16(kt, dsb[kb][st], dq[db]);
+        if (m + 1 < 2 * NCB)
+          kt = kfragT((m + 1) / NCB, ((m + 1) / DBLK) & 1, (m + 1) % DBLK);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m < NCB) {
+#pragma unroll
+          for (int t = 0; t < EPC; ++t) ds_elem(1, EPC * m + t);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
   for (int j = 0; j < ntiles; j += 2) {
     body(j, IntConst<0>{});
