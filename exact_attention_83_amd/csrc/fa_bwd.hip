@@ -180,6 +180,8 @@ namespace {
 constexpr int kKvWaves = 4;
 constexpr int kKvKb = 2;                         // 32-key blocks per wave
 constexpr int kKvBkv = 32 * kKvKb * kKvWaves;    // keys per dK/dV work unit
+// Bytes of dynamic LDS of the dK/dV kernel: each wave's V rows.
+constexpr int dkdv_vbuf_bytes(int d) { return kKvWaves * 32 * kKvKb * 2 * d; }
 constexpr int kKvBq = 32;              // query rows per inner tile
 constexpr int kDqWaves = 8;
 constexpr int kDqBr = 32 * kDqWaves;   // query rows per dQ work unit
@@ -219,9 +221,10 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Wave w owns KB blocks of 32 keys, kv0 + 32*KB*w + 32*kb + (0..31),
-// whose K and V rows stay in registers as MFMA B operands of S = Q K^T and
-// dP = dO V^T (queries on the m axis, keys on n).  Each A operand read from
+// dK, dV.  Wave w owns KB blocks of 32 keys, kv0 + 32*KB*w + 32*kb + (0..31).
+// Their K rows stay in registers and their V rows in the wave's own LDS
+// region, as the MFMA B operands of S = Q K^T and dP = dO V^T (queries on the
+// m axis, keys on n).  Each A operand read from
 // LDS (a Q or dO row chunk) feeds one product per key block, which halves the
 // LDS read traffic per product at KB = 2: with one LDS operand per product
 // the LDS read bandwidth, not the matrix cores, bounds the kernel.  The S and
@@ -247,7 +250,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   constexpr int QTILE = BQ * ROWB;
   constexpr int LPW = QTILE / 1024 / NW;  // direct loads per wave per Q (or dO) tile
   constexpr int SLOT = 2 * QTILE + 2 * BQ * 4;  // Q, dO, lse, delta
-  __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT];
+  // One variable per slot: with the slot a compile-time constant in the loop
+  // body, the compiler sees that the direct loads into one slot cannot alias
+  // the reads of the other and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) char s0[SLOT], s1[SLOT];
+  auto sslot = [&](int sl) -> char* { return sl == 0 ? s0 : s1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,17 +272,29 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   const int kbase = kv0 + wave * 32 * KB;
 
   // This lane's K and V rows: B operands with n = key, k = head dim.
-  u32x4 kf[KB][KSTEPS], vf[KB][KSTEPS];
+  u32x4 kf[KB][KSTEPS];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = min(kbase + kb * 32 + l32, Nk - 1);
     const uint16_t* kr = K + ((size_t)bhk * Nk + key) * D;
-    const uint16_t* vr = V + ((size_t)bhk * Nk + key) * D;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      kf[kb][ks] = ldg<u32x4>(kr + ks * 16 + hf * 8);
-      vf[kb][ks] = ldg<u32x4>(vr + ks * 16 + hf * 8);
-    }
+    for (int ks = 0; ks < KSTEPS; ++ks) kf[kb][ks] = ldg<u32x4>(kr + ks * 16 + hf * 8);
+  }
+  // This wave's V rows go to its own LDS region (row-major, chunks swizzled
+  // like the query tiles), read back as B operands of dP = dO V^T: that frees
+  // the registers for deeper prefetching of the LDS operands below.  The
+  // region is dynamic LDS, which follows the static slots, so the slots sit
+  // below 64 KB, where a read's immediate offset can hold the slot base.
+  constexpr int VROWS = 32 * KB;
+  static_assert(NW * VROWS * ROWB == dkdv_vbuf_bytes(D), "V region size");
+  static_assert(2 * SLOT + NW * VROWS * ROWB <= 160 * 1024, "LDS per workgroup");
+  extern __shared__ __attribute__((aligned(1024))) char vbuf[];  // dkdv_vbuf_bytes(D)
+  char* vw = vbuf + wave * VROWS * ROWB;
+  {
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (size_t)bhk * Nk * D, (uint32_t)Nk * ROWB);
+#pragma unroll
+    for (int blk = 0; blk < VROWS * ROWB / 1024; ++blk)
+      buffer_load_lds16(rV, vw + blk * 1024, swz_src_offset<ROWB>(lane, blk), kbase * ROWB);
   }
 
   const int nqt = (Nq + BQ - 1) / BQ;
@@ -295,7 +314,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     tile_head(it, &bh, &q0);
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * ROWB);
     const __amdgpu_buffer_rsrc_t rG = make_rsrc(dO + (size_t)bh * Nq * D, (uint32_t)Nq * ROWB);
-    char* qd = smem + slot * SLOT + wave * LPW * 1024;
+    char* qd = sslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       buffer_load_lds16(rQ, qd + i * 1024, qoff[i], q0 * ROWB);
@@ -305,7 +324,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     // pointer chosen per wave would make the descriptor look divergent)
     // (descriptors built outside the lane-divergent branches, so that they
     // stay scalar)
-    char* ld = smem + slot * SLOT + 2 * QTILE;
+    char* ld = sslot(slot) + 2 * QTILE;
     const __amdgpu_buffer_rsrc_t rL = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
     const __amdgpu_buffer_rsrc_t rD = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
     if (wave == 0 && lane < BQ)
@@ -341,40 +360,50 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      settle(kf[kb][ks]);
-      settle(vf[kb][ks]);
-    }
+    for (int ks = 0; ks < KSTEPS; ++ks) settle(kf[kb][ks]);
   if (total > 0) issue(0, 0);
-  for (int it = 0; it < total; ++it) {
-    const int slot = it & 1;
+  auto body = [&](int it, auto S) {
+    constexpr int slot = decltype(S)::value;
     int bh, q0;
     tile_head(it, &bh, &q0);
     wait_vmem();
     lds_barrier();
     if (it + 1 < total) issue(it + 1, slot ^ 1);
-    const char* qs = smem + slot * SLOT;
+    const char* qs = sslot(slot);
     const char* gs = qs + QTILE;
     const char* ls = qs + 2 * QTILE;
 
+    // Four phases of NPH products each: (1) S = Q K^T; (2) dP = dO V^T with
+    // P = exp(S*scale - lse) of the finished S computed between its products;
+    // (3) dV += P^T dO with dS = P (dP - delta) computed between its products;
+    // (4) dK += dS^T Q.  Every LDS operand is read two product pairs ahead
+    // (this kernel has one wave per SIMD, so nothing else hides LDS latency).
+    // Element x of phases 2/3 (EPP per product) is register r = 4*(x/8) + x%4
+    // of block kb = (x/4)%2; register r holds query row 8*(r/4) + 4*hf + r%4.
+    constexpr int NPH = KB * KSTEPS;  // products per phase
+    constexpr int EPP = 32 / NPH;     // elements per product (per lane)
+    constexpr int NPR = NPH / 2;      // product pairs per phase
+    static_assert(KB == 2 && 2 * DBLK * KB == NPH && EPP * NPH == 32, "phase shapes");
     f32x16 sb[KB], dpb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       sb[kb] = f32x16{0};
       dpb[kb] = f32x16{0};
     }
+    // (1) S: pair ks shares the Q fragment.
+    {
+      u32x4 qa[2];
+      qa[0] = lds_read<u32x4>(qs, ard[0]);
+      qa[1] = lds_read<u32x4>(qs, ard[1]);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const u32x4 qa = lds_read<u32x4>(qs, ard[ks]);
-      const u32x4 ga = lds_read<u32x4>(gs, ard[ks]);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const u32x4 a = qa[ks & 1];
+        if (ks + 2 < KSTEPS) qa[ks & 1] = lds_read<u32x4>(qs, ard[ks + 2]);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        sb[kb] = mfma_32x32x16_bf16(qa, kf[kb][ks], sb[kb]);
-        dpb[kb] = mfma_32x32x16_bf16(ga, vf[kb][ks], dpb[kb]);
+        for (int kb = 0; kb < KB; ++kb) sb[kb] = mfma_32x32x16_bf16(a, kf[kb][ks], sb[kb]);
       }
     }
-    // Mask keys past Nk, rows past Nq and (causal) keys after the query;
-    // register r of block kb holds query row 8*(r/4) + 4*hf + r%4 of the tile.
+    // Mask keys past Nk, rows past Nq and (causal) keys after the query.
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int key = kbase + kb * 32 + l32;
@@ -388,53 +417,108 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    u32x4 pa[KB][2], dsa[KB][2];  // [kb][k-step]
+    // (2) dP, with P (in place of S) and its bf16 A operands.  Pair ks uses
+    // the dO fragment ga and the V fragments of both key blocks.
+    {
+      u32x4 ga[2], va[2][KB];
+      f32x4 nl;  // -lse * log2(e) of the current row group
+      f32x4 lvn = lds_read<f32x4>(ls, (hf * 4) * 4);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      // P = exp(S*scale - lse), dS = P (dP - delta) for query rows 16*st ..
-      // +16; register r holds query row 8*(r/4) + 4*hf + r%4 of the tile, and
-      // registers 8*st .. 8*st+7 form the A operand of k-step st.
-      u32x4 pa[KB], dsa[KB];
+      for (int pp = 0; pp < 2; ++pp) {
+        ga[pp] = lds_read<u32x4>(gs, ard[pp]);
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int g = 2 * st + gg;
-        const int qr = g * 8 + hf * 4;
-        const f32x4 lv = lds_read<f32x4>(ls, qr * 4);
-        const f32x4 dl = lds_read<f32x4>(ls, BQ * 4 + qr * 4);
+        for (int kb = 0; kb < KB; ++kb) va[pp][kb] = lds_read<u32x4>(vw, kb * 32 * ROWB + ard[pp]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const u32x4 g = ga[ks & 1];
+        u32x4 v[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) v[kb] = va[ks & 1][kb];
+        if (ks + 2 < KSTEPS) {
+          ga[ks & 1] = lds_read<u32x4>(gs, ard[ks + 2]);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+            va[ks & 1][kb] = lds_read<u32x4>(vw, kb * 32 * ROWB + ard[ks + 2]);
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          float p[4], ds[4];
+          const int m = 2 * ks + kb;
+          dpb[kb] = mfma_32x32x16_bf16(g, v[kb], dpb[kb]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = g * 4 + e;
-            p[e] = fast_exp2(fmaf(sb[kb][r], scale_log2, -lv[e] * kLog2e));
-            ds[e] = p[e] * (dpb[kb][r] - dl[e]);
+          for (int t = 0; t < EPP; ++t) {
+            const int x = EPP * m + t, gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
+            if ((x & 7) == 0) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) nl[q] = -lvn[q] * kLog2e;
+              if (gr < 3) lvn = lds_read<f32x4>(ls, ((gr + 1) * 8 + hf * 4) * 4);
+            }
+            sb[kbe][r] = fast_exp2(fmaf(sb[kbe][r], scale_log2, nl[e]));
+            if (e & 1)
+              pa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(sb[kbe][r - 1], sb[kbe][r]);
           }
-          pa[kb][2 * gg] = pack_bf16(p[0], p[1]);
-          pa[kb][2 * gg + 1] = pack_bf16(p[2], p[3]);
-          dsa[kb][2 * gg] = pack_bf16(ds[0], ds[1]);
-          dsa[kb][2 * gg + 1] = pack_bf16(ds[2], ds[3]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // dV += P^T dO and dK += dS^T Q for this k-step.
+    }
+    // Transposed B operand (dO^T or Q^T rows) of pair j of phases 3/4:
+    // st = j / DBLK, db = j % DBLK.
+    auto trB = [&](const char* base, int j) {
+      const int ro = (j / DBLK) * 16 * ROWB;
+      const u32x2 v0 = lds_read_tr16(base + ro + trd0[j % DBLK]);
+      const u32x2 v1 = lds_read_tr16(base + ro + trd1[j % DBLK]);
+      return u32x4{v0[0], v0[1], v1[0], v1[1]};
+    };
+    // (3) dV += P^T dO, with dS = P (dP - delta) and its bf16 A operands.
+    {
+      f32x4 dl, dln = lds_read<f32x4>(ls, BQ * 4 + (hf * 4) * 4);
+      u32x4 gb[2] = {trB(gs, 0), trB(gs, 1)};
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int ro = st * 16 * ROWB;
-        const u32x2 g0 = lds_read_tr16(gs + ro + trd0[db]);
-        const u32x2 g1 = lds_read_tr16(gs + ro + trd1[db]);
-        const u32x4 gb = u32x4{g0[0], g0[1], g1[0], g1[1]};
-        const u32x2 q0v = lds_read_tr16(qs + ro + trd0[db]);
-        const u32x2 q1v = lds_read_tr16(qs + ro + trd1[db]);
-        const u32x4 qb = u32x4{q0v[0], q0v[1], q1v[0], q1v[1]};
+      for (int j = 0; j < NPR; ++j) {
+        const u32x4 b = gb[j & 1];
+        if (j + 2 < NPR) gb[j & 1] = trB(gs, j + 2);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          mfma_acc_pinned(dv[kb][db], pa[kb], gb);
-          mfma_acc_pinned(dk[kb][db], dsa[kb], qb);
+          const int m = 2 * j + kb;
+          mfma_acc_pinned(dv[kb][j % DBLK], pa[kb][j / DBLK], b);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int t = 0; t < EPP; ++t) {
+            const int x = EPP * m + t, gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
+            if ((x & 7) == 0) {
+              dl = dln;
+              if (gr < 3) dln = lds_read<f32x4>(ls, BQ * 4 + ((gr + 1) * 8 + hf * 4) * 4);
+            }
+            dpb[kbe][r] = sb[kbe][r] * (dpb[kbe][r] - dl[e]);
+            if (e & 1)
+              dsa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(dpb[kbe][r - 1], dpb[kbe][r]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-  }
+    // (4) dK += dS^T Q.
+    {
+      u32x4 qb[2] = {trB(qs, 0), trB(qs, 1)};
+#pragma unroll
+      for (int j = 0; j < NPR; ++j) {
+        const u32x4 b = qb[j & 1];
+        if (j + 2 < NPR) qb[j & 1] = trB(qs, j + 2);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) mfma_acc_pinned(dk[kb][j % DBLK], dsa[kb][j / DBLK], b);
+      }
+    }
+  };
 
+  int it = 0;
+  for (; it + 1 < total; it += 2) {
+    body(it, IntConst<0>{});
+    body(it + 1, IntConst<1>{});
+  }
+  if (it < total) body(it, IntConst<0>{});
+  wait_vmem();  // the V rows when the loop ran no iteration
   // dK = scale * sum dS^T Q, dV = sum P^T dO.  Accumulator register r of
   // block (kb, db) holds key kbase + 32*kb + 8*(r/4) + 4*hf + r%4 at head dim
   // 32*db + l32.
@@ -721,9 +805,9 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   auto dK = (uint16_t*)dk;
   auto dV = (uint16_t*)dv;
   const float sl2 = scale * kLog2e;
-#define FA_LAUNCH_DKDV(DD, CC)                                                                   \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, Q, K, V, G, lse, delta, \
-                     dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv)
+#define FA_LAUNCH_DKDV(DD, CC)                                                          \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, dkdv_vbuf_bytes(DD), stream, \
+                     Q, K, V, G, lse, delta, dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv)
   if (d == 128) {
     if (causal) FA_LAUNCH_DKDV(128, true);
     else FA_LAUNCH_DKDV(128, false);
