@@ -5,8 +5,8 @@
 // rescaling step is the two-block identity of [L21] "CMU 11-868 L21
 // FlashAttention" slide 12.
 //
-// bf16 kernel layout (one workgroup = 4 waves = 128 query rows, KV tiles of 64
-// keys, two workgroups per compute unit):
+// bf16 kernel layout (one workgroup = 8 waves = 256 query rows, two waves per
+// SIMD, KV tiles of 64 keys):
 //   * each wave owns 32 query rows.  It computes S^T = K Q^T with the keys on
 //     the MFMA m axis and its queries on the n axis, so every lane owns one
 //     query column: the row max is an in-register reduction plus one exchange
@@ -17,9 +17,12 @@
 //     next product.  The V^T fragments are read from the row-major V tile with
 //     the transposing LDS read (ds_read_b64_tr_b16).
 //   * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
-//     destination bit), double-buffered, with K one tile ahead of V so that
-//     the QK^T MFMAs of the next tile run while the exponentials of the
-//     current tile are computed (one barrier per tile).
+//     destination bit) through two slots each, K two tiles ahead of use and V
+//     one; each iteration interleaves the QK^T products of tile i+1 and the
+//     PV products of tile i-1 with the softmax work of tile i (one barrier
+//     per tile).
+//   * the running max is lazy: p is computed against a reference that moves
+//     only when a tile's sum of p grows past a bound.
 //   * exp is exp2 with scale*log2(e) folded into one FMA; O is divided by the
 //     row sum once at the end ([CH18] §18.4.3 step 9).
 
