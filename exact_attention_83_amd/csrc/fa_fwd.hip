@@ -312,6 +312,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
           if (e & 1) {
             const int r = e & 15;
             pb_cur[e >> 4][r >> 3][(r & 7) >> 1] = pack_bf16(p[e - 1], p[e]);
+            // Pinned here: left alone, the compiler sinks the conversions
+            // below the rare-rescale branch (they are dead on that path),
+            // out of the product interleave.
+            settle(pb_cur[e >> 4][r >> 3][(r & 7) >> 1]);
           }
         }
       };
