@@ -185,3 +185,72 @@ def combine(o_parts, lse_parts):
     w = np.exp(lse_parts - lse[..., None])
     o = (w[..., None] * o_parts).sum(axis=-2)
     return o, lse
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False):
+    """Packed variable-length forward ([CH18] §18.7.1, flash_attn_varlen_func):
+    the sequences of a batch are concatenated along the token axis and
+    sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and key rows
+    cu_k[b] .. cu_k[b+1]-1; no query attends outside its own sequence, and the
+    causal mask is applied within each sequence (top-left: requires equal
+    query and key lengths per sequence, as for the dense forward).
+
+    q [total_q][Hq][d], k/v [total_k][Hkv][d] (token-major, as on the page),
+    cu_q/cu_k [batch+1] cumulative offsets starting at 0.
+    Returns O [total_q][Hq][d] and LSE [Hq][total_q] in fp64.  A sequence with
+    no keys gives O = 0 and LSE = -inf (no key is visible).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    total_q, Hq, d = q.shape
+    Hkv = k.shape[1]
+    o = np.zeros((total_q, Hq, v.shape[-1]))
+    lse = np.full((Hq, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if q1 == q0 or k1 == k0:
+            continue
+        qb = q[q0:q1].transpose(1, 0, 2)[None]          # [1][Hq][Nq][d]
+        kb = k[k0:k1].transpose(1, 0, 2)[None]
+        vb = v[k0:k1].transpose(1, 0, 2)[None]
+        ob, lb = forward(qb, kb, vb, scale, causal)
+        o[q0:q1] = ob[0].transpose(1, 0, 2)
+        lse[:, q0:q1] = lb[0]
+    return o, lse
+
+
+def gather_pages(cache, block_table, seqlen, hk):
+    """Logical rows 0 .. seqlen-1 of one KV head from a paged cache
+    ([CH18] §18.8.2 (3), §18.8.3 (1): the KV cache lives in fixed-size
+    physical pages and a per-request page table maps logical block j to
+    physical page block_table[j]).  cache [num_pages][page_size][Hkv][d].
+    Returns [seqlen][d]."""
+    page_size = cache.shape[1]
+    rows = [cache[int(block_table[t // page_size]), t % page_size, hk] for t in range(seqlen)]
+    return _f64(np.stack(rows)) if rows else np.zeros((0, cache.shape[-1]))
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seqlens, scale):
+    """Single-query decode over a paged KV cache: for batch entry b the keys
+    are logical rows 0 .. seqlens[b]-1, gathered through block_table[b]; then
+    the plain (unsplit) forward with Nq = 1, non-causal.
+    q [B][Hq][1][d]; k_cache/v_cache [num_pages][page_size][Hkv][d];
+    block_table [B][max_pages]; seqlens [B] (each >= 1).
+    Returns O [B][Hq][1][d], LSE [B][Hq][1] (fp64)."""
+    q = _f64(q)
+    B, Hq, _, d = q.shape
+    Hkv = k_cache.shape[2]
+    o = np.empty((B, Hq, 1, v_cache.shape[-1]))
+    lse = np.empty((B, Hq, 1))
+    for b in range(B):
+        n = int(seqlens[b])
+        assert n >= 1
+        for h in range(Hq):
+            hk = kv_head(h, Hq, Hkv)
+            kb = gather_pages(k_cache, block_table[b], n, hk)
+            vb = gather_pages(v_cache, block_table[b], n, hk)
+            o[b, h], lse[b, h] = head_forward(q[b, h], kb, vb, scale, False)
+    return o, lse

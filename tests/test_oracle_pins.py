@@ -402,3 +402,111 @@ def test_flop_formula_against_table_18_5():
         wc = w.scaled(causal=True)
         assert wc.fwd_flops() == w.fwd_flops() / 2
         assert w.bwd_flops() == 2.5 * w.fwd_flops()
+
+
+# ---------------------------------------------------------------- varlen pins
+
+def _pack_lengths(lens):
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    return cu
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_uniform_scores_mean_of_own_sequence(causal):
+    """Closed form: Q = 0 makes every visible score equal, so row i of
+    sequence b is the mean of the V rows it may see in its own sequence and
+    LSE = ln(count); rows of other sequences never contribute."""
+    lens = [5, 1, 7, 3]
+    cu = _pack_lengths(lens)
+    Hq, Hkv, d = 4, 2, 6
+    q = np.zeros((cu[-1], Hq, d))
+    k, v = rnd(cu[-1], Hkv, d), rnd(cu[-1], Hkv, d)
+    o, lse = A.forward_varlen(q, k, v, cu, cu, 0.7, causal)
+    for b, n in enumerate(lens):
+        for i in range(n):
+            row = cu[b] + i
+            cnt = i + 1 if causal else n
+            for h in range(Hq):
+                hk = h // (Hq // Hkv)
+                ref = v[cu[b]:cu[b] + cnt, hk].mean(axis=0)
+                assert np.allclose(o[row, h], ref, rtol=0, atol=1e-13)
+                assert abs(lse[h, row] - math.log(cnt)) < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_block_diagonal_masked_attention(causal):
+    """Brute force: attention over the whole packed token axis with a
+    block-diagonal mask (same sequence, and j <= i within it when causal),
+    written with explicit loops, independent of the per-sequence slicing."""
+    lens = [4, 9, 2]
+    cu = _pack_lengths(lens)
+    T, Hq, Hkv, d = cu[-1], 2, 1, 5
+    q, k, v = rnd(T, Hq, d), rnd(T, Hkv, d), rnd(T, Hkv, d)
+    scale = 0.45
+    o, lse = A.forward_varlen(q, k, v, cu, cu, scale, causal)
+    seq = np.repeat(np.arange(len(lens)), lens)
+    pos = np.concatenate([np.arange(n) for n in lens])
+    for h in range(Hq):
+        for i in range(T):
+            w = []
+            for j in range(T):
+                ok = seq[i] == seq[j] and (not causal or pos[j] <= pos[i])
+                w.append(math.exp(scale * float(q[i, h] @ k[j, 0])) if ok else 0.0)
+            w = np.array(w)
+            assert np.allclose(o[i, h], (w[:, None] * v[:, 0]).sum(0) / w.sum(), atol=1e-12)
+            assert abs(lse[h, i] - math.log(w.sum())) < 1e-12
+
+
+def test_varlen_sequences_are_isolated():
+    """Changing one sequence's K/V rows leaves every other sequence's output
+    unchanged (no attention across the packing boundary)."""
+    lens = [6, 3, 8]
+    cu = _pack_lengths(lens)
+    T, Hq, d = cu[-1], 2, 4
+    q, k, v = rnd(T, Hq, d), rnd(T, Hq, d), rnd(T, Hq, d)
+    o1, l1 = A.forward_varlen(q, k, v, cu, cu, 0.5, True)
+    k2, v2 = k.copy(), v.copy()
+    k2[cu[1]:cu[2]] += 3.0
+    v2[cu[1]:cu[2]] -= 2.0
+    o2, l2 = A.forward_varlen(q, k2, v2, cu, cu, 0.5, True)
+    keep = np.r_[cu[0]:cu[1], cu[2]:cu[3]]
+    assert np.array_equal(o1[keep], o2[keep]) and np.array_equal(l1[:, keep], l2[:, keep])
+    assert not np.allclose(o1[cu[1]:cu[2]], o2[cu[1]:cu[2]])
+
+
+# ------------------------------------------------------------ paged KV pins
+
+def test_paged_gather_reproduces_scattered_rows():
+    """Rows scattered into randomly permuted physical pages come back in
+    logical order through the page table, including a partial last page."""
+    page, Hkv, d, n = 4, 3, 5, 18
+    npages = 9
+    contig = rnd(n, Hkv, d)
+    perm = rng.permutation(npages)
+    cache = rnd(npages, page, Hkv, d)          # unused slots hold noise
+    table = perm[: (n + page - 1) // page]
+    for t in range(n):
+        cache[table[t // page], t % page] = contig[t]
+    for hk in range(Hkv):
+        assert np.array_equal(A.gather_pages(cache, table, n, hk), contig[:, hk])
+
+
+def test_paged_decode_uniform_scores_mean_of_first_rows():
+    """Closed form: Q = 0 gives O = mean of the sequence's first seqlen
+    logical V rows and LSE = ln(seqlen); rows past seqlen (still inside the
+    last page) must not count."""
+    page, Hq, Hkv, d = 8, 4, 2, 6
+    seqlens = [13, 1, 16]
+    npages = 10
+    kc, vc = rnd(npages, page, Hkv, d), rnd(npages, page, Hkv, d)
+    table = np.stack([rng.permutation(npages)[:2] for _ in seqlens])
+    q = np.zeros((len(seqlens), Hq, 1, d))
+    o, lse = A.decode_paged(q, kc, vc, table, seqlens, 0.9)
+    for b, n in enumerate(seqlens):
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            rows = [vc[table[b][t // page], t % page, hk] for t in range(n)]
+            assert np.allclose(o[b, h, 0], np.mean(rows, axis=0), atol=1e-13)
+            assert abs(lse[b, h, 0] - math.log(n)) < 1e-13
