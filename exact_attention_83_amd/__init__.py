@@ -42,6 +42,8 @@ _SIGS = {
     "fa_bwd_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                         _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_decode_splitkv_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                     _I, _F, _I, _P]),
     "fa_decode_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -168,6 +170,14 @@ def fa_decode_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nk, d, scale, num_s
           Hkv, Nk, d, scale, num_splits, _stream(stream))
 
 
+def fa_decode_splitkv_paged(q, k_cache, v_cache, block_table, seqlens, o_part, lse_part, B, Hq,
+                            Hkv, num_pages, page_size, max_pages, max_seqlen, d, scale,
+                            num_splits, stream=None):
+    _call("fa_decode_splitkv_paged", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+          _ptr(seqlens), _ptr(o_part), _ptr(lse_part), B, Hq, Hkv, num_pages, page_size,
+          max_pages, max_seqlen, d, scale, num_splits, _stream(stream))
+
+
 def fa_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream=None):
     _call("fa_decode_combine", _ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, d,
           num_splits, _stream(stream))
@@ -247,6 +257,30 @@ def decode(q, k, v, num_splits, scale=None, stream=None, return_partials=False):
     fa_decode_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nk, d, s, num_splits, stream)
     fa_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream)
     assert rows == o_part.shape[0] * o_part.shape[1] * o_part.shape[2]
+    if return_partials:
+        return o, lse, o_part, lse_part
+    return o, lse
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seqlens, num_splits, max_seqlen=None,
+                 scale=None, stream=None, return_partials=False):
+    """Split-KV decode over a paged cache: q [B][Hq][1][d], k_cache/v_cache
+    [num_pages][page_size][Hkv][d], block_table int32 [B][max_pages], seqlens
+    int32 [B] (device tensors) -> (O, LSE).  ``max_seqlen`` defaults to the
+    table's capacity (max_pages * page_size)."""
+    import torch
+    B, Hq, _, d = q.shape
+    num_pages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    max_pages = block_table.shape[1]
+    ms = max_pages * page_size if max_seqlen is None else int(max_seqlen)
+    s = _default_scale(d, scale)
+    o_part = torch.empty((B, Hq, num_splits, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device)
+    fa_decode_splitkv_paged(q, k_cache, v_cache, block_table, seqlens, o_part, lse_part, B, Hq,
+                            Hkv, num_pages, page_size, max_pages, ms, d, s, num_splits, stream)
+    fa_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream)
     if return_partials:
         return o, lse, o_part, lse_part
     return o, lse

@@ -30,11 +30,18 @@ constexpr int kDecWaves = 4;
 constexpr int kDecBlk = 32;  // keys per wave iteration
 }  // namespace
 
-template <int D>
+// PAGED: K and V are paged caches [num_pages][page_size][Hkv][D] and batch
+// entry b's logical key t sits in page table[b][t / page_size] at row
+// t % page_size ([CH18] §18.8.2 (3), §18.8.3 (1)); its length is seqlens[b]
+// and chunk c covers logical keys [c*L, (c+1)*L) of it (possibly none).  The
+// dense layout is [B][Hkv][Nk][D] with L = Nk / num_splits.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ o_part, float* __restrict__ lse_part,
-    int Hq, int Hkv, int Nk, int num_splits, float scale, float scale_log2) {
+    int Hq, int Hkv, int Nk, int num_splits, float scale, float scale_log2,
+    const int* __restrict__ table, const int* __restrict__ seqlens, int page_shift,
+    int max_pages, int num_pages, int chunk) {
   constexpr int KS = D / 16;      // k-steps over the head dim
   constexpr int DBLK = D / 32;
   constexpr int DCH = D / 8;      // 16-byte chunks per row
@@ -58,12 +65,29 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int bhk = blockIdx.x / num_splits;
   const int b = bhk / Hkv;
   const int hk = bhk - b * Hkv;
-  const int L = Nk / num_splits;
+  const int L = PAGED ? chunk : Nk / num_splits;
   const int key_begin = c * L;
-  const int key_end = key_begin + L;
+  // (paged: the length is clamped to what the table can address and page ids
+  // to the cache, so bad table data reads wrong rows but never out of bounds)
+  const int key_end =
+      PAGED ? min(key_begin + L, min(seqlens[b], max_pages << page_shift)) : key_begin + L;
 
-  const uint16_t* Kp = K + (size_t)bhk * Nk * D;
-  const uint16_t* Vp = V + (size_t)bhk * Nk * D;
+  const uint16_t* Kp = PAGED ? K : K + (size_t)bhk * Nk * D;
+  const uint16_t* Vp = PAGED ? V : V + (size_t)bhk * Nk * D;
+  const int* trow = PAGED ? table + (size_t)b * max_pages : nullptr;
+  // Element offset of key row `key` of this KV head.  Paged: a 32-key block
+  // starting at k0 (a multiple of 32; pages are at least 16 keys) touches at
+  // most the pages of k0 and k0 + 31, looked up once per block (pg0, pg1).
+  auto row_off = [&](int key, int k0, int pg0, int pg1) -> size_t {
+    if constexpr (PAGED) {
+      const int pg = (key >> page_shift) == (k0 >> page_shift) ? pg0 : pg1;
+      const int slot = (pg << page_shift) | (key & ((1 << page_shift) - 1));
+      return ((size_t)slot * Hkv + hk) * D;
+    } else {
+      (void)k0; (void)pg0; (void)pg1;
+      return (size_t)key * D;
+    }
+  };
   char* vt = vt_all + wave * D * VP;
 
   // Q^T B operand: column n = l32 is query head hk*G + l32 (zero past G).
@@ -79,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     }
   }
 
-  const int nblk = (L + kDecBlk - 1) / kDecBlk;
+  const int nblk = key_end > key_begin ? (key_end - key_begin + kDecBlk - 1) / kDecBlk : 0;
   u32x4 kreg[KREG], vreg[VREG];
   // V staging: lane -> 4 consecutive keys (group l/DCH) x 8 head dims.
   const int v_grp = lane / DCH;
@@ -88,9 +112,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
 
   auto load_blk = [&](int blk) {
     const int k0 = key_begin + blk * kDecBlk;
+    int pg0 = 0, pg1 = 0;
+    if constexpr (PAGED) {
+      pg0 = min(max(trow[k0 >> page_shift], 0), num_pages - 1);
+      pg1 = min(max(trow[(min(k0 + kDecBlk, key_end) - 1) >> page_shift], 0), num_pages - 1);
+    }
     int key = k0 + l32;
     key = key < key_end ? key : key_end - 1;
-    const uint16_t* kr = Kp + (size_t)key * D + hf * HALF;
+    const uint16_t* kr = Kp + row_off(key, k0, pg0, pg1) + hf * HALF;
 #pragma unroll
     for (int i = 0; i < KREG; ++i) kreg[i] = ldg<u32x4>(kr + i * 8);
 #pragma unroll
@@ -98,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
       const int round = i / 4;
       int vk = k0 + (round * VGRP_PER_ROUND + v_grp) * 4 + (i & 3);
       vk = vk < key_end ? vk : key_end - 1;
-      vreg[i] = ldg<u32x4>(Vp + (size_t)vk * D + v_col * 8);
+      vreg[i] = ldg<u32x4>(Vp + row_off(vk, k0, pg0, pg1) + v_col * 8);
     }
   };
 
@@ -195,7 +224,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w)
       Lsum += red_l[w][l32] * fast_exp2((red_m[w][l32] - Mr) * scale_log2);
-    const float f = fast_exp2((m_run - Mr) * scale_log2) / Lsum;
+    // (a chunk with no keys -- possible when paged -- gives O = 0, lse = -inf)
+    const float f = Lsum > 0.f ? fast_exp2((m_run - Mr) * scale_log2) / Lsum : 0.f;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) o[db] *= f;
   }
@@ -219,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   }
   if (wave == 0 && hf == 0 && l32 < G) {
     const size_t row = ((size_t)b * Hq + hk * G + l32) * num_splits + c;
-    lse_part[row] = M * scale + __logf(Lsum);
+    lse_part[row] = Lsum > 0.f ? M * scale + __logf(Lsum) : -INFINITY;
   }
 }
 
@@ -296,13 +326,33 @@ hipError_t launch_decode_split(const void* q, const void* k, const void* v, floa
   dim3 grid(B * Hkv * num_splits), block(256);
   const float sl2 = scale * kLog2e;
   if (d == 128)
-    hipLaunchKernelGGL((decode_split_kernel<128>), grid, block, 0, stream, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, Hq, Hkv, Nk,
-                       num_splits, scale, sl2);
+    hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, block, 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part,
+                       lse_part, Hq, Hkv, Nk, num_splits, scale, sl2, nullptr, nullptr, 0, 0, 0, 0);
   else
-    hipLaunchKernelGGL((decode_split_kernel<64>), grid, block, 0, stream, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, o_part, lse_part, Hq, Hkv, Nk,
-                       num_splits, scale, sl2);
+    hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, block, 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part,
+                       lse_part, Hq, Hkv, Nk, num_splits, scale, sl2, nullptr, nullptr, 0, 0, 0, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split_paged(const void* q, const void* k_cache, const void* v_cache,
+                                     const int* block_table, const int* seqlens, float* o_part,
+                                     float* lse_part, int B, int Hq, int Hkv, int page_shift,
+                                     int max_pages, int num_pages, int chunk, int d, float scale,
+                                     int num_splits, hipStream_t stream) {
+  dim3 grid(B * Hkv * num_splits), block(256);
+  const float sl2 = scale * kLog2e;
+  if (d == 128)
+    hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, block, 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
+                       o_part, lse_part, Hq, Hkv, 0, num_splits, scale, sl2, block_table,
+                       seqlens, page_shift, max_pages, num_pages, chunk);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, block, 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
+                       o_part, lse_part, Hq, Hkv, 0, num_splits, scale, sl2, block_table,
+                       seqlens, page_shift, max_pages, num_pages, chunk);
   return hipGetLastError();
 }
 

@@ -160,6 +160,36 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v,
                             float scale, int num_splits, hipStream_t stream);
 
 /*
+ * Split-KV decode over a paged KV cache ([CH18] §18.8.2 (3): Flash-Decoding
+ * combined with a paged cache; §18.8.3 (1): the cache lives in fixed-size
+ * physical pages and each request's page table maps its logical block j to a
+ * physical page).  Same partial outputs as fa_decode_splitkv, merged by
+ * fa_decode_combine.
+ *   q [B][Hq][1][d] bf16.
+ *   k_cache, v_cache [num_pages][page_size][Hkv][d] bf16: page p, row r holds
+ *   one token's K (V) for every KV head.
+ *   block_table: device int32 [B][max_pages]; logical key t of batch entry b
+ *   is row t % page_size of page block_table[b][t / page_size].
+ *   seqlens: device int32 [B], the number of keys of each entry (>= 1).
+ *   o_part [B][Hq][num_splits][d], lse_part [B][Hq][num_splits] fp32 as for
+ *   fa_decode_splitkv.  Chunk c covers logical keys [c*L, (c+1)*L) with
+ *   L = ceil(max_seqlen / num_splits) rounded up to a multiple of 32; a chunk
+ *   past an entry's length writes O_c = 0 and lse_c = -inf.
+ * Requirements: page_size a power of two in [16, 4096]; max_seqlen >= every
+ * seqlens[b] and <= max_pages * page_size; d in {64, 128}; Hq/Hkv <= 32.
+ * The table and lengths are device data and are not checked on the host: a
+ * page id outside [0, num_pages) or a length past max_pages * page_size is
+ * clamped by the kernel (wrong rows are read, never memory out of bounds).
+ * Both pointers must be 4-byte aligned.
+ */
+fa_status fa_decode_splitkv_paged(const void* q, const void* k_cache, const void* v_cache,
+                                  const int* block_table, const int* seqlens,
+                                  float* o_part, float* lse_part,
+                                  int B, int Hq, int Hkv, int num_pages, int page_size,
+                                  int max_pages, int max_seqlen, int d,
+                                  float scale, int num_splits, hipStream_t stream);
+
+/*
  * Merge of the split partials ([CH18] §18.8.2 (2), reduction step):
  *   lse = M + ln sum_c exp(lse_c - M) with M = max_c lse_c,
  *   O   = sum_c exp(lse_c - lse) * O_c.

@@ -248,6 +248,102 @@ def test_decode_config_full(fa_gpu):
             assert maxabs(lp[b, sl], rlp[0]) <= BF16_LSE
 
 
+# ------------------------------------------------------------- paged decode
+
+def paged_case(B, Hq, Hkv, seqlens, page, d, splits, seed, spare=3):
+    import dataclasses
+    from workloads import PAGED, make_paged_inputs
+    w = dataclasses.replace(PAGED["decode_paged"], B=B, Hq=Hq, Hkv=Hkv, seqlens=tuple(seqlens),
+                            page_size=page, d=d, num_splits=splits, seed=seed,
+                            spare_pages=spare)
+    return w, make_paged_inputs(w, device="cuda")
+
+
+@pytest.mark.parametrize("cfg", [
+    (2, 8, 2, (1000, 77), 16, 128, 8),       # ragged lengths, 16-key pages
+    (3, 4, 4, (1, 33, 512), 32, 128, 4),     # a single key; chunks past the end
+    (1, 32, 4, (4096,), 64, 128, 16),        # G = 8
+    (2, 16, 2, (3000, 2048), 256, 64, 5),    # d = 64, large pages
+    (2, 6, 2, (95, 200), 16, 64, 7)])
+def test_decode_paged_small(fa_gpu, cfg):
+    B, Hq, Hkv, seqlens, page, d, splits = cfg
+    w, x = paged_case(*cfg, seed=61)
+    say(f"decode paged B={B} Hq={Hq} Hkv={Hkv} seqlens={seqlens} page={page} d={d} splits={splits}")
+    o, lse, op, lp = fa_gpu.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"],
+                                         x["seqlens"], splits, max_seqlen=max(seqlens),
+                                         return_partials=True)
+    torch.cuda.synchronize()
+    ro, rl = A.decode_paged(to_f64(x["q"]), to_f64(x["k_cache"]), to_f64(x["v_cache"]),
+                            x["block_table"].cpu().numpy(), seqlens, w.scale)
+    assert maxabs(to_f64(o), ro) <= BF16_O
+    assert maxabs(to_f64(lse), rl) <= BF16_LSE
+    # chunks that start past a sequence's end hold exactly O = 0, lse = -inf
+    per = -(-max(seqlens) // splits)
+    L = -(-per // 32) * 32
+    lpn, opn = lp.cpu().numpy(), op.cpu().numpy()
+    for b, n in enumerate(seqlens):
+        for c in range(splits):
+            if c * L >= n:
+                assert np.all(np.isneginf(lpn[b, :, c])) and not np.any(opn[b, :, c])
+            else:
+                assert np.all(np.isfinite(lpn[b, :, c]))
+
+
+def test_decode_paged_equals_dense(fa_gpu):
+    """The same K/V rows laid out densely and scattered over 16-key pages,
+    with the same 512-key chunks: the two kernels run the same arithmetic, so
+    partials and outputs agree bit for bit."""
+    B, Hq, Hkv, N, d, splits, page = 2, 8, 2, 4096, 128, 8, 16
+    w, x = paged_case(B, Hq, Hkv, (N, N), page, d, splits, seed=62)
+    say("decode paged vs dense")
+    op = fa_gpu.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"],
+                             x["seqlens"], splits, return_partials=True)
+    t = torch.arange(N, device="cuda")
+    kd = torch.empty(B, Hkv, N, d, dtype=torch.bfloat16, device="cuda")
+    vd = torch.empty_like(kd)
+    for b in range(B):
+        rows = x["block_table"][b].long()[t // page]
+        kd[b] = x["k_cache"][rows, t % page].permute(1, 0, 2)
+        vd[b] = x["v_cache"][rows, t % page].permute(1, 0, 2)
+    od = fa_gpu.decode(x["q"], kd.contiguous(), vd.contiguous(), splits, return_partials=True)
+    torch.cuda.synchronize()
+    for a, b_ in zip(op, od):
+        assert torch.equal(a, b_)
+
+
+def test_decode_paged_config(fa_gpu):
+    """B=8 Hq=32 Hkv=8, 131072 keys each in 16-key pages scattered over the
+    cache, 64 splits: equal bit for bit to the dense kernel on the gathered
+    rows (itself checked against the oracle at full size), and two (b, KV
+    head) groups against the oracle directly."""
+    from workloads import PAGED, make_paged_inputs
+    w = PAGED["decode_paged"]
+    say("decode_paged inputs")
+    x = make_paged_inputs(w, device="cuda")
+    say("decode_paged full size")
+    o, lse = fa_gpu.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"],
+                                 x["seqlens"], w.num_splits)
+    N, page = w.seqlens[0], w.page_size
+    t = torch.arange(N, device="cuda")
+    kd = torch.empty(w.B, w.Hkv, N, w.d, dtype=torch.bfloat16, device="cuda")
+    vd = torch.empty_like(kd)
+    for b in range(w.B):
+        rows = x["block_table"][b].long()[t // page]
+        kd[b] = x["k_cache"][rows, t % page].permute(1, 0, 2)
+        vd[b] = x["v_cache"][rows, t % page].permute(1, 0, 2)
+    od, lsed = fa_gpu.decode(x["q"], kd, vd, w.num_splits)
+    torch.cuda.synchronize()
+    assert torch.equal(o, od) and torch.equal(lse, lsed)
+    G = w.Hq // w.Hkv
+    for b, hk in ((0, 0), (w.B - 1, w.Hkv - 1)):
+        qq = to_f64(x["q"][b:b + 1, hk * G:(hk + 1) * G])
+        ro, rl = A.forward(qq, to_f64(kd[b:b + 1, hk:hk + 1]), to_f64(vd[b:b + 1, hk:hk + 1]),
+                           w.scale)
+        assert maxabs(to_f64(o[b:b + 1, hk * G:(hk + 1) * G]), ro) <= BF16_O
+        assert maxabs(to_f64(lse[b:b + 1, hk * G:(hk + 1) * G]), rl) <= BF16_LSE
+    del kd, vd
+
+
 # ---------------------------------------------------------------------- fp8
 
 def test_quantizer_codes_match_oracle_bytes(fa_gpu):

@@ -121,3 +121,108 @@ def make_inputs(w: Workload, device: str = "cpu", seed: int | None = None):
 def to_f64(t: torch.Tensor):
     """Exact widening of a bf16 / fp32 tensor to a float64 numpy array."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+# ------------------------------------------------------------ paged decode
+
+@dataclass(frozen=True)
+class PagedDecode:
+    """Single-query decode over a paged KV cache: sequence b has seqlens[b]
+    keys stored in pages of ``page_size`` tokens, the pages of all sequences
+    scattered over the cache in a seeded random order."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    seqlens: tuple
+    page_size: int
+    d: int
+    num_splits: int
+    seed: int = 0
+    spare_pages: int = 0  # pages in the cache that no sequence uses
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def max_pages(self) -> int:
+        return max((n + self.page_size - 1) // self.page_size for n in self.seqlens)
+
+    @property
+    def num_pages(self) -> int:
+        return sum((n + self.page_size - 1) // self.page_size for n in self.seqlens) + self.spare_pages
+
+
+def make_paged_inputs(w: PagedDecode, device: str = "cpu"):
+    """q [B][Hq][1][d], k_cache/v_cache [num_pages][page_size][Hkv][d] (bf16),
+    block_table int32 [B][max_pages] (unused entries -1), seqlens int32 [B].
+    Draw order: Q, K cache, V cache, then the page permutation."""
+    gen = _gen(w.seed, device)
+    q = _randn((w.B, w.Hq, 1, w.d), gen, device).to(torch.bfloat16)
+    cs = (w.num_pages, w.page_size, w.Hkv, w.d)
+    kc = _randn(cs, gen, device).to(torch.bfloat16)
+    vc = _randn(cs, gen, device).to(torch.bfloat16)
+    perm = torch.randperm(w.num_pages, generator=gen, device=device).to(torch.int32)
+    table = torch.full((w.B, w.max_pages), -1, dtype=torch.int32, device=device)
+    at = 0
+    for b, n in enumerate(w.seqlens):
+        np_b = (n + w.page_size - 1) // w.page_size
+        table[b, :np_b] = perm[at:at + np_b]
+        at += np_b
+    seqlens = torch.tensor(w.seqlens, dtype=torch.int32, device=device)
+    return {"q": q.contiguous(), "k_cache": kc.contiguous(), "v_cache": vc.contiguous(),
+            "block_table": table, "seqlens": seqlens}
+
+
+# ------------------------------------------------------ variable-length batch
+
+@dataclass(frozen=True)
+class Varlen:
+    """Packed variable-length batch: the sequences are concatenated along the
+    token axis (q [total][Hq][d], k/v [total][Hkv][d]) with cumulative offsets
+    cu = [0, n0, n0+n1, ...]; queries and keys have the same lengths."""
+    name: str
+    seqlens: tuple
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool = True
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def total(self) -> int:
+        return sum(self.seqlens)
+
+    def fwd_flops(self) -> float:
+        f = sum(4.0 * self.Hq * n * n * self.d for n in self.seqlens)
+        return f * 0.5 if self.causal else f
+
+
+def make_varlen_inputs(w: Varlen, device: str = "cpu"):
+    """q [total][Hq][d], k/v [total][Hkv][d] (bf16) and cu int32 [len+1].
+    Draw order: Q, K, V."""
+    gen = _gen(w.seed, device)
+    T = w.total
+    q = _randn((T, w.Hq, w.d), gen, device).to(torch.bfloat16)
+    k = _randn((T, w.Hkv, w.d), gen, device).to(torch.bfloat16)
+    v = _randn((T, w.Hkv, w.d), gen, device).to(torch.bfloat16)
+    cu = [0]
+    for n in w.seqlens:
+        cu.append(cu[-1] + n)
+    return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(),
+            "cu": torch.tensor(cu, dtype=torch.int32, device=device)}
+
+
+PAGED = {
+    "decode_paged": PagedDecode("decode_paged", 8, 32, 8, (131072,) * 8, 16, 128, 64,
+                                seed=8307, spare_pages=1024),
+}
+VARLEN = {
+    "varlen_bf16": Varlen("varlen_bf16", (7919, 509, 3061, 1021, 6143, 257, 2053, 4099, 1531, 5113),
+                          16, 16, 128, causal=True, seed=8306),
+}
