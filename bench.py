@@ -267,6 +267,59 @@ def main(argv=None):
         log(f"decode {t_all:.3f} ms {gbs:.0f} GB/s (split {t_split:.3f} ms)")
         del xd, od, ld, opart, lpart
 
+    if not only or "decode_paged" in only:
+        from workloads import PAGED, make_paged_inputs
+        wg = PAGED["decode_paged"]
+        log("paged decode inputs")
+        xg = make_paged_inputs(wg, device="cuda")
+        S = wg.num_splits
+        og = torch.empty_like(xg["q"])
+        lg = torch.empty(wg.B, wg.Hq, 1, dtype=torch.float32, device="cuda")
+        opg = torch.empty(wg.B, wg.Hq, S, wg.d, dtype=torch.float32, device="cuda")
+        lpg = torch.empty(wg.B, wg.Hq, S, dtype=torch.float32, device="cuda")
+        mx = max(wg.seqlens)
+
+        def paged():
+            fa.fa_decode_splitkv_paged(xg["q"], xg["k_cache"], xg["v_cache"], xg["block_table"],
+                                       xg["seqlens"], opg, lpg, wg.B, wg.Hq, wg.Hkv,
+                                       wg.num_pages, wg.page_size, wg.max_pages, mx, wg.d,
+                                       wg.scale, S, sh)
+            fa.fa_decode_combine(opg, lpg, og, lg, wg.B, wg.Hq, wg.d, S, sh)
+
+        paged()
+        t = timed(paged, iters, stream)
+        keys = sum(wg.seqlens)
+        nbytes = 2 * keys * wg.Hkv * wg.d * 2 + 2 * wg.B * wg.Hq * wg.d * 2 + wg.B * wg.Hq * 4
+        gbs = nbytes / (t * 1e-3) / 1e9
+        parts["decode_paged"] = {"ms": round(t, 4), "page_size": wg.page_size,
+                                 "algorithmic_bytes": nbytes, "GB/s": round(gbs, 1),
+                                 "frac_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"paged decode {t:.3f} ms {gbs:.0f} GB/s")
+        del xg, og, lg, opg, lpg
+
+    if not only or "varlen" in only:
+        from workloads import VARLEN, make_varlen_inputs
+        wv = VARLEN["varlen_bf16"]
+        log("varlen inputs")
+        xv = make_varlen_inputs(wv, device="cuda")
+        ov = torch.empty_like(xv["q"])
+        lv = torch.empty(wv.Hq, wv.total, dtype=torch.float32, device="cuda")
+        mx = max(wv.seqlens)
+
+        def vfwd():
+            fa.fa_fwd_varlen(xv["q"], xv["k"], xv["v"], ov, lv, xv["cu"], xv["cu"],
+                             len(wv.seqlens), wv.Hq, wv.Hkv, wv.total, wv.total, mx, mx, wv.d,
+                             wv.scale, wv.causal, sh)
+
+        vfwd()
+        t = timed(vfwd, iters, stream)
+        tf = wv.fwd_flops() / (t * 1e-3) / 1e12
+        parts["fwd_varlen"] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                               "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                               "sequences": len(wv.seqlens), "tokens": wv.total}
+        log(f"varlen fwd {t:.3f} ms {tf:.0f} TF")
+        del xv, ov, lv
+
     if not only or "fp8" in only:
         wf = WORKLOADS["fp8_fwd"]
         log("fp8 inputs")

@@ -44,6 +44,8 @@ _SIGS = {
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                      _I, _F, _I, _P]),
+    "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                           _P]),
     "fa_decode_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -178,6 +180,13 @@ def fa_decode_splitkv_paged(q, k_cache, v_cache, block_table, seqlens, o_part, l
           max_pages, max_seqlen, d, scale, num_splits, _stream(stream))
 
 
+def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, Hq, Hkv, total_q, total_k, max_seqlen_q,
+                  max_seqlen_k, d, scale, causal, stream=None):
+    _call("fa_fwd_varlen", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_q), _ptr(cu_k),
+          batch, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, scale, int(causal),
+          _stream(stream))
+
+
 def fa_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream=None):
     _call("fa_decode_combine", _ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, d,
           num_splits, _stream(stream))
@@ -259,6 +268,22 @@ def decode(q, k, v, num_splits, scale=None, stream=None, return_partials=False):
     assert rows == o_part.shape[0] * o_part.shape[1] * o_part.shape[2]
     if return_partials:
         return o, lse, o_part, lse_part
+    return o, lse
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, causal=False, scale=None,
+                   stream=None):
+    """Packed variable-length forward: q [total_q][Hq][d], k/v [total_k][Hkv][d]
+    (bf16, device), cu_q/cu_k int32 [batch+1] device offsets ->
+    (O [total_q][Hq][d], LSE [Hq][total_q])."""
+    import torch
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    s = _default_scale(d, scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, cu_q.shape[0] - 1, Hq, Hkv, total_q, total_k,
+                  int(max_seqlen_q), int(max_seqlen_k), d, s, causal, stream)
     return o, lse
 
 

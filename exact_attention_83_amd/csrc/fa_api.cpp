@@ -59,6 +59,30 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
       fa::launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream));
 }
 
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int Hq,
+                        int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                        int d, float scale, int causal, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (batch <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || total_q <= 0 || total_k <= 0 ||
+      max_seqlen_q <= 0 || max_seqlen_k <= 0 || max_seqlen_q > total_q ||
+      max_seqlen_k > total_k || d <= 0)
+    return FA_ERR_INVALID_ARG;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: every K/V row of the pack must be addressable.
+  if ((int64_t)total_k * Hkv * d * 2 >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)batch * Hq * ((max_seqlen_q + 255) / 256);
+  if (units >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_fwd_bf16_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k,
+                                               batch, Hq, Hkv, total_q, max_seqlen_q, d, scale,
+                                               causal != 0, stream));
+}
+
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                      hipStream_t stream) {

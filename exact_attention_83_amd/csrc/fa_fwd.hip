@@ -56,11 +56,19 @@ __device__ __forceinline__ int fwd_swz_v(int r) {
   return D == 128 ? (4 * (r & 3)) : (4 * ((r >> 1) & 1));
 }
 
-template <int D, bool CAUSAL, int NW, int NS>
+// VARLEN: packed variable-length batch ([CH18] §18.7.1): Q/O are token-major
+// [total_q][Hq][D], K/V [total_k][Hkv][D]; sequence b owns query rows
+// cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1, and its
+// attention (causal: top-left) stays inside them; LSE is [Hq][total_q].  The
+// grid covers batch x Hq x (query tiles of the longest sequence); tiles past
+// a sequence's end exit at once.
+template <int D, bool CAUSAL, int NW, int NS, bool VARLEN = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int Hq, int Hkv, int Nq, int Nk, float scale, float scale_log2, int BH, int nqt) {
+    int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale, float scale_log2, int BH, int nqt,
+    const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
+    int total_q = 0) {
   constexpr int BC = kFwdBc;
   constexpr int ROWB = D * 2;               // bytes per K/V row in LDS (no padding)
   constexpr int NCH = D / 8;                // 16-byte chunks per row
@@ -97,14 +105,41 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int hk = h / (Hq / Hkv);
-  const uint16_t* Qp = Q + (size_t)bh * Nq * D;
-  const size_t kv_off = (size_t)(b * Hkv + hk) * Nk * D;
-  // rows past Nk read as zero (and are masked below)
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kv_off, (uint32_t)Nk * ROWB);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * ROWB);
-
+  // This work unit's query and key counts, bases and row strides (elements
+  // between consecutive rows: D for [B][H][N][D], H*D when packed).
+  int Nq = Nq_arg, Nk = Nk_arg;
+  size_t q_base = (size_t)bh * Nq * D;
+  size_t kv_off = (size_t)(b * Hkv + hk) * Nk * D;
+  size_t lse_base = (size_t)bh * Nq;
+  const int SQ = VARLEN ? Hq * D : D;
+  const int SKVB = (VARLEN ? Hkv * D : D) * 2;  // bytes
   const int q0 = qt * BR;
   const int qrow = q0 + wave * 32 + l32;
+  if constexpr (VARLEN) {
+    const int qs0 = cu_q[b], ks0 = cu_k[b];
+    Nq = cu_q[b + 1] - qs0;
+    Nk = cu_k[b + 1] - ks0;
+    if (q0 >= Nq) return;  // the whole workgroup: past this sequence's rows
+    q_base = ((size_t)qs0 * Hq + h) * D;
+    kv_off = ((size_t)ks0 * Hkv + hk) * D;
+    lse_base = (size_t)h * total_q + qs0;
+    if (Nk <= 0) {  // no visible key: O = 0, LSE = -inf
+      if (qrow < Nq) {
+        uint16_t* Op = O + q_base + (size_t)qrow * SQ;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) stg<u32x2>(Op + db * 32 + g * 8 + hf * 4, u32x2{0u, 0u});
+        if (hf == 0) LSE[lse_base + qrow] = -INFINITY;
+      }
+      return;
+    }
+  }
+  const uint16_t* Qp = Q + q_base;
+  // rows past Nk read as zero (and are masked below)
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kv_off, (uint32_t)Nk * SKVB);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * SKVB);
+
   const int qrow_c = qrow < Nq ? qrow : Nq - 1;
 
   // Q fragments (B operand of S^T = K Q^T): k-step ks covers head dims
@@ -112,7 +147,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   u32x4 qf[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks)
-    qf[ks] = ldg<u32x4>(Qp + (size_t)qrow_c * D + ks * 16 + hf * 8);
+    qf[ks] = ldg<u32x4>(Qp + (size_t)qrow_c * SQ + ks * 16 + hf * 8);
 
   const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -124,18 +159,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   for (int i = 0; i < LPW; ++i) {
     const int r = (wave * LPW + i) * RPL + lane / NCH;
     const int p = lane % NCH;
-    koff[i] = r * ROWB + ((p ^ fwd_swz_k<D>(r)) << 4);
-    voff[i] = r * ROWB + ((p ^ fwd_swz_v<D>(r)) << 4);
+    koff[i] = r * SKVB + ((p ^ fwd_swz_k<D>(r)) << 4);
+    voff[i] = r * SKVB + ((p ^ fwd_swz_v<D>(r)) << 4);
   }
   auto issue_k = [&](int j, int slot) {
     char* d = kslot(slot) + wave * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rK, d + i * 1024, koff[i], j * TILE);
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rK, d + i * 1024, koff[i], j * BC * SKVB);
   };
   auto issue_v = [&](int j, int slot) {
     char* d = vslot(slot) + wave * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rV, d + i * 1024, voff[i], j * TILE);
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rV, d + i * 1024, voff[i], j * BC * SKVB);
   };
 
   // Per-lane LDS read offsets.  K (A operand, row kb*32 + l32, chunk 2*kk + hf):
@@ -384,7 +419,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   const float l_tot = sum_halves(l_run);
   const float inv = 1.f / l_tot;
   if (qrow < Nq) {
-    uint16_t* Op = O + ((size_t)bh * Nq + qrow) * D;
+    uint16_t* Op = O + q_base + (size_t)qrow * SQ;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -393,7 +428,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
         stg<u32x2>(Op + d0, u32x2{pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
                                   pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)});
       }
-    if (hf == 0) LSE[(size_t)bh * Nq + qrow] = (M + __log2f(l_tot)) * kLn2;
+    if (hf == 0) LSE[lse_base + qrow] = (M + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -492,6 +527,33 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
       hipLaunchKernelGGL((fwd_bf16_kernel<64, false, NW, NS>), grid, block, 0, stream, Qp, Kp,
                          Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int* cu_q, const int* cu_k, int batch,
+                                  int Hq, int Hkv, int total_q, int max_seqlen_q, int d,
+                                  float scale, bool causal, hipStream_t stream) {
+  constexpr int NW = kFwdWaves, NS = kFwdStages;
+  const int BH = batch * Hq;
+  const int nqt = (max_seqlen_q + kFwdBr - 1) / kFwdBr;
+  dim3 grid(BH * nqt), block(NW * 64);
+  const float sl2 = scale * kLog2e;
+  auto Qp = (const uint16_t*)q;
+  auto Kp = (const uint16_t*)k;
+  auto Vp = (const uint16_t*)v;
+  auto Op = (uint16_t*)o;
+#define FA_LAUNCH_VARLEN(DD, CC)                                                              \
+  hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC, NW, NS, true>), grid, block, 0, stream, Qp, Kp, \
+                     Vp, Op, lse, Hq, Hkv, 0, 0, scale, sl2, BH, nqt, cu_q, cu_k, total_q)
+  if (d == 128) {
+    if (causal) FA_LAUNCH_VARLEN(128, true);
+    else FA_LAUNCH_VARLEN(128, false);
+  } else {
+    if (causal) FA_LAUNCH_VARLEN(64, true);
+    else FA_LAUNCH_VARLEN(64, false);
+  }
+#undef FA_LAUNCH_VARLEN
   return hipGetLastError();
 }
 

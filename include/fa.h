@@ -75,6 +75,31 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, hipStream_t stream);
 
 /*
+ * Forward over a packed variable-length batch, bf16 ([CH18] §18.7.1: the
+ * sequences are concatenated along the token axis and cumulative offsets
+ * give each one's rows; attention never crosses a sequence boundary and the
+ * causal mask applies inside each sequence).
+ *   q, o [total_q][Hq][d] and k, v [total_k][Hkv][d], bf16, token-major (the
+ *   page's (total_tokens, nheads, headdim)).
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [batch+1], non-decreasing, from
+ *   0 to total_q / total_k; sequence b owns query rows cu_seqlens_q[b] ..
+ *   cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.
+ *   lse [Hq][total_q] fp32 (natural log).
+ *   max_seqlen_q / max_seqlen_k: the longest sequence (sizes the launch;
+ *   must be >= every sequence's length).
+ * causal: key j visible to query i of the same sequence iff j <= i
+ * (top-left, as for fa_fwd; meant for equal query and key lengths).  A
+ * sequence with queries but no keys gets O = 0 and LSE = -inf.  The offsets
+ * are device data and are not checked on the host; they must satisfy the
+ * above.  d in {64, 128}; total_k * Hkv * d * 2 < 2^31.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k,
+                        int batch, int Hq, int Hkv, int total_q, int total_k,
+                        int max_seqlen_q, int max_seqlen_k, int d,
+                        float scale, int causal, hipStream_t stream);
+
+/*
  * Forward, fp32 in and out (same layout and meaning as fa_fwd).  d == 64.
  * Query and key tiles are 64 rows, so Nk = 256 exercises four rounds of
  * online rescaling.

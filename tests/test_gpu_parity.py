@@ -248,6 +248,99 @@ def test_decode_config_full(fa_gpu):
             assert maxabs(lp[b, sl], rlp[0]) <= BF16_LSE
 
 
+# ---------------------------------------------------------- varlen forward
+
+def varlen_case(lens_q, Hq, Hkv, d, seed, lens_k=None):
+    lens_k = lens_q if lens_k is None else lens_k
+    g = torch.Generator("cpu").manual_seed(seed)
+    tq, tk = sum(lens_q), sum(lens_k)
+    q = torch.randn(tq, Hq, d, generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn(tk, Hkv, d, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(tk, Hkv, d, generator=g).to(torch.bfloat16).cuda()
+    cq, ck = [0], [0]
+    for a, b in zip(lens_q, lens_k):
+        cq.append(cq[-1] + a)
+        ck.append(ck[-1] + b)
+    return q, k, v, cq, ck
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,d", [
+    ((5, 300, 1, 257), 4, 2, 128),       # ragged tails, a single-token sequence
+    ((1000,), 2, 2, 64),
+    ((40, 0, 77, 513), 8, 1, 128),       # an empty sequence; G = 8
+    ((256, 255, 257), 2, 2, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_forward_small(fa_gpu, lens, Hq, Hkv, d, causal):
+    q, k, v, cq, ck = varlen_case(lens, Hq, Hkv, d, seed=71)
+    say(f"varlen forward lens={lens} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    cqd = torch.tensor(cq, dtype=torch.int32, device="cuda")
+    o, lse = fa_gpu.forward_varlen(q, k, v, cqd, cqd, max(lens), max(lens), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = A.forward_varlen(to_f64(q), to_f64(k), to_f64(v), cq, ck, 1 / math.sqrt(d), causal)
+    assert maxabs(to_f64(o), ro) <= BF16_O
+    assert maxabs(to_f64(lse), rl) <= BF16_LSE
+
+
+def test_varlen_queries_without_keys(fa_gpu):
+    """Non-causal pack where one sequence has queries but no keys: its rows
+    get O = 0 and LSE = -inf; the others are unaffected."""
+    q, k, v, cq, ck = varlen_case((5, 9, 70), 2, 2, 128, seed=72, lens_k=(0, 33, 100))
+    say("varlen forward, a sequence without keys")
+    o, lse = fa_gpu.forward_varlen(q, k, v, torch.tensor(cq, dtype=torch.int32, device="cuda"),
+                                   torch.tensor(ck, dtype=torch.int32, device="cuda"), 70, 100)
+    torch.cuda.synchronize()
+    ro, rl = A.forward_varlen(to_f64(q), to_f64(k), to_f64(v), cq, ck, 1 / math.sqrt(128))
+    lo = to_f64(lse)
+    assert np.all(np.isneginf(lo[:, :5])) and not np.any(to_f64(o)[:5])
+    assert maxabs(to_f64(o), ro) <= BF16_O
+    assert maxabs(lo[:, 5:], rl[:, 5:]) <= BF16_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_dense(fa_gpu, causal):
+    """Sequences of equal length packed token-major run the same arithmetic as
+    the [B][H][N][d] forward: outputs agree bit for bit."""
+    B, N, Hq, Hkv, d = 3, 1000, 4, 2, 128
+    q, k, v, cq, _ = varlen_case((N,) * B, Hq, Hkv, d, seed=73)
+    say(f"varlen vs dense causal={causal}")
+    cqd = torch.tensor(cq, dtype=torch.int32, device="cuda")
+    o, lse = fa_gpu.forward_varlen(q, k, v, cqd, cqd, N, N, causal=causal)
+    qd = q.view(B, N, Hq, d).permute(0, 2, 1, 3).contiguous()
+    kd = k.view(B, N, Hkv, d).permute(0, 2, 1, 3).contiguous()
+    vd = v.view(B, N, Hkv, d).permute(0, 2, 1, 3).contiguous()
+    od, lsed = fa_gpu.forward(qd, kd, vd, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(B, N, Hq, d).permute(0, 2, 1, 3), od)
+    assert torch.equal(lse.view(Hq, B, N).permute(1, 0, 2), lsed)
+
+
+def test_varlen_config_sampled(fa_gpu):
+    """The packed workload (10 sequences, 31706 tokens, H=16, d=128, causal):
+    sampled query rows of every sequence and head against the oracle."""
+    from workloads import VARLEN, make_varlen_inputs
+    w = VARLEN["varlen_bf16"]
+    x = make_varlen_inputs(w, device="cuda")
+    say("varlen_bf16 full size")
+    mx = max(w.seqlens)
+    o, lse = fa_gpu.forward_varlen(x["q"], x["k"], x["v"], x["cu"], x["cu"], mx, mx,
+                                   causal=w.causal)
+    torch.cuda.synchronize()
+    o, lse = to_f64(o), to_f64(lse)
+    cu = x["cu"].tolist()
+    rs = np.random.default_rng(5)
+    for b, n in enumerate(w.seqlens):
+        rows = sorted(set([0, n - 1] + rs.integers(0, n, 6).tolist()))
+        sl = slice(cu[b], cu[b + 1])
+        qq = to_f64(x["q"][sl]).transpose(1, 0, 2)[None]
+        kk = to_f64(x["k"][sl]).transpose(1, 0, 2)[None]
+        vv = to_f64(x["v"][sl]).transpose(1, 0, 2)[None]
+        ro, rl = A.forward(qq, kk, vv, w.scale, w.causal, rows=rows)
+        got_o = o[cu[b] + np.array(rows)].transpose(1, 0, 2)
+        got_l = lse[:, cu[b] + np.array(rows)]
+        assert maxabs(got_o, ro[0]) <= BF16_O, b
+        assert maxabs(got_l, rl[0]) <= BF16_LSE, b
+
+
 # ------------------------------------------------------------- paged decode
 
 def paged_case(B, Hq, Hkv, seqlens, page, d, splits, seed, spare=3):
