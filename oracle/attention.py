@@ -33,30 +33,43 @@ def kv_head(hq: int, Hq: int, Hkv: int) -> int:
     return hq // (Hq // Hkv)
 
 
-def allowed(Nq: int, Nk: int, causal: bool, rows=None) -> np.ndarray:
+def allowed(Nq: int, Nk: int, causal: bool, rows=None, window=None) -> np.ndarray:
     """Boolean [len(rows)][Nk] mask of keys each query may attend.
 
     [CH18] §18.2.2 (3): M_ij = 0 for j <= i and -inf for j > i.
+    ``window`` = (left, right) ([CH18] §18.7.1, window_size): key j is visible
+    to query i only if i - left <= j <= i + right; -1 leaves that side
+    unbounded, and (-1, -1) is global attention.
     """
     rows = np.arange(Nq) if rows is None else np.asarray(rows)
-    if not causal:
-        return np.ones((len(rows), Nk), dtype=bool)
-    assert Nq == Nk, "causal attention is defined here for Nq == Nk only"
-    return np.arange(Nk)[None, :] <= rows[:, None]
+    ok = np.ones((len(rows), Nk), dtype=bool)
+    j = np.arange(Nk)[None, :]
+    i = rows[:, None]
+    if causal or window is not None:
+        assert Nq == Nk, "causal / windowed attention is defined here for Nq == Nk only"
+    if causal:
+        ok &= j <= i
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            ok &= j >= i - left
+        if right >= 0:
+            ok &= j <= i + right
+    return ok
 
 
-def scores(q, k, scale, causal, rows=None):
+def scores(q, k, scale, causal, rows=None, window=None):
     """S = scale * Q K^T for one head, with masked entries set to -inf.
 
     q: [Nq][d], k: [Nk][d]; ``rows`` selects query rows.  [CH18] §18.2.1 and
-    §18.2.2 (3).
+    §18.2.2 (3); ``window`` as in ``allowed``.
     """
     q = _f64(q)
     k = _f64(k)
     r = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     s = scale * (q[r] @ k.T)
-    if causal:
-        s = np.where(allowed(q.shape[0], k.shape[0], True, r), s, -np.inf)
+    if causal or window is not None:
+        s = np.where(allowed(q.shape[0], k.shape[0], causal, r, window), s, -np.inf)
     return s
 
 
@@ -69,19 +82,19 @@ def softmax_rows(s):
     return e / l[:, None], m, l
 
 
-def head_forward(q, k, v, scale, causal, rows=None):
+def head_forward(q, k, v, scale, causal, rows=None, window=None):
     """O and LSE for one (b, head): O = softmax(scale Q K^T + M) V.
 
     [CH18] §18.2.1 (definition), §18.2.2 (causal mask); LSE as stored by the
     forward for the recomputation backward ([CH18] §18.2.4, Fig. 18-6).
     """
-    s = scores(q, k, scale, causal, rows)
+    s = scores(q, k, scale, causal, rows, window)
     p, m, l = softmax_rows(s)
     o = p @ _f64(v)
     return o, m + np.log(l)
 
 
-def forward(q, k, v, scale, causal=False, rows=None):
+def forward(q, k, v, scale, causal=False, rows=None, window=None):
     """Batched forward.  q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] -> (O, LSE) fp64.
 
     ``rows`` optionally restricts the queries evaluated (each row of O depends
@@ -97,13 +110,13 @@ def forward(q, k, v, scale, causal=False, rows=None):
         for h in range(Hq):
             hk = kv_head(h, Hq, Hkv)
             o[b, h], lse[b, h] = head_forward(q[b, h], k[b, hk], v[b, hk], scale,
-                                              causal, rows)
+                                              causal, rows, window)
     return o, lse
 
 
-def probabilities(q, k, scale, causal=False):
+def probabilities(q, k, scale, causal=False, window=None):
     """Full attention matrix P for one head (used by invariance checks)."""
-    p, _, _ = softmax_rows(scores(q, k, scale, causal))
+    p, _, _ = softmax_rows(scores(q, k, scale, causal, window=window))
     return p
 
 
@@ -113,13 +126,13 @@ def softmax_backward(p, dp):
     return p * (dp - (p * dp).sum(axis=1, keepdims=True))
 
 
-def head_backward(q, k, v, do, scale, causal):
+def head_backward(q, k, v, do, scale, causal, window=None):
     """Materialising backward for one head, [CH18] §18.2.4 (2):
     dV = P^T dO, dP = dO V^T, dS = softmax_backward(P, dP), dQ = scale dS K,
     dK = scale dS^T Q.  Returns (dq, dk, dv, delta) with delta_i = sum_j P_ij dP_ij.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    p, _, _ = softmax_rows(scores(q, k, scale, causal))
+    p, _, _ = softmax_rows(scores(q, k, scale, causal, window=window))
     dv = p.T @ do
     dp = do @ v.T
     ds = softmax_backward(p, dp)
@@ -129,7 +142,7 @@ def head_backward(q, k, v, do, scale, causal):
     return dq, dk, dv, delta
 
 
-def backward(q, k, v, do, scale, causal=False):
+def backward(q, k, v, do, scale, causal=False, window=None):
     """Batched backward -> (dQ, dK, dV) fp64.  A KV head's gradient is the sum
     over the query heads that read it (GQA broadcast, [CH18] §18.2.2)."""
     q = _f64(q)
@@ -142,7 +155,7 @@ def backward(q, k, v, do, scale, causal=False):
         for h in range(Hq):
             hk = kv_head(h, Hq, Hkv)
             a, bk, bv, _ = head_backward(q[b, h], k[b, hk], v[b, hk], do[b, h],
-                                         scale, causal)
+                                         scale, causal, window)
             dq[b, h] = a
             dk[b, hk] += bk
             dv[b, hk] += bv

@@ -510,3 +510,80 @@ def test_paged_decode_uniform_scores_mean_of_first_rows():
             rows = [vc[table[b][t // page], t % page, hk] for t in range(n)]
             assert np.allclose(o[b, h, 0], np.mean(rows, axis=0), atol=1e-13)
             assert abs(lse[b, h, 0] - math.log(n)) < 1e-13
+
+
+# ------------------------------------------------------- sliding-window pins
+
+@pytest.mark.parametrize("causal,window", [(False, (3, 2)), (True, (4, -1)), (True, (0, 0)),
+                                           (False, (-1, 1)), (False, (0, 5))])
+def test_window_uniform_scores_mean_of_window(causal, window):
+    """Closed form: Q = 0 gives row i the mean of V over the keys
+    max(0, i-left) .. min(N-1, i+right) (and <= i when causal), and
+    LSE = ln(count)."""
+    N, d = 11, 4
+    q = np.zeros((1, 1, N, d))
+    k, v = rnd(1, 1, N, d), rnd(1, 1, N, d)
+    o, lse = A.forward(q, k, v, 0.8, causal, window=window)
+    left, right = window
+    for i in range(N):
+        lo = 0 if left < 0 else max(0, i - left)
+        hi = N - 1 if right < 0 else min(N - 1, i + right)
+        if causal:
+            hi = min(hi, i)
+        assert np.allclose(o[0, 0, i], v[0, 0, lo:hi + 1].mean(axis=0), atol=1e-13)
+        assert abs(lse[0, 0, i] - math.log(hi - lo + 1)) < 1e-13
+
+
+def test_window_brute_force_loops():
+    """Scalar loops over (i, j) with the window written out."""
+    N, d, left, right, scale = 9, 3, 2, 3, 0.6
+    q, k, v = rnd(1, 1, N, d), rnd(1, 1, N, d), rnd(1, 1, N, d)
+    o, lse = A.forward(q, k, v, scale, False, window=(left, right))
+    for i in range(N):
+        w = [math.exp(scale * float(q[0, 0, i] @ k[0, 0, j])) if i - left <= j <= i + right
+             else 0.0 for j in range(N)]
+        w = np.array(w)
+        assert np.allclose(o[0, 0, i], (w[:, None] * v[0, 0]).sum(0) / w.sum(), atol=1e-12)
+        assert abs(lse[0, 0, i] - math.log(w.sum())) < 1e-12
+
+
+def test_window_degenerate_and_trivial_cases():
+    """(0, 0): each row sees only its own key, so O = V and LSE = s_ii.
+    (-1, -1) is global attention; causal with (-1, 0) or (N, 0) is causal."""
+    N, d, scale = 7, 5, 0.9
+    q, k, v = rnd(2, 2, N, d), rnd(2, 2, N, d), rnd(2, 2, N, d)
+    o, lse = A.forward(q, k, v, scale, False, window=(0, 0))
+    assert np.allclose(o, v, atol=1e-14)
+    assert np.allclose(lse, scale * np.einsum("bhnd,bhnd->bhn", q, k), atol=1e-13)
+    og, lg = A.forward(q, k, v, scale, False)
+    ow, lw = A.forward(q, k, v, scale, False, window=(-1, -1))
+    assert np.array_equal(og, ow) and np.array_equal(lg, lw)
+    oc, lc = A.forward(q, k, v, scale, True)
+    for win in ((-1, 0), (N, 0), (-1, -1)):
+        ow, lw = A.forward(q, k, v, scale, True, window=win)
+        assert np.array_equal(oc, ow) and np.array_equal(lc, lw)
+
+
+@pytest.mark.parametrize("causal,window", [(True, (2, -1)), (False, (1, 2))])
+def test_window_backward_finite_differences(causal, window):
+    """Central differences of L = sum(O * G) under a sliding window (GQA)."""
+    B, Hq, Hkv, N, d, scale = 1, 2, 1, 6, 3, 0.7
+    q, k, v, g = rnd(B, Hq, N, d), rnd(B, Hkv, N, d), rnd(B, Hkv, N, d), rnd(B, Hq, N, d)
+    dq, dk, dv = A.backward(q, k, v, g, scale, causal, window=window)
+
+    def loss(q_, k_, v_):
+        return float((A.forward(q_, k_, v_, scale, causal, window=window)[0] * g).sum())
+
+    h = 1e-6
+    for x, dx in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.linalg.norm(num - dx) <= 1e-7 * max(1.0, np.linalg.norm(dx))
