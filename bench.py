@@ -267,6 +267,40 @@ def main(argv=None):
         log(f"decode {t_all:.3f} ms {gbs:.0f} GB/s (split {t_split:.3f} ms)")
         del xd, od, ld, opart, lpart
 
+    if not only or "window" in only:
+        from workloads import WINDOWED
+        ww = WINDOWED["window_bf16"]
+        log("window inputs")
+        xw = make_inputs(ww, device="cuda")
+        ow = torch.empty_like(xw["q"])
+        lw = torch.empty(ww.B, ww.Hq, ww.Nq, dtype=torch.float32, device="cuda")
+        dqw, dkw, dvw = (torch.empty_like(xw[n]) for n in ("q", "k", "v"))
+        wsb = fa.fa_bwd_workspace_size(ww.B, ww.Hq, ww.Nq, ww.d)
+        wsw = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        wa = (ww.B, ww.Hq, ww.Hkv, ww.Nq, ww.Nk, ww.d, ww.scale, ww.causal, ww.window_left,
+              ww.window_right, sh)
+
+        def wf():
+            fa.fa_fwd_window(xw["q"], xw["k"], xw["v"], ow, lw, *wa)
+
+        def wb():
+            fa.fa_bwd_window(xw["q"], xw["k"], xw["v"], ow, xw["do"], lw, dqw, dkw, dvw, wsw, wsb,
+                             *wa)
+
+        wf(); wb()
+        tfw = timed(wf, iters, stream)
+        tbw = timed(wb, iters, stream)
+        fl = ww.fwd_flops()
+        parts["window_causal"] = {"window": [ww.window_left, ww.window_right],
+                                  "fwd_ms": round(tfw, 4),
+                                  "fwd_tflops": round(fl / (tfw * 1e-3) / 1e12, 1),
+                                  "bwd_ms": round(tbw, 4),
+                                  "bwd_tflops": round(2.5 * fl / (tbw * 1e-3) / 1e12, 1),
+                                  "fwd_frac_peak": round(fl / (tfw * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                  "bwd_frac_peak": round(2.5 * fl / (tbw * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"window fwd {tfw:.3f} ms, bwd {tbw:.3f} ms")
+        del xw, ow, lw, dqw, dkw, dvw, wsw
+
     if not only or "decode_paged" in only:
         from workloads import PAGED, make_paged_inputs
         wg = PAGED["decode_paged"]

@@ -46,6 +46,9 @@ _SIGS = {
                                      _I, _F, _I, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                            _P]),
+    "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                           _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_decode_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -187,6 +190,19 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, Hq, Hkv, total_q, total_k,
           _stream(stream))
 
 
+def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, window_left,
+                  window_right, stream=None):
+    _call("fa_fwd_window", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+          scale, int(causal), window_left, window_right, _stream(stream))
+
+
+def fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq,
+                  Nk, d, scale, causal, window_left, window_right, stream=None):
+    _call("fa_bwd_window", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+          _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale,
+          int(causal), window_left, window_right, _stream(stream))
+
+
 def fa_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream=None):
     _call("fa_decode_combine", _ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, d,
           num_splits, _stream(stream))
@@ -222,21 +238,27 @@ def _default_scale(d, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def forward(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
-    """O, LSE for bf16 (or fp32) q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d]."""
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None, window=None):
+    """O, LSE for bf16 (or fp32) q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d].
+    ``window`` = (left, right) selects the sliding-window entry point (bf16)."""
     import torch
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     s = _default_scale(d, scale)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if window is not None:
+        fa_fwd_window(q, k, v, o, l, B, Hq, Hkv, Nq, Nk, d, s, causal, int(window[0]),
+                      int(window[1]), stream)
+        return o, l
     fn = fa_fwd_f32 if q.dtype == torch.float32 else fa_fwd
     fn(q, k, v, o, l, B, Hq, Hkv, Nq, Nk, d, s, causal, stream)
     return o, l
 
 
-def backward(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None, stream=None):
-    """dQ, dK, dV for the forward above (same dtype as q)."""
+def backward(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None, stream=None,
+             window=None):
+    """dQ, dK, dV for the forward above (same dtype as q; ``window`` as there)."""
     import torch
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
@@ -246,6 +268,10 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None, st
     dv = torch.empty_like(v)
     ws_bytes = fa_bwd_workspace_size(B, Hq, Nq, d)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    if window is not None:
+        fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, ws, ws.numel() * ws.element_size(), B,
+                      Hq, Hkv, Nq, Nk, d, s, causal, int(window[0]), int(window[1]), stream)
+        return dq, dk, dv
     fn = fa_bwd_f32 if q.dtype == torch.float32 else fa_bwd
     fn(q, k, v, o, dout, lse, dq, dk, dv, ws, ws.numel() * ws.element_size(), B, Hq, Hkv, Nq,
        Nk, d, s, causal, stream)

@@ -59,6 +59,21 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
       fa::launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream));
 }
 
+static bool good_window(int win_l, int win_r) { return win_l >= -1 && win_r >= -1; }
+
+fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                        int window_left, int window_right, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (!good_scale(scale) || !good_window(window_left, window_right)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Nq != Nk) return FA_ERR_UNSUPPORTED;  // window positions are defined for Nq == Nk
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                                        causal != 0, stream, window_left, window_right));
+}
+
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int Hq,
                         int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
@@ -132,6 +147,28 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (e == hipSuccess)
     e = fa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Nq, Nk, d, scale,
                           causal != 0, stream);
+  return hip_status(e);
+}
+
+fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                        int Nk, int d, float scale, int causal, int window_left,
+                        int window_right, hipStream_t stream) {
+  if (fa_status s = bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
+                               Hq, Hkv, Nq, Nk, d, scale, causal))
+    return s;
+  if (!good_window(window_left, window_right)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Nq != Nk) return FA_ERR_UNSUPPORTED;
+  float* delta = static_cast<float*>(workspace);
+  hipError_t e = fa::launch_bwd_pre(o, dout, delta, B, Hq, Nq, d, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                            causal != 0, stream, window_left, window_right);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Nq, Nk, d, scale,
+                          causal != 0, stream, window_left, window_right);
   return hip_status(e);
 }
 

@@ -233,13 +233,16 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk) {
 // transposing reads of the row-major dO and Q tiles, again shared by the key
 // blocks.  The dK/dV accumulators (256 registers at d = 128) live in the
 // accumulation registers, so one wave runs per SIMD.
-template <int D, bool CAUSAL>
+// WIN: sliding window (key j visible to query i iff i - win_l <= j <= i +
+// win_r; negative = unbounded): only the query tiles whose windows reach this
+// work unit's keys are visited.
+template <int D, bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk,
-    float scale, float scale_log2, int BHkv) {
+    float scale, float scale_log2, int BHkv, int win_l = -1, int win_r = -1) {
   constexpr int NW = kKvWaves;
   constexpr int KB = kKvKb;
   constexpr int BQ = kKvBq;
@@ -298,8 +301,13 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   }
 
   const int nqt = (Nq + BQ - 1) / BQ;
-  const int qt_begin = CAUSAL ? kv0 / BQ : 0;
-  const int per_head = nqt - qt_begin;
+  int qt_begin = CAUSAL ? kv0 / BQ : 0;
+  int qt_end = nqt;
+  if constexpr (WIN) {
+    if (win_r >= 0) qt_begin = max(qt_begin, max(0, kv0 - win_r) / BQ);
+    if (win_l >= 0) qt_end = min(qt_end, (kv0 + BKV - 1 + win_l) / BQ + 1);
+  }
+  const int per_head = max(0, qt_end - qt_begin);
   const int total = per_head * G;
   auto tile_head = [&](int it, int* bh, int* q0) {
     const int gi = it / per_head;
@@ -407,12 +415,19 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int key = kbase + kb * 32 + l32;
-      if ((kbase + kb * 32 + 32 > Nk) || (q0 + BQ > Nq) ||
-          (CAUSAL && kbase + kb * 32 + 31 > q0)) {
+      const int kb0 = kbase + kb * 32;
+      bool need = (kb0 + 32 > Nk) || (q0 + BQ > Nq) || (CAUSAL && kb0 + 31 > q0);
+      if constexpr (WIN)
+        need = need || (win_l >= 0 && kb0 < q0 + BQ - 1 - win_l) ||
+               (win_r >= 0 && kb0 + 31 > q0 + win_r);
+      if (need) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = q0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= Nk || qi >= Nq || (CAUSAL && key > qi)) sb[kb][r] = -INFINITY;
+          bool out = key >= Nk || qi >= Nq || (CAUSAL && key > qi);
+          if constexpr (WIN)
+            out = out || (win_l >= 0 && key < qi - win_l) || (win_r >= 0 && key > qi + win_r);
+          if (out) sb[kb][r] = -INFINITY;
         }
       }
     }
@@ -552,13 +567,15 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 // so lse and delta are per-lane scalars; dS^T (rounded to bf16) is the B
 // operand of dQ^T += K^T dS^T, whose A operand is a transposing read of the
 // row-major K tile.  K/V tiles of 64 keys are double-buffered in LDS.
-template <int D, bool CAUSAL>
+// WIN: sliding window as for bwd_dkdv_kernel; only the key tiles that some
+// row's window reaches are visited.
+template <int D, bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, float scale, float scale_log2,
-    int BH, int nqt) {
+    int BH, int nqt, int win_l = -1, int win_r = -1) {
   constexpr int NW = kDqWaves;
   constexpr int BR = kDqBr;
   constexpr int BC = kDqBc;
@@ -603,8 +620,13 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   const float lse2 = LSE[(size_t)bh * Nq + qrow_c] * kLog2e;
   const float dlt = Delta[(size_t)bh * Nq + qrow_c];
 
-  const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
+  int jf = 0;  // first key tile visited
+  if constexpr (WIN) {
+    if (win_r >= 0) kv_end = min(kv_end, q0 + BR + win_r);
+    if (win_l >= 0) jf = max(0, q0 - win_l) / BC;
+  }
+  const int ntiles = (kv_end + BC - 1) / BC - jf;
 
   int ldo[LPW];
 #pragma unroll
@@ -614,8 +636,8 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     char* dv_ = vslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      buffer_load_lds16(rK, dk_ + i * 1024, ldo[i], j * TILE);
-      buffer_load_lds16(rV, dv_ + i * 1024, ldo[i], j * TILE);
+      buffer_load_lds16(rK, dk_ + i * 1024, ldo[i], (jf + j) * TILE);
+      buffer_load_lds16(rV, dv_ + i * 1024, ldo[i], (jf + j) * TILE);
     }
   };
   // A operands of S^T / dP^T (b128): key row kb*32 + l32, chunk 2*ks + hf.
@@ -643,7 +665,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   }
   settle(lse2);
   settle(dlt);
-  issue(0, 0);
+  if (ntiles > 0) issue(0, 0);
   // One iteration per KV tile; S = slot (a compile-time constant).
   auto body = [&](int j, auto S) {
     constexpr int slot = decltype(S)::value;
@@ -651,7 +673,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     lds_barrier();
     const char* ks_ = kslot(slot);
     const char* vs_ = vslot(slot);
-    const int kv0 = j * BC;
+    const int kv0 = (jf + j) * BC;
 
     // Three phases so that the elementwise work runs beside matrix products:
     // (A) S^T = K Q^T; (B) dP^T = V dO^T with P = exp(S*scale - lse) of the
@@ -680,14 +702,21 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
       }
       s[kb] = mfma_32x32x16_bf16(ka, qf[kk], s[kb]);
     }
-    const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
+    const int rw0 = q0 + wave * 32;  // this wave's first row
+    bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > rw0);
+    if constexpr (WIN)
+      need_mask = need_mask || (win_l >= 0 && kv0 < rw0 + 31 - win_l) ||
+                  (win_r >= 0 && kv0 + BC - 1 > rw0 + win_r);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= Nk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+          bool out = key >= Nk || (CAUSAL && key > qrow);
+          if constexpr (WIN)
+            out = out || (win_l >= 0 && key < qrow - win_l) || (win_r >= 0 && key > qrow + win_r);
+          if (out) s[kb][r] = -INFINITY;
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -795,7 +824,7 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int B, 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                            const float* lse, const float* delta, void* dk, void* dv, int B,
                            int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal,
-                           hipStream_t stream) {
+                           hipStream_t stream, int win_l, int win_r) {
   const int BHkv = B * Hkv;
   dim3 grid(BHkv * ((Nk + kKvBkv - 1) / kKvBkv)), block(kKvWaves * 64);
   auto Q = (const uint16_t*)q;
@@ -805,15 +834,27 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   auto dK = (uint16_t*)dk;
   auto dV = (uint16_t*)dv;
   const float sl2 = scale * kLog2e;
-#define FA_LAUNCH_DKDV(DD, CC)                                                          \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, dkdv_vbuf_bytes(DD), stream, \
-                     Q, K, V, G, lse, delta, dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv)
+#define FA_LAUNCH_DKDV(DD, CC, WW)                                                          \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC, WW>), grid, block, dkdv_vbuf_bytes(DD), stream, \
+                     Q, K, V, G, lse, delta, dK, dV, Hq, Hkv, Nq, Nk, scale, sl2, BHkv, win_l,  \
+                     win_r)
+  const bool win = win_l >= 0 || win_r >= 0;
   if (d == 128) {
-    if (causal) FA_LAUNCH_DKDV(128, true);
-    else FA_LAUNCH_DKDV(128, false);
+    if (win) {
+      if (causal) FA_LAUNCH_DKDV(128, true, true);
+      else FA_LAUNCH_DKDV(128, false, true);
+    } else {
+      if (causal) FA_LAUNCH_DKDV(128, true, false);
+      else FA_LAUNCH_DKDV(128, false, false);
+    }
   } else {
-    if (causal) FA_LAUNCH_DKDV(64, true);
-    else FA_LAUNCH_DKDV(64, false);
+    if (win) {
+      if (causal) FA_LAUNCH_DKDV(64, true, true);
+      else FA_LAUNCH_DKDV(64, false, true);
+    } else {
+      if (causal) FA_LAUNCH_DKDV(64, true, false);
+      else FA_LAUNCH_DKDV(64, false, false);
+    }
   }
 #undef FA_LAUNCH_DKDV
   return hipGetLastError();
@@ -821,7 +862,8 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                          const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
-                         int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream) {
+                         int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream,
+                         int win_l, int win_r) {
   const int BH = B * Hq;
   const int nqt = (Nq + kDqBr - 1) / kDqBr;
   dim3 grid(BH * nqt), block(kDqWaves * 64);
@@ -831,15 +873,26 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   auto G = (const uint16_t*)dout;
   auto dQ = (uint16_t*)dq;
   const float sl2 = scale * kLog2e;
-#define FA_LAUNCH_DQ(DD, CC)                                                                   \
-  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, Q, K, V, G, lse, delta, \
-                     dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt)
+#define FA_LAUNCH_DQ(DD, CC, WW)                                                              \
+  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW>), grid, block, 0, stream, Q, K, V, G, lse,     \
+                     delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, win_l, win_r)
+  const bool win = win_l >= 0 || win_r >= 0;
   if (d == 128) {
-    if (causal) FA_LAUNCH_DQ(128, true);
-    else FA_LAUNCH_DQ(128, false);
+    if (win) {
+      if (causal) FA_LAUNCH_DQ(128, true, true);
+      else FA_LAUNCH_DQ(128, false, true);
+    } else {
+      if (causal) FA_LAUNCH_DQ(128, true, false);
+      else FA_LAUNCH_DQ(128, false, false);
+    }
   } else {
-    if (causal) FA_LAUNCH_DQ(64, true);
-    else FA_LAUNCH_DQ(64, false);
+    if (win) {
+      if (causal) FA_LAUNCH_DQ(64, true, true);
+      else FA_LAUNCH_DQ(64, false, true);
+    } else {
+      if (causal) FA_LAUNCH_DQ(64, true, false);
+      else FA_LAUNCH_DQ(64, false, false);
+    }
   }
 #undef FA_LAUNCH_DQ
   return hipGetLastError();

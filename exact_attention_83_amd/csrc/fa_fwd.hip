@@ -62,13 +62,17 @@ __device__ __forceinline__ int fwd_swz_v(int r) {
 // attention (causal: top-left) stays inside them; LSE is [Hq][total_q].  The
 // grid covers batch x Hq x (query tiles of the longest sequence); tiles past
 // a sequence's end exit at once.
-template <int D, bool CAUSAL, int NW, int NS, bool VARLEN = false>
+// WIN: sliding window ([CH18] §18.7.1, window_size = (left, right)): key j is
+// visible to query i only if i - win_l <= j <= i + win_r (a negative bound is
+// unbounded); only the key tiles that intersect some row's window are
+// visited.
+template <int D, bool CAUSAL, int NW, int NS, bool VARLEN = false, bool WIN = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale, float scale_log2, int BH, int nqt,
     const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
-    int total_q = 0) {
+    int total_q = 0, int win_l = -1, int win_r = -1) {
   constexpr int BC = kFwdBc;
   constexpr int ROWB = D * 2;               // bytes per K/V row in LDS (no padding)
   constexpr int NCH = D / 8;                // 16-byte chunks per row
@@ -149,8 +153,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   for (int ks = 0; ks < KSTEPS; ++ks)
     qf[ks] = ldg<u32x4>(Qp + (size_t)qrow_c * SQ + ks * 16 + hf * 8);
 
-  const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
+  int jf = 0;  // first key tile visited
+  if constexpr (WIN) {
+    if (win_r >= 0) kv_end = min(kv_end, q0 + BR + win_r);
+    if (win_l >= 0) jf = max(0, q0 - win_l) / BC;
+  }
+  const int ntiles = (kv_end + BC - 1) / BC - jf;
 
   // Per-lane source offsets of this wave's direct loads (same for every tile):
   // LDS block (wave*LPW + i) of a tile holds rows r, lane -> position p.
@@ -165,12 +174,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   auto issue_k = [&](int j, int slot) {
     char* d = kslot(slot) + wave * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rK, d + i * 1024, koff[i], j * BC * SKVB);
+    for (int i = 0; i < LPW; ++i)
+      buffer_load_lds16(rK, d + i * 1024, koff[i], (jf + j) * BC * SKVB);
   };
   auto issue_v = [&](int j, int slot) {
     char* d = vslot(slot) + wave * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rV, d + i * 1024, voff[i], j * BC * SKVB);
+    for (int i = 0; i < LPW; ++i)
+      buffer_load_lds16(rV, d + i * 1024, voff[i], (jf + j) * BC * SKVB);
   };
 
   // Per-lane LDS read offsets.  K (A operand, row kb*32 + l32, chunk 2*kk + hf):
@@ -222,15 +233,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   // Mask one S^T tile: keys past the end (ragged tail) and, on tiles crossing
   // the diagonal, keys after the query ([CH18] §18.5.2).
   auto mask = [&](int j, f32x16* s) {
-    const int kv0 = j * BC;
-    const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
+    const int kv0 = (jf + j) * BC;
+    const int rw0 = q0 + wave * 32;  // this wave's first row
+    bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > rw0);
+    if constexpr (WIN)
+      need_mask = need_mask || (win_l >= 0 && kv0 < rw0 + 31 - win_l) ||
+                  (win_r >= 0 && kv0 + BC - 1 > rw0 + win_r);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= Nk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+          bool out = key >= Nk || (CAUSAL && key > qrow);
+          if constexpr (WIN)
+            out = out || (win_l >= 0 && key < qrow - win_l) || (win_r >= 0 && key > qrow + win_r);
+          if (out) s[kb][r] = -INFINITY;
         }
     }
   };
@@ -272,8 +290,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   __syncthreads();
   qk(0, sbuf[0]);
   mask(0, sbuf[0]);
-  // Start the reference at tile 0's max (finite: key 0 is visible to every
-  // row; the floor only guards rows past Nq).
+  // Start the reference at tile 0's max (finite without a window: key 0 is
+  // visible to every row).  The floor covers rows that see nothing in tile 0
+  // (past Nq, or outside a sliding window): their first visible tile then
+  // overflows the lazy bound and takes the rescale path, which moves the
+  // reference to that tile's max and zeroes the (empty) O and l.
   M = fmaxf(tile_max(sbuf[0]), -1e30f);
   lds_barrier();  // K slot 0 is refilled below
 
@@ -502,7 +523,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                           bool causal, hipStream_t stream) {
+                           bool causal, hipStream_t stream, int win_l, int win_r) {
   constexpr int NW = kFwdWaves, NS = kFwdStages;
   const int BH = B * Hq;
   const int nqt = (Nq + kFwdBr - 1) / kFwdBr;
@@ -512,21 +533,29 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   auto Kp = (const uint16_t*)k;
   auto Vp = (const uint16_t*)v;
   auto Op = (uint16_t*)o;
+#define FA_LAUNCH_FWD(DD, CC, WW)                                                               \
+  hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC, NW, NS, false, WW>), grid, block, 0, stream, Qp, \
+                     Kp, Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, nullptr, nullptr, 0, \
+                     win_l, win_r)
+  const bool win = win_l >= 0 || win_r >= 0;
   if (d == 128) {
-    if (causal)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, true, NW, NS>), grid, block, 0, stream, Qp, Kp,
-                         Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, false, NW, NS>), grid, block, 0, stream, Qp, Kp,
-                         Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
+    if (win) {
+      if (causal) FA_LAUNCH_FWD(128, true, true);
+      else FA_LAUNCH_FWD(128, false, true);
+    } else {
+      if (causal) FA_LAUNCH_FWD(128, true, false);
+      else FA_LAUNCH_FWD(128, false, false);
+    }
   } else {
-    if (causal)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, true, NW, NS>), grid, block, 0, stream, Qp, Kp,
-                         Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, false, NW, NS>), grid, block, 0, stream, Qp, Kp,
-                         Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt);
+    if (win) {
+      if (causal) FA_LAUNCH_FWD(64, true, true);
+      else FA_LAUNCH_FWD(64, false, true);
+    } else {
+      if (causal) FA_LAUNCH_FWD(64, true, false);
+      else FA_LAUNCH_FWD(64, false, false);
+    }
   }
+#undef FA_LAUNCH_FWD
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ namespace fa {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                           bool causal, hipStream_t stream);
+                           bool causal, hipStream_t stream, int win_l = -1, int win_r = -1);
 hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o,
                                   float* lse, const int* cu_q, const int* cu_k, int batch,
                                   int Hq, int Hkv, int total_q, int max_seqlen_q, int d,
@@ -31,10 +31,11 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int B, 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                            const float* lse, const float* delta, void* dk, void* dv, int B,
                            int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal,
-                           hipStream_t stream);
+                           hipStream_t stream, int win_l = -1, int win_r = -1);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                          const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
-                         int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream);
+                         int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream,
+                         int win_l = -1, int win_r = -1);
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
                                float* lse_part, int B, int Hq, int Hkv, int Nk, int d,

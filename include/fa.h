@@ -75,6 +75,21 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, hipStream_t stream);
 
 /*
+ * Forward with a sliding window, bf16 ([CH18] §18.7.1, window_size =
+ * (left, right); §18.8.1: a sliding window is a block-sparse pattern, and
+ * only the key tiles inside some row's window are visited).  Same tensors and
+ * meaning as fa_fwd, with key j visible to query i only if
+ * i - window_left <= j <= i + window_right (and j <= i when causal); -1
+ * leaves a side unbounded, so (-1, -1) is plain fa_fwd.  Requires Nq == Nk
+ * (positions are aligned top-left); window values below -1 are
+ * FA_ERR_INVALID_ARG.  d in {64, 128}.
+ */
+fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                        float scale, int causal, int window_left, int window_right,
+                        hipStream_t stream);
+
+/*
  * Forward over a packed variable-length batch, bf16 ([CH18] §18.7.1: the
  * sequences are concatenated along the token axis and cumulative offsets
  * give each one's rows; attention never crosses a sequence boundary and the
@@ -134,6 +149,19 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* workspace, size_t workspace_bytes,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d,
                  float scale, int causal, hipStream_t stream);
+
+/*
+ * Backward with a sliding window (the gradients of fa_fwd_window): same
+ * arguments and workspace as fa_bwd plus the window; o and lse as written by
+ * fa_fwd_window for the same inputs and window.  Requires Nq == Nk.
+ */
+fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                        float scale, int causal, int window_left, int window_right,
+                        hipStream_t stream);
 
 /*
  * The three stages of fa_bwd as separate calls, for callers that schedule or

@@ -166,6 +166,81 @@ def test_causal_config_sampled(fa_gpu):
             assert e <= BF16_GRAD, (b, h, name, e)
 
 
+# ----------------------------------------------------------- sliding window
+
+WINDOWS = [(37, 5), (0, 0), (200, -1), (-1, 100), (300, 300), (1000, 0), (64, 63)]
+
+
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,shape", [(128, (1, 4, 2, 700)), (64, (2, 2, 1, 1111))])
+def test_window_forward_backward_small(fa_gpu, window, causal, d, shape):
+    B, Hq, Hkv, N = shape
+    x = gen(B, Hq, Hkv, N, N, d, "bf16", 91, grad=True)
+    say(f"window fwd+bwd window={window} causal={causal} d={d} shape={shape}")
+    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=causal, window=window)
+    torch.cuda.synchronize()
+    q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    ro, rl = A.forward(q, k, v, 1 / math.sqrt(d), causal, window=window)
+    assert maxabs(to_f64(o), ro) <= BF16_O
+    assert maxabs(to_f64(lse), rl) <= BF16_LSE
+    grads = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal,
+                            window=window)
+    torch.cuda.synchronize()
+    ref = A.backward(q, k, v, do, 1 / math.sqrt(d), causal, window=window)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        e = rel_l2(to_f64(got), want)
+        assert e <= BF16_GRAD, (name, e)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_covering_everything_equals_dense(fa_gpu, causal):
+    """A window wider than the sequence runs the windowed kernels with every
+    mask test false: outputs and gradients equal the plain kernels' bit for
+    bit."""
+    N = 1000
+    x = gen(2, 4, 2, N, N, 128, "bf16", 92, grad=True)
+    say(f"window covering everything causal={causal}")
+    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=causal)
+    ow, lw = fa_gpu.forward(x["q"], x["k"], x["v"], causal=causal, window=(N, N))
+    g = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal)
+    gw = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal, window=(N, N))
+    torch.cuda.synchronize()
+    assert torch.equal(o, ow) and torch.equal(lse, lw)
+    for a, b in zip(g, gw):
+        assert torch.equal(a, b)
+
+
+def test_window_config_sampled(fa_gpu):
+    """B=2 H=16 N=8192 d=128, causal with a 4096-key left window (the page's
+    Mistral example), in the benchmark's launch configuration: sampled
+    forward rows of every head, dQ/dK/dV of two heads from the oracle."""
+    from workloads import WINDOWED
+    w = WINDOWED["window_bf16"]
+    x = {n: t.cuda() for n, t in make_inputs(w).items()}
+    win = (w.window_left, w.window_right)
+    say("forward window_bf16 full size")
+    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=w.causal, window=win)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 4095, 4096, 4097, 4352, 5000, 6143, 8000, 8191])
+    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
+    o_ref, lse_ref = A.forward(q, k, v, w.scale, w.causal, rows=rows, window=win)
+    assert maxabs(to_f64(o)[:, :, rows], o_ref) <= BF16_O
+    assert maxabs(to_f64(lse)[:, :, rows], lse_ref) <= BF16_LSE
+    say("backward window_bf16 full size")
+    dq, dk, dv = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=w.causal,
+                                 window=win)
+    torch.cuda.synchronize()
+    do = to_f64(x["do"])
+    dq, dk, dv = to_f64(dq), to_f64(dk), to_f64(dv)
+    for (b, h) in ((0, 3), (1, 12)):
+        rq, rk, rv, _ = A.head_backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal,
+                                        window=win)
+        for name, got, want in (("dq", dq[b, h], rq), ("dk", dk[b, h], rk), ("dv", dv[b, h], rv)):
+            e = rel_l2(got, want)
+            assert e <= BF16_GRAD, (b, h, name, e)
+
+
 # ------------------------------------------------------------------- decode
 
 def check_decode(fa, B, Hq, Hkv, Nk, d, splits, seed):

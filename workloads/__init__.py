@@ -226,3 +226,34 @@ VARLEN = {
     "varlen_bf16": Varlen("varlen_bf16", (7919, 509, 3061, 1021, 6143, 257, 2053, 4099, 1531, 5113),
                           16, 16, 128, causal=True, seed=8306),
 }
+
+
+# ---------------------------------------------------------- sliding window
+
+@dataclass(frozen=True)
+class Windowed(Workload):
+    """A Workload with a sliding window: key j is visible to query i only if
+    i - window_left <= j <= i + window_right (-1: unbounded)."""
+    window_left: int = -1
+    window_right: int = -1
+
+    def visible_pairs(self) -> int:
+        # keys visible per query row, summed over the rows
+        n = self.Nq
+        tot = 0
+        for i in range(n):
+            lo = 0 if self.window_left < 0 else max(0, i - self.window_left)
+            hi = n - 1 if self.window_right < 0 else min(n - 1, i + self.window_right)
+            if self.causal:
+                hi = min(hi, i)
+            tot += max(0, hi - lo + 1)
+        return tot
+
+    def fwd_flops(self) -> float:
+        return 4.0 * self.B * self.Hq * self.d * self.visible_pairs()
+
+
+WINDOWED = {
+    "window_bf16": Windowed("window_bf16", 2, 16, 16, 8192, 8192, 128, "bf16", causal=True,
+                            backward=True, seed=8308, window_left=4096, window_right=0),
+}
