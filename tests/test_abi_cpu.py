@@ -160,3 +160,60 @@ def test_forward_schedule_matches_greedy_lpt(lib, workers):
     inorder = sorted(range(len(cost)), key=lambda i: (bh[i], qt[i]))
     worst, _ = SCH.list_schedule([cost[i] for i in inorder], workers)
     assert max(loads) <= max(worst)
+
+
+def test_window_validation(lib):
+    """fa_fwd_window / fa_bwd_window: window sides below -1, Nq != Nk, head
+    dims, workspace."""
+    N = 128
+
+    def fwd(wl=-1, wr=0, Nq=N, Nk=N, d=128):
+        return lib.fa_fwd_window(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, Nq, Nk, d, 0.1, 1, wl, wr,
+                                 None)
+    assert fwd(wl=-2) == fa.FA_ERR_INVALID_ARG
+    assert fwd(wr=-7) == fa.FA_ERR_INVALID_ARG
+    assert fwd(Nk=N + 1) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(d=96) == fa.FA_ERR_UNSUPPORTED
+    need = lib.fa_bwd_workspace_size(1, 2, N, 128)
+
+    def bwd(ws=FAKE, wl=16, wr=16, Nk=N):
+        return lib.fa_bwd_window(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, need,
+                                 1, 2, 2, N, Nk, 128, 0.1, 0, wl, wr, None)
+    assert bwd(ws=None) == fa.FA_ERR_WORKSPACE
+    assert bwd(wl=-3) == fa.FA_ERR_INVALID_ARG
+    assert bwd(Nk=N - 1) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_varlen_validation(lib):
+    """fa_fwd_varlen: offset pointers, totals against the longest sequence,
+    the GQA ratio, head dims and the 32-bit K/V byte range."""
+    def call(cq=FAKE, ck=FAKE, batch=2, Hq=4, Hkv=2, tq=100, tk=100, mq=60, mk=60, d=128):
+        return lib.fa_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, cq, ck, batch, Hq, Hkv, tq, tk, mq,
+                                 mk, d, 0.1, 1, None)
+    assert call(cq=None) == fa.FA_ERR_INVALID_ARG
+    assert call(ck=FAKE + 2) == fa.FA_ERR_INVALID_ARG
+    assert call(batch=0) == fa.FA_ERR_INVALID_ARG
+    assert call(mq=101) == fa.FA_ERR_INVALID_ARG
+    assert call(mk=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Hq=3) == fa.FA_ERR_INVALID_ARG
+    assert call(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert call(tk=1 << 20, mk=1 << 20, Hkv=16, Hq=16) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_paged_decode_validation(lib):
+    """fa_decode_splitkv_paged: page sizes (powers of two, 16..4096), table
+    capacity against max_seqlen, pointers, splits, group size."""
+    def call(table=FAKE, lens=FAKE, B=2, Hq=8, Hkv=2, pages=64, page=16, maxp=8, maxs=100,
+             d=128, S=4):
+        return lib.fa_decode_splitkv_paged(FAKE, FAKE, FAKE, table, lens, FAKE, FAKE, B, Hq, Hkv,
+                                           pages, page, maxp, maxs, d, 0.1, S, None)
+    assert call(page=24) == fa.FA_ERR_UNSUPPORTED
+    assert call(page=8) == fa.FA_ERR_UNSUPPORTED
+    assert call(page=8192, maxs=100) == fa.FA_ERR_UNSUPPORTED
+    assert call(maxs=129) == fa.FA_ERR_INVALID_ARG       # 8 pages of 16 hold 128 keys
+    assert call(table=None) == fa.FA_ERR_INVALID_ARG
+    assert call(lens=FAKE + 1) == fa.FA_ERR_INVALID_ARG
+    assert call(S=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Hq=7) == fa.FA_ERR_INVALID_ARG
+    assert call(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert call(Hq=128, Hkv=2) == fa.FA_ERR_UNSUPPORTED  # group of 64 > 32
