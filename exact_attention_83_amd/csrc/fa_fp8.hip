@@ -133,143 +133,170 @@ __global__ __launch_bounds__(128) void quantize_fp8_kernel(const uint16_t* __res
 
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kF8Br = 128;
-constexpr int kF8Bc = 64;
+constexpr int kF8Waves = 8;
+constexpr int kF8Br = 32 * kF8Waves;  // query rows per workgroup
+constexpr int kF8Bc = 64;             // keys per tile (one 64-deep k-step of P V)
+
+// Chunk swizzles of the fp8 K and V tiles (128-byte rows, 16-byte chunks):
+// K is read as the A operand of S^T = K Q^T (16 rows, one chunk pair each),
+// V through the transposing byte read (two lanes per row, 8 rows, one chunk
+// per lane pair), so each swizzle spreads its own read pattern over all 64
+// banks.
+__device__ __forceinline__ int f8_swz_k(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int f8_swz_v(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+// ds_read_b64_tr_b8: within each group of 16 lanes, lanes 2r and 2r+1 address
+// the two 8-byte halves of row r (r = 0..7) of an 8 x 16-byte tile, and output
+// lane i receives byte i of rows 0..7 (byte k of the result from row k).
+__device__ __forceinline__ i32x2_t lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p);
+}
 }  // namespace
 
+// FP8 forward, the bf16 forward's layout on the 32x32x64 fp8 MFMA: 8 waves x
+// 32 query rows, S^T = K Q^T with Q in registers (B operand), P^T rounded to
+// e4m3 as the B operand of O^T += V^T P^T, K and V tiles of 64 keys straight
+// from HBM into two LDS slots each (swizzled), V^T A operands from transposing
+// byte reads.  The QK^T products of tile i+1 and the PV products of tile i-1
+// run one by one between the exp work of tile i; the reference max is lazy.
+// Scales: S = (Q8 K8^T) s_q s_k scale, folded into one coefficient per tile;
+// V's per-block scale s_v is folded into the exp argument relative to the
+// largest V scale of the row's keys (p' = 2^3 p s_v / s_vmax), so O needs no
+// per-tile rescale and l sums p' s_vmax / s_v.  The lazy bound (a lane's sum
+// of p' over a tile at most 448) keeps every code inside e4m3's range; the
+// 2^3 keeps probabilities down to 2^-13 of the reference representable, and
+// cancels in O / l (LSE subtracts it).
 template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
+__global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk,
     float scale_log2, int BH, int nqt) {
   constexpr int D = 128;
+  constexpr int NW = kF8Waves;
+  constexpr int BR = kF8Br;
   constexpr int BC = kF8Bc;
-  constexpr int KP = D + 16;      // K row pitch (bytes)
-  constexpr int VP = BC + 4;      // V^T row pitch (bytes)
-  constexpr int KSLOT = BC * KP;
-  constexpr int VSLOT = D * VP;
+  constexpr int ROWB = D;              // bytes per fp8 row
+  constexpr int TILE = BC * ROWB;      // 8 KB
   constexpr int DBLK = D / 32;
-  __shared__ __attribute__((aligned(16))) char smem[2 * (KSLOT + VSLOT)];
+  static_assert(TILE / 1024 == NW, "one 1 KB direct load per wave per tile");
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE], kb1[TILE], vb0[TILE], vb1[TILE];
+  auto kslot = [&](int s) -> char* { return s == 0 ? kb0 : kb1; };
+  auto vslot = [&](int s) -> char* { return s == 0 ? vb0 : vb1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int bh = blockIdx.x % BH;
-  const int qt = CAUSAL ? (nqt - 1 - blockIdx.x / BH) : (blockIdx.x / BH);
+  int bh, qt;
+  query_tile_of(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int hk = h / (Hq / Hkv);
   const int bhk = b * Hkv + hk;
-  const uint8_t* Qp = Q + (size_t)bh * Nq * D;
-  const uint8_t* Kp = K + (size_t)bhk * Nk * D;
-  const uint8_t* Vp = V + (size_t)bhk * Nk * D;
   const int nkb = (Nk + kQBlk - 1) / kQBlk;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (size_t)bhk * Nk * D, (uint32_t)Nk * ROWB);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (size_t)bhk * Nk * D, (uint32_t)Nk * ROWB);
 
-  const int q0 = qt * kF8Br;
+  const int q0 = qt * BR;
   const int qrow = q0 + wave * 32 + l32;
   const int qrow_c = qrow < Nq ? qrow : Nq - 1;
-  const float sq = QS[(size_t)bh * ((Nq + kQBlk - 1) / kQBlk) + qt];
+  // this wave's 32 rows lie in one 128-row quantisation block of Q (clamped:
+  // rows past Nq are computed but never written)
+  const int nqb = (Nq + kQBlk - 1) / kQBlk;
+  const float sq = QS[(size_t)bh * nqb + min((q0 + wave * 32) / kQBlk, nqb - 1)];
 
   // Q8 fragments: k-step s, lane half hf holds head dims 64*s + 32*hf .. +32.
   i32x8 qf[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const uint8_t* p = Qp + (size_t)qrow_c * D + s * 64 + hf * 32;
+    const uint8_t* p = Q + ((size_t)bh * Nq + qrow_c) * D + s * 64 + hf * 32;
     u32x4 a = ldg<u32x4>(p), c = ldg<u32x4>(p + 16);
     qf[s] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
   }
 
-  const int kv_end = CAUSAL ? min(Nk, q0 + kF8Br) : Nk;
+  const int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
   const int ntiles = (kv_end + BC - 1) / BC;
+  // Largest V scale over the key blocks this unit visits.
+  float svm = 0.f;
+  {
+    const int nb = (kv_end + kQBlk - 1) / kQBlk;
+    for (int i = lane; i < nb; i += 64) svm = fmaxf(svm, VS[(size_t)bhk * nkb + i]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) svm = fmaxf(svm, __shfl_xor(svm, m, 64));
+  }
 
-  // staging: K 2 chunks/thread; V: 128 threads x (4 keys x 16 bytes)
-  u32x4 kreg[2], vreg[4];
-  const int v_rg = tid >> 3;   // 0..31 for tid < 128 -> keys 4*v_rg..
-  const int v_col = tid & 7;   // 16-byte column
-  const bool v_active = tid < 128;
-  auto load_tile = [&](int j) {
-    const int kv0 = j * BC;
+  // Direct loads: wave w moves rows 8w .. 8w+7 of a tile; lane -> row 8w +
+  // lane/8, LDS chunk position lane%8 holding source chunk (lane%8) ^ swz.
+  const int drow = wave * 8 + (lane >> 3);
+  const int dpos = lane & 7;
+  const int koff = drow * ROWB + ((dpos ^ f8_swz_k(drow)) << 4);
+  const int voff = drow * ROWB + ((dpos ^ f8_swz_v(drow)) << 4);
+  auto issue_k = [&](int j, int slot) { buffer_load_lds16(rK, kslot(slot) + wave * 1024, koff, j * TILE); };
+  auto issue_v = [&](int j, int slot) { buffer_load_lds16(rV, vslot(slot) + wave * 1024, voff, j * TILE); };
+
+  // K A operand (row kb*32 + l32, head dims 64*st + 32*hf .. +32 = chunks
+  // c0 = 4*st + 2*hf and c0 + 1, stored at positions c0 ^ swz and that ^ 1).
+  int krd[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, col = c & 7;
-      int key = kv0 + row;
-      key = key < Nk ? key : Nk - 1;
-      kreg[i] = ldg<u32x4>(Kp + (size_t)key * D + col * 16);
-    }
-    if (v_active) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int key = kv0 + (v_rg & 15) * 4 + i;
-        key = key < Nk ? key : Nk - 1;
-        // threads 0..127: 16 key groups x 8 columns
-        vreg[i] = ldg<u32x4>(Vp + (size_t)key * D + v_col * 16);
-      }
-    }
+  for (int st = 0; st < 2; ++st) krd[st] = l32 * ROWB + (((4 * st + 2 * hf) ^ f8_swz_k(l32)) << 4);
+  auto kfrag = [&](const char* ks, int kb, int st) {
+    const char* p = ks + kb * 32 * ROWB;
+    const u32x4 a0 = lds_read<u32x4>(p, krd[st]);
+    const u32x4 a1 = lds_read<u32x4>(p, krd[st] ^ 16);
+    return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
   };
-  auto store_tile = [&](int slot) {
-    char* ks = smem + slot * (KSLOT + VSLOT);
-    char* vs = ks + KSLOT;
+  // V^T A operand of head-dim block db: byte i of lane half hf is key
+  // 32*(i/16) + 8*((i/4)%4) + 4*hf + i%4 (the S accumulator's order), four
+  // transposing reads of 8 keys each.  Source lane 2r + half of group g16
+  // addresses key row 8*(r/4) + 4*hf + r%4 (+ 16*(read%2) + 32*(read/2)),
+  // head dims 32*db + 16*(g16%2) + 8*half.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int vr = j16 >> 1, vhalf = j16 & 1;
+  const int vrow = 8 * (vr >> 2) + 4 * hf + (vr & 3);
+  int vrd[DBLK];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, col = c & 7;
-      lds_write<u32x4>(ks, row * KP + col * 16, kreg[i]);
+  for (int db = 0; db < DBLK; ++db)
+    vrd[db] = vrow * ROWB + (((2 * db + (g16 & 1)) ^ f8_swz_v(vrow)) << 4) + 8 * vhalf;
+  auto vfrag = [&](const char* vs, int db) {
+    int w[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const i32x2_t x = lds_read_tr8(vs + ((t >> 1) * 32 + (t & 1) * 16) * ROWB + vrd[db]);
+      w[2 * t] = x[0];
+      w[2 * t + 1] = x[1];
     }
-    if (v_active) {
-      const int rg = v_rg & 15;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // byte e of word w of each of the 4 key rows -> one dword of 4 keys
-          const uint32_t sel = 0x0c0c0000u | ((e + 4) << 8) | e;  // (k0.e, k1.e, 0, 0)
-          const uint32_t lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-          const uint32_t hi = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-          const uint32_t v4 = (lo & 0xffffu) | (hi << 16);
-          lds_write<uint32_t>(vs, (v_col * 16 + w * 4 + e) * VP + rg * 4, v4);
-        }
-    }
+    return i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
   };
 
-  f32x16 o[DBLK];
+  // Per-tile coefficients: c_j multiplies the raw fp8 product (log2 units),
+  // e_j = log2(s_v / s_vmax) is added to the exp argument, r_j = s_vmax / s_v
+  // converts the tile's sum of p' back to p.
+  auto tile_coef = [&](int j, float* c, float* e, float* r) {
+    const int blk = (j * BC) / kQBlk;
+    const float sk = KS[(size_t)bhk * nkb + blk];
+    const float sv = VS[(size_t)bhk * nkb + blk];
+    *c = sq * sk * scale_log2;
+    *e = sv > 0.f ? __log2f(sv / svm) : 0.f;
+    *r = sv > 0.f ? svm / sv : 0.f;
+  };
+
+  auto qk = [&](int j, f32x16* s) {
+    const char* ks = kslot(j & 1);
+    s[0] = f32x16{0};
+    s[1] = f32x16{0};
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{0};
-  float m_run = -INFINITY;  // running max in log2 units
-  float l_run = 0.f;
-  float sv_prev = 1.f;
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int slot = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-    const char* ks = smem + slot * (KSLOT + VSLOT);
-    const char* vs = ks + KSLOT;
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_32x32x64_fp8(kfrag(ks, kb, st), qf[st], s[kb]);
+  };
+  auto mask = [&](int j, f32x16* s) {
     const int kv0 = j * BC;
-    const int kblk = kv0 / kQBlk;
-    const float cj = sq * KS[(size_t)bhk * nkb + kblk] * scale_log2;
-    const float sv = VS[(size_t)bhk * nkb + kblk];
-
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{0};
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int off = (kb * 32 + l32) * KP + st * 64 + hf * 32;
-        u32x4 a0 = lds_read<u32x4>(ks, off), a1 = lds_read<u32x4>(ks, off + 16);
-        i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                        (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        s[kb] = mfma_32x32x64_fp8(a, qf[st], s[kb]);
-      }
-    }
     const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + wave * 32);
     if (need_mask) {
 #pragma unroll
@@ -280,56 +307,150 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
           if (key >= Nk || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
         }
     }
+  };
+  auto tile_max = [&](const f32x16* s) {
     float mt = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, xor32(mt)) * cj;
-    const float m_new = fmaxf(m_run, mt);
-    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_ref);
-    const float bias = 8.f - m_ref;  // P is produced as 2^8 * p
-    m_run = m_new;
-    // O is kept in units of the current tile's V scale.
-    const float f = alpha * (sv_prev / sv);
-    sv_prev = sv;
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) o[i] *= f;
+    return max_halves(mt);
+  };
 
-    float psum = 0.f;
-    int pw[8];
+  f32x16 o[DBLK];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{0};
+  constexpr float kLazyLimit = 448.f;  // e4m3 max
+  constexpr float kP8Shift = 3.f;      // p' carries a factor 2^3
+  float M;
+  float l_run = 0.f;
+
+  f32x16 sbuf[2][2];
+  i32x8 pbuf[2];  // [parity]: P'^T B operands (e4m3)
+  pbuf[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  // prologue: K_0, K_1; V slot 1 zeroed so that the first step's product with
+  // "tile -1" (P = 0) adds exactly zero.
+  issue_k(0, 0);
+  if (ntiles > 1) issue_k(1, 1);
+  for (int off = tid * 16; off < TILE; off += NW * 64 * 16) lds_write<u32x4>(vslot(1), off, u32x4{0, 0, 0, 0});
+  wait_vmem();
+  __syncthreads();
+  qk(0, sbuf[0]);
+  mask(0, sbuf[0]);
+  {
+    float c0, e0, r0;
+    tile_coef(0, &c0, &e0, &r0);
+    M = fmaxf(tile_max(sbuf[0]) * c0, -1e30f);
+  }
+  lds_barrier();  // K slot 0 is refilled below
+
+  constexpr int NG = 8;            // product groups per step: 4 QK^T, 4 PV
+  constexpr int EPG = 32 / NG;     // elements of S_i per group (per lane)
+  auto step = [&](int i, auto U) {
+    constexpr int u = decltype(U)::value;
+    f32x16* s_cur = sbuf[u];
+    f32x16* s_nxt = sbuf[u ^ 1];
+    const bool more_k = i + 2 < ntiles;
+    float ci, ei, ri;
+    tile_coef(i, &ci, &ei, &ri);
+    const float bias = ei - M + kP8Shift;
+    float lt = 0.f;
+    {
+      const char* ks = kslot(u ^ 1);   // K_{i+1}
+      const char* vs = vslot(u ^ 1);   // V_{i-1}
+      s_nxt[0] = f32x16{0};
+      s_nxt[1] = f32x16{0};
+      i32x8 kfr = kfrag(ks, 0, 0);
+      i32x8 vfr = vfrag(vs, 0);
+      asm volatile("" ::: "memory");
+      if (more_k) issue_k(i + 2, u);
+      issue_v(i, u);
+      float p[32];
+      int pw[8];
+      auto F = [&](int gg) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float p[4];
+        for (int e = gg * EPG; e < (gg + 1) * EPG; ++e)
+          p[e] = fmaf(s_cur[e >> 4][e & 15], ci, bias);
+      };
+      auto X = [&](int gg) {
+#pragma unroll
+        for (int e = gg * EPG; e < (gg + 1) * EPG; ++e) p[e] = fast_exp2(p[e]);
+      };
+      auto A = [&](int gg) {
+#pragma unroll
+        for (int e = gg * EPG; e < (gg + 1) * EPG; ++e) lt += p[e];
+        const int k = gg;  // EPG == 4: one dword of four codes per group
+        pw[k] = cvt_fp8x4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
+        settle(pw[k]);
+      };
+      static_assert(EPG == 4, "one packed dword per group");
+      F(0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int h = g >> 1;  // product index within its kind (0..3)
+        if ((g & 1) == 0) {
+          // QK^T product h: kb = h%2, st = h/2
+          s_nxt[h & 1] = mfma_32x32x64_fp8(kfr, qf[h >> 1], s_nxt[h & 1]);
+          if (h + 1 < 4) kfr = kfrag(ks, (h + 1) & 1, (h + 1) >> 1);
+        } else {
+          o[h] = mfma_32x32x64_fp8(vfr, pbuf[u ^ 1], o[h]);
+          if (h + 1 < DBLK) vfr = vfrag(vs, h + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 1 < NG) F(g + 1);
+        X(g);
+        if (g > 0) A(g - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      A(NG - 1);
+      pbuf[u] = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    }
+    // Rare: the reference is too low for tile i.  Move it to the tile's max,
+    // rescale O (which holds tiles up to i-1) and l, and redo tile i's p'.
+    if (__builtin_amdgcn_ballot_w64(lt > kLazyLimit)) {
+      const float Mn = fmaxf(M, tile_max(s_cur) * ci);
+      const float alpha = fast_exp2(M - Mn);
+      M = Mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int d4 = 0; d4 < DBLK; ++d4) o[d4] *= alpha;
+      lt = 0.f;
+      const float bias2 = ei - M + kP8Shift;
+      int pw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float q4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(fmaf(s[kb][4 * g + e], cj, bias));
-          psum += p[e];
+          q4[e] = fast_exp2(fmaf(s_cur[(4 * k + e) >> 4][(4 * k + e) & 15], ci, bias2));
+          lt += q4[e];
         }
-        pw[kb * 4 + g] = cvt_fp8x4(p[0], p[1], p[2], p[3]);
+        pw[k] = cvt_fp8x4(q4[0], q4[1], q4[2], q4[3]);
       }
-    l_run = l_run * alpha + psum;
-    // B element i = 16*kb + 4*g + e of lane half hf is key kb*32 + 8*g + 4*hf + e.
-    const i32x8 pb = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      int a[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          a[kb * 4 + g] = (int)lds_read<uint32_t>(vs, (db * 32 + l32) * VP + kb * 32 + g * 8 + hf * 4);
-      o[db] = mfma_32x32x64_fp8(i32x8{a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7]}, pb, o[db]);
+      pbuf[u] = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     }
-    if (j + 1 < ntiles) store_tile(slot ^ 1);
-    __syncthreads();
+    l_run += lt * ri;
+    if (i + 1 < ntiles) mask(i + 1, s_nxt);
+    wait_vmem();
+    lds_barrier();
+  };
+  for (int i0 = 0; i0 < ntiles; i0 += 2) {
+    step(i0, IntConst<0>{});
+    if (i0 + 1 < ntiles) step(i0 + 1, IntConst<1>{});
   }
+  // The last tile's O^T += V^T P'^T.
+  auto pv_last = [&](auto U) {
+    constexpr int u = decltype(U)::value;
+    const char* vs = vslot(u);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[db] = mfma_32x32x64_fp8(vfrag(vs, db), pbuf[u], o[db]);
+  };
+  if ((ntiles - 1) & 1) pv_last(IntConst<1>{});
+  else pv_last(IntConst<0>{});
 
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = sv_prev / l_tot;
+  // Epilogue: O = O^T s_vmax / l', LSE = (M + log2 l' - 3) ln 2 (l' = 2^3 l).
+  const float l_tot = sum_halves(l_run);
+  const float inv = svm / l_tot;
   if (qrow < Nq) {
     uint16_t* Op = O + ((size_t)bh * Nq + qrow) * D;
 #pragma unroll
@@ -340,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(
         stg<u32x2>(Op + d0, u32x2{pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
                                   pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)});
       }
-    if (hf == 0) LSE[(size_t)bh * Nq + qrow] = (m_run - 8.f) * kLn2 + __logf(l_tot);
+    if (hf == 0) LSE[(size_t)bh * Nq + qrow] = (M + __log2f(l_tot) - kP8Shift) * kLn2;
   }
 }
 
@@ -358,7 +479,7 @@ hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v
                           float scale, bool causal, hipStream_t stream) {
   const int BH = B * Hq;
   const int nqt = (Nq + kF8Br - 1) / kF8Br;
-  dim3 grid(BH * nqt), block(256);
+  dim3 grid(BH * nqt), block(kF8Waves * 64);
   const float sl2 = scale * kLog2e;
   if (causal)
     hipLaunchKernelGGL((fwd_fp8_kernel<true>), grid, block, 0, stream, q8, k8, v8, qs, ks, vs,

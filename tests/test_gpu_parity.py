@@ -582,6 +582,34 @@ def test_fp8_forward_small(fa_gpu, causal):
     assert maxabs(to_f64(lse), rl) <= 5e-2
 
 
+@pytest.mark.parametrize("case", ["ragged_gqa", "v_scales", "rising_scores"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_forward_edge_cases(fa_gpu, case, causal):
+    """Ragged key tail with GQA; V blocks whose scales differ 50x (the fold
+    of s_v relative to the largest V scale); scores that grow along the keys,
+    so the reference max must move up many times (the rescale path)."""
+    N = 300 if case == "ragged_gqa" else 640
+    Hq, Hkv = (4, 2) if case == "ragged_gqa" else (2, 2)
+    x = gen(1, Hq, Hkv, N, N, 128, "bf16", 63)
+    if case == "v_scales":
+        f = torch.ones(N, device="cuda")
+        f[128:256] = 50.0
+        f[384:512] = 0.05
+        x["v"] = (x["v"].float() * f[None, None, :, None]).to(torch.bfloat16)
+    if case == "rising_scores":
+        ramp = torch.linspace(0.2, 3.0, N, device="cuda")
+        x["k"] = (x["k"].float() * ramp[None, None, :, None]).to(torch.bfloat16)
+        x["q"] = (x["q"].float().abs() + 0.5).to(torch.bfloat16)
+        x["k"] = x["k"].float().abs().to(torch.bfloat16)
+    say(f"fp8 forward edge case={case} causal={causal}")
+    o, lse, parts = fp8_pipeline(fa_gpu, x, None, causal)
+    torch.cuda.synchronize()
+    dq, dk, dv = dequant_inputs(parts)
+    ro, rl = A.forward(dq, dk, dv, 1 / math.sqrt(128), causal)
+    assert rel_l2(to_f64(o), ro) <= FP8_REL, rel_l2(to_f64(o), ro)
+    assert maxabs(to_f64(lse), rl) <= 5e-2
+
+
 def test_fp8_config_sampled(fa_gpu):
     """B=2 H=16 N=8192 d=128 with 0.1% outliers of magnitude 50 in Q and K,
     rotated: sampled rows of every head against the oracle on the dequantised
