@@ -267,3 +267,45 @@ def decode_paged(q, k_cache, v_cache, block_table, seqlens, scale):
             vb = gather_pages(v_cache, block_table[b], n, hk)
             o[b, h], lse[b, h] = head_forward(q[b, h], kb, vb, scale, False)
     return o, lse
+
+
+def block_sparse_allowed(Nq, Nk, q_ptr, kv_idx, block_q, block_k, causal=False):
+    """Boolean [Nq][Nk] mask of a block-sparse pattern ([CH18] §18.8.1: query
+    block i attends only to the key blocks kv_idx[q_ptr[i] .. q_ptr[i+1]-1];
+    skipped blocks contribute nothing, as if their scores were -inf).  Query
+    block i is rows i*block_q .. +block_q-1, key block j keys j*block_k ..
+    +block_k-1 (clipped at the ends); causal additionally requires j <= i."""
+    ok = np.zeros((Nq, Nk), dtype=bool)
+    for i in range(len(q_ptr) - 1):
+        r0, r1 = i * block_q, min((i + 1) * block_q, Nq)
+        for j in kv_idx[int(q_ptr[i]):int(q_ptr[i + 1])]:
+            c0, c1 = int(j) * block_k, min((int(j) + 1) * block_k, Nk)
+            ok[r0:r1, c0:c1] = True
+    if causal:
+        assert Nq == Nk
+        ok &= np.arange(Nk)[None, :] <= np.arange(Nq)[:, None]
+    return ok
+
+
+def forward_block_sparse(q, k, v, scale, q_ptr, kv_idx, block_q, block_k, causal=False):
+    """Block-sparse forward ([CH18] §18.8.1) with one pattern for every
+    (b, head).  q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] -> (O, LSE) fp64.
+    A row that sees no key gets O = 0 and LSE = -inf."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    ok = block_sparse_allowed(Nq, Nk, q_ptr, kv_idx, block_q, block_k, causal)
+    live = ok.any(axis=1)
+    o = np.zeros((B, Hq, Nq, v.shape[-1]))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head(h, Hq, Hkv)
+            s = scale * (q[b, h][live] @ k[b, hk].T)
+            s = np.where(ok[live], s, -np.inf)
+            p, m, l = softmax_rows(s)
+            o[b, h][live] = p @ v[b, hk]
+            lse[b, h][live] = m + np.log(l)
+    return o, lse

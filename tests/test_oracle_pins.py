@@ -587,3 +587,59 @@ def test_window_backward_finite_differences(causal, window):
             args_m = [xm if y is x else y for y in (q, k, v)]
             num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
         assert np.linalg.norm(num - dx) <= 1e-7 * max(1.0, np.linalg.norm(dx))
+
+
+# -------------------------------------------------------- block-sparse pins
+
+def _csr(rows):
+    ptr, idx = [0], []
+    for r in rows:
+        idx += list(r)
+        ptr.append(len(idx))
+    return ptr, idx
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_uniform_scores_and_empty_rows(causal):
+    """Closed form: Q = 0 gives each row the mean of V over its visible keys
+    (the union of its listed blocks, intersected with j <= i when causal)
+    and LSE = ln(count); a row with no listed block gets O = 0, LSE = -inf."""
+    N, d, bq, bk = 12, 3, 4, 3
+    ptr, idx = _csr([[0, 2], [], [3, 1]])       # query blocks 0, 1, 2
+    q = np.zeros((1, 1, N, d))
+    k, v = rnd(1, 1, N, d), rnd(1, 1, N, d)
+    o, lse = A.forward_block_sparse(q, k, v, 0.5, ptr, idx, bq, bk, causal)
+    vis = {0: set(range(0, 3)) | set(range(6, 9)), 1: set(), 2: set(range(9, 12)) | set(range(3, 6))}
+    for i in range(N):
+        keys = sorted(j for j in vis[i // bq] if not causal or j <= i)
+        if not keys:
+            assert np.all(o[0, 0, i] == 0) and np.isneginf(lse[0, 0, i])
+        else:
+            assert np.allclose(o[0, 0, i], v[0, 0, keys].mean(axis=0), atol=1e-13)
+            assert abs(lse[0, 0, i] - math.log(len(keys))) < 1e-13
+
+
+def test_block_sparse_brute_force_loops():
+    """Scalar loops over (i, j) with the block test written out."""
+    N, Nk, d, bq, bk, scale = 7, 10, 3, 3, 4, 0.7
+    ptr, idx = _csr([[2], [0, 1], [1, 2]])
+    q, k, v = rnd(1, 1, N, d), rnd(1, 1, Nk, d), rnd(1, 1, Nk, d)
+    o, lse = A.forward_block_sparse(q, k, v, scale, ptr, idx, bq, bk)
+    for i in range(N):
+        blocks = idx[ptr[i // bq]:ptr[i // bq + 1]]
+        w = np.array([math.exp(scale * float(q[0, 0, i] @ k[0, 0, j])) if j // bk in blocks else 0.0
+                      for j in range(Nk)])
+        assert np.allclose(o[0, 0, i], (w[:, None] * v[0, 0]).sum(0) / w.sum(), atol=1e-12)
+        assert abs(lse[0, 0, i] - math.log(w.sum())) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_all_blocks_is_dense(causal):
+    """Listing every key block reproduces the dense (or causal) forward."""
+    N, d, bq, bk = 20, 4, 8, 6
+    q, k, v = rnd(2, 2, N, d), rnd(2, 2, N, d), rnd(2, 2, N, d)
+    nb = -(-N // bk)
+    ptr, idx = _csr([list(range(nb))] * (-(-N // bq)))
+    o, lse = A.forward_block_sparse(q, k, v, 0.4, ptr, idx, bq, bk, causal)
+    od, ld = A.forward(q, k, v, 0.4, causal)
+    assert np.allclose(o, od, atol=1e-14) and np.allclose(lse, ld, atol=1e-14)
