@@ -301,6 +301,31 @@ def main(argv=None):
         log(f"window fwd {tfw:.3f} ms, bwd {tbw:.3f} ms")
         del xw, ow, lw, dqw, dkw, dvw, wsw
 
+    if not only or "sparse" in only:
+        from workloads import SPARSE
+        wsp = SPARSE["sparse_bf16"]
+        log("block-sparse inputs")
+        xs = make_inputs(wsp, device="cuda")
+        ptr, idx = wsp.pattern()
+        pd = torch.tensor(ptr, dtype=torch.int32, device="cuda")
+        idd = torch.tensor(idx, dtype=torch.int32, device="cuda")
+        mb = max(ptr[i + 1] - ptr[i] for i in range(len(ptr) - 1))
+        osp = torch.empty_like(xs["q"])
+        lsp = torch.empty(wsp.B, wsp.Hq, wsp.Nq, dtype=torch.float32, device="cuda")
+
+        def spf():
+            fa.fa_fwd_block_sparse(xs["q"], xs["k"], xs["v"], osp, lsp, wsp.B, wsp.Hq, wsp.Hkv,
+                                   wsp.Nq, wsp.Nk, wsp.d, wsp.scale, wsp.causal, pd, idd, mb, sh)
+
+        spf()
+        t = timed(spf, iters, stream)
+        tf = wsp.fwd_flops() / (t * 1e-3) / 1e12
+        parts["fwd_block_sparse"] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                                     "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                     "density": round(wsp.visible_pairs() / (wsp.Nq * wsp.Nk), 4)}
+        log(f"block-sparse fwd {t:.3f} ms {tf:.0f} TF")
+        del xs, osp, lsp
+
     if not only or "decode_paged" in only:
         from workloads import PAGED, make_paged_inputs
         wg = PAGED["decode_paged"]

@@ -49,6 +49,8 @@ _SIGS = {
     "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                            _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_fwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I,
+                                 _P]),
     "fa_decode_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "fa_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -203,6 +205,13 @@ def fa_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
           int(causal), window_left, window_right, _stream(stream))
 
 
+def fa_fwd_block_sparse(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, q_tile_ptr,
+                        kv_block_idx, max_blocks_per_tile, stream=None):
+    _call("fa_fwd_block_sparse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk,
+          d, scale, int(causal), _ptr(q_tile_ptr), _ptr(kv_block_idx), max_blocks_per_tile,
+          _stream(stream))
+
+
 def fa_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream=None):
     _call("fa_decode_combine", _ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, d,
           num_splits, _stream(stream))
@@ -310,6 +319,29 @@ def forward_varlen(q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, causal=False
     lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, cu_q.shape[0] - 1, Hq, Hkv, total_q, total_k,
                   int(max_seqlen_q), int(max_seqlen_k), d, s, causal, stream)
+    return o, lse
+
+
+SPARSE_BLOCK_Q = 256   # query rows per block of a block-sparse pattern
+SPARSE_BLOCK_K = 64    # keys per block
+
+
+def forward_block_sparse(q, k, v, q_tile_ptr, kv_block_idx, causal=False, scale=None,
+                         max_blocks_per_tile=None, stream=None):
+    """Block-sparse forward: q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] (bf16), one
+    CSR pattern for every (b, head): query tile t (SPARSE_BLOCK_Q rows) sees
+    the key blocks (SPARSE_BLOCK_K keys) kv_block_idx[q_tile_ptr[t] ..
+    q_tile_ptr[t+1]-1] (int32 device tensors) -> (O, LSE)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    s = _default_scale(d, scale)
+    if max_blocks_per_tile is None:
+        max_blocks_per_tile = int((q_tile_ptr[1:] - q_tile_ptr[:-1]).max().item())
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_block_sparse(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, s, causal, q_tile_ptr,
+                        kv_block_idx, max_blocks_per_tile, stream)
     return o, lse
 
 

@@ -74,6 +74,25 @@ fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, fl
                                         causal != 0, stream, window_left, window_right));
 }
 
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                              int causal, const int* q_tile_ptr, const int* kv_block_idx,
+                              int max_blocks_per_tile, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      q_tile_ptr == nullptr || kv_block_idx == nullptr ||
+      (reinterpret_cast<uintptr_t>(q_tile_ptr) & 3u) ||
+      (reinterpret_cast<uintptr_t>(kv_block_idx) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (max_blocks_per_tile < 0) return FA_ERR_INVALID_ARG;
+  if (max_blocks_per_tile > 256) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_fwd_bf16_sparse(q, k, v, o, lse, q_tile_ptr, kv_block_idx, B, Hq,
+                                               Hkv, Nq, Nk, d, scale, causal != 0, stream));
+}
+
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int Hq,
                         int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,

@@ -66,13 +66,19 @@ __device__ __forceinline__ int fwd_swz_v(int r) {
 // visible to query i only if i - win_l <= j <= i + win_r (a negative bound is
 // unbounded); only the key tiles that intersect some row's window are
 // visited.
-template <int D, bool CAUSAL, int NW, int NS, bool VARLEN = false, bool WIN = false>
+// SPARSE: block-sparse pattern ([CH18] §18.8.1): query tile t (BR rows)
+// visits only the 64-key tiles sp_idx[sp_ptr[t] .. sp_ptr[t+1]-1] (at most
+// 256 of them), the same list for every (b, head).  A row that sees no key
+// gets O = 0 and LSE = -inf.
+template <int D, bool CAUSAL, int NW, int NS, bool VARLEN = false, bool WIN = false,
+          bool SPARSE = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale, float scale_log2, int BH, int nqt,
     const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
-    int total_q = 0, int win_l = -1, int win_r = -1) {
+    int total_q = 0, int win_l = -1, int win_r = -1, const int* __restrict__ sp_ptr = nullptr,
+    const int* __restrict__ sp_idx = nullptr) {
   constexpr int BC = kFwdBc;
   constexpr int ROWB = D * 2;               // bytes per K/V row in LDS (no padding)
   constexpr int NCH = D / 8;                // 16-byte chunks per row
@@ -159,7 +165,37 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     if (win_r >= 0) kv_end = min(kv_end, q0 + BR + win_r);
     if (win_l >= 0) jf = max(0, q0 - win_l) / BC;
   }
-  const int ntiles = (kv_end + BC - 1) / BC - jf;
+  int ntiles = (kv_end + BC - 1) / BC - jf;
+  // The sparse list of this query tile, one entry per lane and register
+  // (list position p in register p/64, lane p%64), read back with readlane.
+  int spc[4] = {0, 0, 0, 0};
+  if constexpr (SPARSE) {
+    const int lo = sp_ptr[qt];
+    ntiles = min(max(sp_ptr[qt + 1] - lo, 0), 256);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r * 64 + lane < ntiles) spc[r] = sp_idx[lo + r * 64 + lane];
+    if (ntiles == 0) {  // nothing visible: O = 0, LSE = -inf
+      if (qrow < Nq) {
+        uint16_t* Op = O + q_base + (size_t)qrow * SQ;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) stg<u32x2>(Op + db * 32 + g * 8 + hf * 4, u32x2{0u, 0u});
+        if (hf == 0) LSE[lse_base + qrow] = -INFINITY;
+      }
+      return;
+    }
+  }
+  // Key tile (of BC keys) visited at loop position j.
+  auto tile_of = [&](int j) -> int {
+    if constexpr (SPARSE) {
+      const int v = j < 64 ? spc[0] : j < 128 ? spc[1] : j < 192 ? spc[2] : spc[3];
+      return __builtin_amdgcn_readlane(v, j & 63);
+    } else {
+      return jf + j;
+    }
+  };
 
   // Per-lane source offsets of this wave's direct loads (same for every tile):
   // LDS block (wave*LPW + i) of a tile holds rows r, lane -> position p.
@@ -175,13 +211,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     char* d = kslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i)
-      buffer_load_lds16(rK, d + i * 1024, koff[i], (jf + j) * BC * SKVB);
+      buffer_load_lds16(rK, d + i * 1024, koff[i], tile_of(j) * BC * SKVB);
   };
   auto issue_v = [&](int j, int slot) {
     char* d = vslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i)
-      buffer_load_lds16(rV, d + i * 1024, voff[i], (jf + j) * BC * SKVB);
+      buffer_load_lds16(rV, d + i * 1024, voff[i], tile_of(j) * BC * SKVB);
   };
 
   // Per-lane LDS read offsets.  K (A operand, row kb*32 + l32, chunk 2*kk + hf):
@@ -233,12 +269,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   // Mask one S^T tile: keys past the end (ragged tail) and, on tiles crossing
   // the diagonal, keys after the query ([CH18] §18.5.2).
   auto mask = [&](int j, f32x16* s) {
-    const int kv0 = (jf + j) * BC;
+    const int kv0 = tile_of(j) * BC;
     const int rw0 = q0 + wave * 32;  // this wave's first row
     bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > rw0);
     if constexpr (WIN)
       need_mask = need_mask || (win_l >= 0 && kv0 < rw0 + 31 - win_l) ||
                   (win_r >= 0 && kv0 + BC - 1 > rw0 + win_r);
+    if constexpr (SPARSE) need_mask = need_mask || kv0 < 0;  // a bad list entry
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -248,6 +285,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
           bool out = key >= Nk || (CAUSAL && key > qrow);
           if constexpr (WIN)
             out = out || (win_l >= 0 && key < qrow - win_l) || (win_r >= 0 && key > qrow + win_r);
+          if constexpr (SPARSE) out = out || key < 0;
           if (out) s[kb][r] = -INFINITY;
         }
     }
@@ -436,9 +474,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
   if ((ntiles - 1) & 1) pv_last(IntConst<1>{});
   else pv_last(IntConst<0>{});
 
-  // Epilogue: O = O^T / l, LSE = (M + log2 l) ln 2.
+  // Epilogue: O = O^T / l, LSE = (M + log2 l) ln 2 (a row that saw no key,
+  // possible with a block-sparse list: O = 0, LSE = -inf).
   const float l_tot = sum_halves(l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < Nq) {
     uint16_t* Op = O + q_base + (size_t)qrow * SQ;
 #pragma unroll
@@ -449,7 +488,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
         stg<u32x2>(Op + d0, u32x2{pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
                                   pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)});
       }
-    if (hf == 0) LSE[lse_base + qrow] = (M + __log2f(l_tot)) * kLn2;
+    if (hf == 0) LSE[lse_base + qrow] = l_tot > 0.f ? (M + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -556,6 +595,34 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     }
   }
 #undef FA_LAUNCH_FWD
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int* sp_ptr, const int* sp_idx, int B,
+                                  int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal,
+                                  hipStream_t stream) {
+  constexpr int NW = kFwdWaves, NS = kFwdStages;
+  const int BH = B * Hq;
+  const int nqt = (Nq + kFwdBr - 1) / kFwdBr;
+  dim3 grid(BH * nqt), block(NW * 64);
+  const float sl2 = scale * kLog2e;
+  auto Qp = (const uint16_t*)q;
+  auto Kp = (const uint16_t*)k;
+  auto Vp = (const uint16_t*)v;
+  auto Op = (uint16_t*)o;
+#define FA_LAUNCH_SPARSE(DD, CC)                                                                \
+  hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC, NW, NS, false, false, true>), grid, block, 0,     \
+                     stream, Qp, Kp, Vp, Op, lse, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, nullptr, \
+                     nullptr, 0, -1, -1, sp_ptr, sp_idx)
+  if (d == 128) {
+    if (causal) FA_LAUNCH_SPARSE(128, true);
+    else FA_LAUNCH_SPARSE(128, false);
+  } else {
+    if (causal) FA_LAUNCH_SPARSE(64, true);
+    else FA_LAUNCH_SPARSE(64, false);
+  }
+#undef FA_LAUNCH_SPARSE
   return hipGetLastError();
 }
 

@@ -12,6 +12,10 @@ namespace fa {
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                            bool causal, hipStream_t stream, int win_l = -1, int win_r = -1);
+hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int* sp_ptr, const int* sp_idx, int B,
+                                  int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal,
+                                  hipStream_t stream);
 hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o,
                                   float* lse, const int* cu_q, const int* cu_k, int batch,
                                   int Hq, int Hkv, int total_q, int max_seqlen_q, int d,

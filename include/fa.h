@@ -90,6 +90,29 @@ fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, fl
                         hipStream_t stream);
 
 /*
+ * Block-sparse forward, bf16 ([CH18] §18.8.1: query block i attends only to
+ * the key blocks in its list; skipped blocks contribute nothing).  Same
+ * tensors and meaning as fa_fwd, plus one pattern shared by every (b, head):
+ *   query tile t is rows t*FA_SPARSE_BLOCK_Q .. +FA_SPARSE_BLOCK_Q-1, key
+ *   block c is keys c*FA_SPARSE_BLOCK_K .. +FA_SPARSE_BLOCK_K-1;
+ *   q_tile_ptr: device int32 [ceil(Nq/FA_SPARSE_BLOCK_Q) + 1], CSR row
+ *   offsets; kv_block_idx: device int32, the listed key blocks of each query
+ *   tile (distinct within a tile; any order, ascending is fastest).
+ *   max_blocks_per_tile: the longest list (<= 256; FA_ERR_UNSUPPORTED above).
+ * causal additionally masks j > i (requires Nq == Nk).  A row that sees no
+ * key gets O = 0 and LSE = -inf.  The lists are device data and are not
+ * checked on the host; a block index outside [0, ceil(Nk/64)) reads zeros
+ * and is masked, and a tile's list is cut at 256 entries.  d in {64, 128}.
+ */
+#define FA_SPARSE_BLOCK_Q 256
+#define FA_SPARSE_BLOCK_K 64
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                              float scale, int causal, const int* q_tile_ptr,
+                              const int* kv_block_idx, int max_blocks_per_tile,
+                              hipStream_t stream);
+
+/*
  * Forward over a packed variable-length batch, bf16 ([CH18] §18.7.1: the
  * sequences are concatenated along the token axis and cumulative offsets
  * give each one's rows; attention never crosses a sequence boundary and the

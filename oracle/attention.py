@@ -287,23 +287,26 @@ def block_sparse_allowed(Nq, Nk, q_ptr, kv_idx, block_q, block_k, causal=False):
     return ok
 
 
-def forward_block_sparse(q, k, v, scale, q_ptr, kv_idx, block_q, block_k, causal=False):
+def forward_block_sparse(q, k, v, scale, q_ptr, kv_idx, block_q, block_k, causal=False,
+                         rows=None):
     """Block-sparse forward ([CH18] §18.8.1) with one pattern for every
-    (b, head).  q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] -> (O, LSE) fp64.
-    A row that sees no key gets O = 0 and LSE = -inf."""
+    (b, head).  q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] -> (O, LSE) fp64 for
+    the query rows ``rows`` (all by default).  A row that sees no key gets
+    O = 0 and LSE = -inf."""
     q = _f64(q)
     k = _f64(k)
     v = _f64(v)
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
-    ok = block_sparse_allowed(Nq, Nk, q_ptr, kv_idx, block_q, block_k, causal)
+    r = np.arange(Nq) if rows is None else np.asarray(rows)
+    ok = block_sparse_allowed(Nq, Nk, q_ptr, kv_idx, block_q, block_k, causal)[r]
     live = ok.any(axis=1)
-    o = np.zeros((B, Hq, Nq, v.shape[-1]))
-    lse = np.full((B, Hq, Nq), -np.inf)
+    o = np.zeros((B, Hq, len(r), v.shape[-1]))
+    lse = np.full((B, Hq, len(r)), -np.inf)
     for b in range(B):
         for h in range(Hq):
             hk = kv_head(h, Hq, Hkv)
-            s = scale * (q[b, h][live] @ k[b, hk].T)
+            s = scale * (q[b, h][r[live]] @ k[b, hk].T)
             s = np.where(ok[live], s, -np.inf)
             p, m, l = softmax_rows(s)
             o[b, h][live] = p @ v[b, hk]

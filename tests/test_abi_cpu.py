@@ -217,3 +217,17 @@ def test_paged_decode_validation(lib):
     assert call(Hq=7) == fa.FA_ERR_INVALID_ARG
     assert call(d=256) == fa.FA_ERR_UNSUPPORTED
     assert call(Hq=128, Hkv=2) == fa.FA_ERR_UNSUPPORTED  # group of 64 > 32
+
+
+def test_block_sparse_validation(lib):
+    """fa_fwd_block_sparse: list pointers, the per-tile list bound (256),
+    causal shapes, head dims."""
+    def call(ptr=FAKE, idx=FAKE, mb=8, causal=0, Nq=512, Nk=512, d=128):
+        return lib.fa_fwd_block_sparse(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, Nq, Nk, d, 0.1,
+                                       causal, ptr, idx, mb, None)
+    assert call(ptr=None) == fa.FA_ERR_INVALID_ARG
+    assert call(idx=FAKE + 1) == fa.FA_ERR_INVALID_ARG
+    assert call(mb=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(mb=257) == fa.FA_ERR_UNSUPPORTED
+    assert call(causal=1, Nk=640) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED

@@ -241,6 +241,86 @@ def test_window_config_sampled(fa_gpu):
             assert e <= BF16_GRAD, (b, h, name, e)
 
 
+# ------------------------------------------------------------- block-sparse
+
+def random_pattern(nq, nk, seed, p=0.4):
+    """Random CSR lists (shuffled, some empty) over nq query tiles, nk key blocks."""
+    rs = np.random.default_rng(seed)
+    ptr, idx = [0], []
+    for t in range(nq):
+        blocks = [c for c in range(nk) if rs.random() < p] if t % 3 != 1 else []
+        rs.shuffle(blocks)
+        idx += blocks
+        ptr.append(len(idx))
+    return ptr, idx
+
+
+@pytest.mark.parametrize("shape,causal", [((1, 4, 2, 700, 700, 128), False),
+                                          ((1, 4, 2, 700, 700, 128), True),
+                                          ((2, 2, 1, 513, 600, 64), False),
+                                          ((1, 2, 2, 1100, 1100, 128), True)])
+def test_block_sparse_small(fa_gpu, shape, causal):
+    """Random shuffled lists with empty query tiles (their rows: O = 0,
+    LSE = -inf) and ragged ends, against the oracle."""
+    B, Hq, Hkv, Nq, Nk, d = shape
+    x = gen(B, Hq, Hkv, Nq, Nk, d, "bf16", 101)
+    nq, nk = -(-Nq // fa_gpu.SPARSE_BLOCK_Q), -(-Nk // fa_gpu.SPARSE_BLOCK_K)
+    ptr, idx = random_pattern(nq, nk, 7 + Nq)
+    say(f"block-sparse fwd shape={shape} causal={causal} nnz={len(idx)}")
+    pd = torch.tensor(ptr, dtype=torch.int32, device="cuda")
+    idd = torch.tensor(idx if idx else [0], dtype=torch.int32, device="cuda")
+    o, lse = fa_gpu.forward_block_sparse(x["q"], x["k"], x["v"], pd, idd, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = A.forward_block_sparse(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]),
+                                    1 / math.sqrt(d), ptr, idx, fa_gpu.SPARSE_BLOCK_Q,
+                                    fa_gpu.SPARSE_BLOCK_K, causal)
+    got_o, got_l = to_f64(o), to_f64(lse)
+    dead = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(got_l), dead)
+    assert not np.any(got_o[dead])
+    assert maxabs(got_o, ro) <= BF16_O
+    assert maxabs(got_l[~dead], rl[~dead]) <= BF16_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_all_blocks_equals_dense(fa_gpu, causal):
+    """Every key block listed in ascending order: the same tiles in the same
+    order as the dense kernel, so outputs agree bit for bit."""
+    N = 1000
+    x = gen(2, 4, 2, N, N, 128, "bf16", 102)
+    nq, nk = -(-N // fa_gpu.SPARSE_BLOCK_Q), -(-N // fa_gpu.SPARSE_BLOCK_K)
+    ptr = [t * nk for t in range(nq + 1)]
+    idx = list(range(nk)) * nq
+    say(f"block-sparse all blocks causal={causal}")
+    o, lse = fa_gpu.forward_block_sparse(x["q"], x["k"], x["v"],
+                                         torch.tensor(ptr, dtype=torch.int32, device="cuda"),
+                                         torch.tensor(idx, dtype=torch.int32, device="cuda"),
+                                         causal=causal)
+    od, ld = fa_gpu.forward(x["q"], x["k"], x["v"], causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, od) and torch.equal(lse, ld)
+
+
+def test_block_sparse_config_sampled(fa_gpu):
+    """B=2 H=16 N=8192 d=128 with the local (+-1024 keys) + global (first 256
+    keys) pattern, in the benchmark's launch configuration: sampled rows of
+    every head against the oracle."""
+    from workloads import SPARSE
+    w = SPARSE["sparse_bf16"]
+    x = {n: t.cuda() for n, t in make_inputs(w).items()}
+    ptr, idx = w.pattern()
+    say("block-sparse full size")
+    o, lse = fa_gpu.forward_block_sparse(x["q"], x["k"], x["v"],
+                                         torch.tensor(ptr, dtype=torch.int32, device="cuda"),
+                                         torch.tensor(idx, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    rows = np.array([0, 255, 256, 1500, 4095, 4096, 6000, 8191])
+    ro, rl = A.forward_block_sparse(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), w.scale, ptr,
+                                    idx, w.block_q, w.block_k, False, rows=rows)
+    assert maxabs(to_f64(o)[:, :, rows], ro) <= BF16_O
+    assert maxabs(to_f64(lse)[:, :, rows], rl) <= BF16_LSE
+
+
 # ------------------------------------------------------------------- decode
 
 def check_decode(fa, B, Hq, Hkv, Nk, d, splits, seed):

@@ -257,3 +257,48 @@ WINDOWED = {
     "window_bf16": Windowed("window_bf16", 2, 16, 16, 8192, 8192, 128, "bf16", causal=True,
                             backward=True, seed=8308, window_left=4096, window_right=0),
 }
+
+
+# ----------------------------------------------------------- block-sparse
+
+@dataclass(frozen=True)
+class BlockSparse(Workload):
+    """A Workload with a block-sparse pattern shared by every (b, head):
+    query tile t (block_q rows) sees the key blocks (block_k keys) within
+    `local` keys of the tile on either side, plus the first `global_blocks`
+    key blocks (a local + global pattern)."""
+    block_q: int = 256
+    block_k: int = 64
+    local: int = 1024
+    global_blocks: int = 4
+
+    def pattern(self):
+        nq = -(-self.Nq // self.block_q)
+        nk = -(-self.Nk // self.block_k)
+        ptr, idx = [0], []
+        for t in range(nq):
+            lo = max(0, (t * self.block_q - self.local) // self.block_k)
+            hi = min(nk, -(-((t + 1) * self.block_q + self.local) // self.block_k))
+            blocks = sorted(set(range(min(self.global_blocks, nk))) | set(range(lo, hi)))
+            idx += blocks
+            ptr.append(len(idx))
+        return ptr, idx
+
+    def visible_pairs(self) -> int:
+        ptr, idx = self.pattern()
+        tot = 0
+        for t in range(len(ptr) - 1):
+            rows = min(self.block_q, self.Nq - t * self.block_q)
+            for c in idx[ptr[t]:ptr[t + 1]]:
+                cols = min(self.block_k, self.Nk - c * self.block_k)
+                tot += rows * cols
+        return tot
+
+    def fwd_flops(self) -> float:
+        return 4.0 * self.B * self.Hq * self.d * self.visible_pairs()
+
+
+SPARSE = {
+    "sparse_bf16": BlockSparse("sparse_bf16", 2, 16, 16, 8192, 8192, 128, "bf16", causal=False,
+                               seed=8309),
+}
