@@ -166,6 +166,24 @@ def test_causal_config_sampled(fa_gpu):
             assert e <= BF16_GRAD, (b, h, name, e)
 
 
+def test_backward_is_deterministic(fa_gpu):
+    """No atomics and a fixed accumulation order: repeated backward passes
+    (plain and windowed, GQA, causal) give bit-identical gradients."""
+    x = gen(2, 8, 2, 1500, 1500, 128, "bf16", 93, grad=True)
+    say("backward determinism")
+    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=True)
+    runs = [fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=True)
+            for _ in range(3)]
+    ow, lw = fa_gpu.forward(x["q"], x["k"], x["v"], causal=True, window=(300, 0))
+    runs_w = [fa_gpu.backward(x["q"], x["k"], x["v"], ow, lw, x["do"], causal=True,
+                              window=(300, 0)) for _ in range(3)]
+    torch.cuda.synchronize()
+    for rr in (runs, runs_w):
+        for r in rr[1:]:
+            for a, b in zip(r, rr[0]):
+                assert torch.equal(a, b)
+
+
 # ----------------------------------------------------------- sliding window
 
 WINDOWS = [(37, 5), (0, 0), (200, -1), (-1, 100), (300, 300), (1000, 0), (64, 63)]
