@@ -274,6 +274,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
     return i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
   };
 
+  const float lsvm = __log2f(svm);
   // Per-tile coefficients: c_j multiplies the raw fp8 product (log2 units),
   // e_j = log2(s_v / s_vmax) is added to the exp argument, r_j = s_vmax / s_v
   // converts the tile's sum of p' back to p.
@@ -282,8 +283,8 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
     const float sk = KS[(size_t)bhk * nkb + blk];
     const float sv = VS[(size_t)bhk * nkb + blk];
     *c = sq * sk * scale_log2;
-    *e = sv > 0.f ? __log2f(sv / svm) : 0.f;
-    *r = sv > 0.f ? svm / sv : 0.f;
+    *e = __log2f(sv) - lsvm;  // scales are positive (the quantizer writes 1 for a zero block)
+    *r = fast_exp2(-*e);
   };
 
   auto qk = [&](int j, f32x16* s) {

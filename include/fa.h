@@ -300,6 +300,10 @@ fa_status fa_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float
  * fp32; P is rounded to e4m3 for the P V product; O is bf16, lse fp32.
  *   q8 [B][Hq][Nq][d], k8,v8 [B][Hkv][Nk][d]; q_scale [B][Hq][ceil(Nq/128)],
  *   k_scale, v_scale [B][Hkv][ceil(Nk/128)].  d == 128.
+ * Every scale must be positive and finite, as fa_quantize_fp8 writes them
+ * (1 for an all-zero block): the kernel folds each V block's scale into the
+ * exponent as log2(s_v / max s_v), so a zero or negative scale gives
+ * undefined output.  Scales live in device memory and are not checked.
  */
 fa_status fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                      const float* q_scale, const float* k_scale, const float* v_scale,

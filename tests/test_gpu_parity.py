@@ -680,13 +680,16 @@ def test_fp8_forward_small(fa_gpu, causal):
     assert maxabs(to_f64(lse), rl) <= 5e-2
 
 
-@pytest.mark.parametrize("case", ["ragged_gqa", "v_scales", "rising_scores"])
+@pytest.mark.parametrize("case", ["ragged_gqa", "v_scales", "rising_scores", "tiles_1", "tiles_3",
+                                  "tiles_7"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_forward_edge_cases(fa_gpu, case, causal):
     """Ragged key tail with GQA; V blocks whose scales differ 50x (the fold
     of s_v relative to the largest V scale); scores that grow along the keys,
-    so the reference max must move up many times (the rescale path)."""
-    N = 300 if case == "ragged_gqa" else 640
+    so the reference max must move up many times (the rescale path); key
+    counts of 1, 3 and 7 tiles of 64 (every remainder of the four-slot load
+    rotation, and units shorter than one round of it)."""
+    N = {"ragged_gqa": 300, "tiles_1": 40, "tiles_3": 190, "tiles_7": 448}.get(case, 640)
     Hq, Hkv = (4, 2) if case == "ragged_gqa" else (2, 2)
     x = gen(1, Hq, Hkv, N, N, 128, "bf16", 63)
     if case == "v_scales":
