@@ -235,6 +235,32 @@ def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False):
     return o, lse
 
 
+def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False):
+    """Gradients of forward_varlen: each sequence's backward on its own rows
+    ([CH18] §18.4.4 per sequence; the packing couples nothing), -> (dQ, dK,
+    dV) fp64 in the packed token-major layouts of q, k, v.  Rows of a sequence
+    with no keys get dQ = 0; keys of a sequence with no queries dK = dV = 0."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    do = _f64(do)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if q1 == q0 or k1 == k0:
+            continue
+        per_seq = [x.transpose(1, 0, 2)[None] for x in (q[q0:q1], k[k0:k1], v[k0:k1], do[q0:q1])]
+        a, bk, bv = backward(*per_seq, scale, causal)
+        dq[q0:q1] = a[0].transpose(1, 0, 2)
+        dk[k0:k1] = bk[0].transpose(1, 0, 2)
+        dv[k0:k1] = bv[0].transpose(1, 0, 2)
+    return dq, dk, dv
+
+
 def gather_pages(cache, block_table, seqlen, hk):
     """Logical rows 0 .. seqlen-1 of one KV head from a paged cache
     ([CH18] §18.8.2 (3), §18.8.3 (1): the KV cache lives in fixed-size

@@ -476,6 +476,42 @@ def test_varlen_sequences_are_isolated():
     assert not np.allclose(o1[cu[1]:cu[2]], o2[cu[1]:cu[2]])
 
 
+@pytest.mark.parametrize("causal,lens_q,lens_k", [
+    (True, [4, 2, 5], [4, 2, 5]),
+    (False, [3, 2, 0, 4], [2, 0, 3, 5]),   # queries without keys, keys without queries
+])
+def test_varlen_backward_finite_differences(causal, lens_q, lens_k):
+    """Central differences of L = sum(O * G) over the packed forward match
+    backward_varlen (GQA), including the zero gradients of rows with no
+    visible key and of keys that no query sees."""
+    cq, ck = _pack_lengths(lens_q), _pack_lengths(lens_k)
+    Hq, Hkv, d, scale, h = 2, 1, 3, 0.6, 1e-6
+    q, k, v = rnd(cq[-1], Hq, d), rnd(ck[-1], Hkv, d), rnd(ck[-1], Hkv, d)
+    g = rnd(cq[-1], Hq, d)
+    dq, dk, dv = A.backward_varlen(q, k, v, g, cq, ck, scale, causal)
+
+    def loss(q_, k_, v_):
+        return float((A.forward_varlen(q_, k_, v_, cq, ck, scale, causal)[0] * g).sum())
+
+    for x, dx in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.linalg.norm(num - dx) <= 1e-7 * max(1.0, np.linalg.norm(dx))
+    for b in range(len(lens_q)):
+        if lens_k[b] == 0:
+            assert not dq[cq[b]:cq[b + 1]].any()
+        if lens_q[b] == 0:
+            assert not dk[ck[b]:ck[b + 1]].any() and not dv[ck[b]:ck[b + 1]].any()
+
+
 # ------------------------------------------------------------ paged KV pins
 
 def test_paged_gather_reproduces_scattered_rows():
