@@ -377,7 +377,22 @@ def main(argv=None):
                                "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                                "sequences": len(wv.seqlens), "tokens": wv.total}
         log(f"varlen fwd {t:.3f} ms {tf:.0f} TF")
-        del xv, ov, lv
+        dqv, dkv, dvv = (torch.empty_like(xv[n]) for n in ("q", "k", "v"))
+        wsv_bytes = fa.fa_bwd_workspace_size(1, wv.Hq, wv.total, wv.d)
+        wsv = torch.empty(wsv_bytes, dtype=torch.uint8, device="cuda")
+
+        def vbwd():
+            fa.fa_bwd_varlen(xv["q"], xv["k"], xv["v"], ov, xv["do"], lv, dqv, dkv, dvv, wsv,
+                             wsv_bytes, xv["cu"], xv["cu"], len(wv.seqlens), wv.Hq, wv.Hkv,
+                             wv.total, wv.total, mx, mx, wv.d, wv.scale, wv.causal, sh)
+
+        vbwd()
+        tb = timed(vbwd, iters, stream)
+        tfb = wv.bwd_flops() / (tb * 1e-3) / 1e12
+        parts["fwd_varlen"].update({"bwd_ms": round(tb, 4), "bwd_tflops": round(tfb, 1),
+                                    "bwd_frac_peak": round(tfb / PEAK_BF16_TFLOPS, 4)})
+        log(f"varlen bwd {tb:.3f} ms {tfb:.0f} TF")
+        del xv, ov, lv, dqv, dkv, dvv, wsv
 
     if not only or "fp8" in only:
         wf = WORKLOADS["fp8_fwd"]

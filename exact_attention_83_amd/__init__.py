@@ -46,6 +46,8 @@ _SIGS = {
                                      _I, _F, _I, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                            _P]),
+    "fa_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P,
+                           _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                            _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
@@ -192,6 +194,15 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, Hq, Hkv, total_q, total_k,
           _stream(stream))
 
 
+def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, cu_q, cu_k,
+                  batch, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, scale, causal,
+                  stream=None):
+    _call("fa_bwd_varlen", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+          _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, _ptr(cu_q), _ptr(cu_k), batch, Hq,
+          Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, scale, int(causal),
+          _stream(stream))
+
+
 def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, window_left,
                   window_right, stream=None):
     _call("fa_fwd_window", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
@@ -320,6 +331,24 @@ def forward_varlen(q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, causal=False
     fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, cu_q.shape[0] - 1, Hq, Hkv, total_q, total_k,
                   int(max_seqlen_q), int(max_seqlen_k), d, s, causal, stream)
     return o, lse
+
+
+def backward_varlen(q, k, v, o, lse, dout, cu_q, cu_k, max_seqlen_q, max_seqlen_k, causal=False,
+                    scale=None, workspace=None, stream=None):
+    """dQ, dK, dV of forward_varlen (packed token-major layouts as there)."""
+    import torch
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    s = _default_scale(d, scale)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws_bytes = fa_bwd_workspace_size(1, Hq, total_q, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, ws, ws.numel() * ws.element_size(), cu_q,
+                  cu_k, cu_q.shape[0] - 1, Hq, Hkv, total_q, total_k, int(max_seqlen_q),
+                  int(max_seqlen_k), d, s, causal, stream)
+    return dq, dk, dv
 
 
 SPARSE_BLOCK_Q = 256   # query rows per block of a block-sparse pattern

@@ -191,6 +191,46 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
   return hip_status(e);
 }
 
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, const int* cu_seqlens_q,
+                        const int* cu_seqlens_k, int batch, int Hq, int Hkv, int total_q,
+                        int total_k, int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                        int causal, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (batch <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || total_q <= 0 || total_k <= 0 ||
+      max_seqlen_q <= 0 || max_seqlen_k <= 0 || max_seqlen_q > total_q ||
+      max_seqlen_k > total_k || d <= 0)
+    return FA_ERR_INVALID_ARG;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: every row of the packs must be addressable.
+  if ((int64_t)total_k * Hkv * d * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)total_q * Hq * d * 2 >= ((int64_t)1 << 31))
+    return FA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * Hq * ((max_seqlen_q + 255) / 256) >= ((int64_t)1 << 31) ||
+      (int64_t)batch * Hkv * ((max_seqlen_k + 255) / 256) >= ((int64_t)1 << 31))
+    return FA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < fa_bwd_workspace_size(1, Hq, total_q, d)) return FA_ERR_WORKSPACE;
+  float* delta = static_cast<float*>(workspace);
+  hipError_t e = fa::launch_bwd_pre(o, dout, delta, 1, 1, total_q * Hq, d, stream, Hq);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dkdv_varlen(q, k, v, dout, lse, delta, dk, dv, cu_seqlens_q,
+                                   cu_seqlens_k, batch, Hq, Hkv, total_q, max_seqlen_k, d,
+                                   scale, causal != 0, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dq_varlen(q, k, v, dout, lse, delta, dq, cu_seqlens_q, cu_seqlens_k,
+                                 batch, Hq, Hkv, total_q, max_seqlen_q, d, scale, causal != 0,
+                                 stream);
+  return hip_status(e);
+}
+
 fa_status fa_bwd_pre(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Nq, int d, hipStream_t stream) {
   if (!aligned16(o) || !aligned16(dout)) return FA_ERR_INVALID_ARG;

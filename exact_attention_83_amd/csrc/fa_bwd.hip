@@ -21,10 +21,14 @@ namespace fa {
 
 // ---------------------------------------------------------------------------
 // delta_i = sum_c dO_ic * O_ic.
+// Rows are (token, head) pairs in memory order; with heads > 1 (packed
+// token-major input, row = token * heads + head) delta is written head-major,
+// delta[head][token], the layout of the forward's LSE.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ O,
                                                         const T* __restrict__ dO,
-                                                        float* __restrict__ delta, int rows) {
+                                                        float* __restrict__ delta, int rows,
+                                                        int heads) {
   // 16 threads per row, each owns D/16 consecutive elements.
   constexpr int E = D / 16;
   const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ O,
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < rows && sub == 0) delta[row] = acc;
+  if (row < rows && sub == 0) delta[(size_t)(row % heads) * (rows / heads) + row / heads] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -214,10 +218,11 @@ __device__ __forceinline__ int tr_offset(int lane, int rb, int c0) {
 // ROWB-byte rows, for this lane: LDS position p of row r receives source
 // chunk p ^ swz(r).
 template <int ROWB>
-__device__ __forceinline__ int swz_src_offset(int lane, int blk) {
+__device__ __forceinline__ int swz_src_offset(int lane, int blk, int stride = ROWB) {
+  // stride: bytes between consecutive source rows (ROWB when rows are dense)
   const int r = blk * (1024 / ROWB) + lane / (ROWB / 16);
   const int p = lane % (ROWB / 16);
-  return r * ROWB + ((p ^ bwd_swz<ROWB>(r)) << 4);
+  return r * stride + ((p ^ bwd_swz<ROWB>(r)) << 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -236,13 +241,15 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk) {
 // WIN: sliding window (key j visible to query i iff i - win_l <= j <= i +
 // win_r; negative = unbounded): only the query tiles whose windows reach this
 // work unit's keys are visited.
-template <int D, bool CAUSAL, bool WIN = false>
+template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false>
 __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk,
-    float scale, float scale_log2, int BHkv, int win_l = -1, int win_r = -1) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq_arg,
+    int Nk_arg, float scale, float scale_log2, int BHkv, int win_l = -1, int win_r = -1,
+    const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
+    int total_q = 0) {
   constexpr int NW = kKvWaves;
   constexpr int KB = kKvKb;
   constexpr int BQ = kKvBq;
@@ -273,13 +280,37 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   const int G = Hq / Hkv;
   const int kv0 = jt * BKV;
   const int kbase = kv0 + wave * 32 * KB;
+  // This unit's sequence lengths, the element offset of its K/V rows and the
+  // row strides in elements (D for [B][H][N][D]; H*D for a packed
+  // token-major batch, VARLEN, whose sequence b spans cu_q/cu_k[b] .. [b+1]).
+  int Nq = Nq_arg, Nk = Nk_arg, qs0 = 0;
+  size_t kv_off = (size_t)bhk * Nk * D;
+  const int SQ = VARLEN ? Hq * D : D;
+  const int SK = VARLEN ? Hkv * D : D;
+  if constexpr (VARLEN) {
+    qs0 = cu_q[b];
+    const int ks0 = cu_k[b];
+    Nq = cu_q[b + 1] - qs0;
+    Nk = cu_k[b + 1] - ks0;
+    if (kv0 >= Nk) return;  // the whole workgroup: past this sequence's keys
+    kv_off = ((size_t)ks0 * Hkv + hk) * D;
+  }
+  // Element offsets of query head bh's Q/dO rows and of its lse/delta.
+  auto q_off = [&](int bh) -> size_t {
+    if constexpr (VARLEN) return ((size_t)qs0 * Hq + (bh - b * Hq)) * D;
+    return (size_t)bh * Nq * D;
+  };
+  auto l_off = [&](int bh) -> size_t {
+    if constexpr (VARLEN) return (size_t)(bh - b * Hq) * total_q + qs0;
+    return (size_t)bh * Nq;
+  };
 
   // This lane's K and V rows: B operands with n = key, k = head dim.
   u32x4 kf[KB][KSTEPS];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = min(kbase + kb * 32 + l32, Nk - 1);
-    const uint16_t* kr = K + ((size_t)bhk * Nk + key) * D;
+    const uint16_t* kr = K + kv_off + (size_t)key * SK;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) kf[kb][ks] = ldg<u32x4>(kr + ks * 16 + hf * 8);
   }
@@ -294,10 +325,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   extern __shared__ __attribute__((aligned(1024))) char vbuf[];  // dkdv_vbuf_bytes(D)
   char* vw = vbuf + wave * VROWS * ROWB;
   {
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (size_t)bhk * Nk * D, (uint32_t)Nk * ROWB);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * SK * 2);
 #pragma unroll
     for (int blk = 0; blk < VROWS * ROWB / 1024; ++blk)
-      buffer_load_lds16(rV, vw + blk * 1024, swz_src_offset<ROWB>(lane, blk), kbase * ROWB);
+      buffer_load_lds16(rV, vw + blk * 1024, swz_src_offset<ROWB>(lane, blk, SK * 2),
+                        kbase * SK * 2);
   }
 
   const int nqt = (Nq + BQ - 1) / BQ;
@@ -316,25 +348,25 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   };
   int qoff[LPW];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) qoff[i] = swz_src_offset<ROWB>(lane, wave * LPW + i);
+  for (int i = 0; i < LPW; ++i) qoff[i] = swz_src_offset<ROWB>(lane, wave * LPW + i, SQ * 2);
   auto issue = [&](int it, int slot) {
     int bh, q0;
     tile_head(it, &bh, &q0);
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * ROWB);
-    const __amdgpu_buffer_rsrc_t rG = make_rsrc(dO + (size_t)bh * Nq * D, (uint32_t)Nq * ROWB);
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Q + q_off(bh), (uint32_t)Nq * SQ * 2);
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc(dO + q_off(bh), (uint32_t)Nq * SQ * 2);
     char* qd = sslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      buffer_load_lds16(rQ, qd + i * 1024, qoff[i], q0 * ROWB);
-      buffer_load_lds16(rG, qd + QTILE + i * 1024, qoff[i], q0 * ROWB);
+      buffer_load_lds16(rQ, qd + i * 1024, qoff[i], q0 * SQ * 2);
+      buffer_load_lds16(rG, qd + QTILE + i * 1024, qoff[i], q0 * SQ * 2);
     }
     // wave 0: lse, wave 1: delta (each with its own uniform descriptor; a
     // pointer chosen per wave would make the descriptor look divergent)
     // (descriptors built outside the lane-divergent branches, so that they
     // stay scalar)
     char* ld = sslot(slot) + 2 * QTILE;
-    const __amdgpu_buffer_rsrc_t rL = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
-    const __amdgpu_buffer_rsrc_t rD = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(LSE + l_off(bh), (uint32_t)Nq * 4);
+    const __amdgpu_buffer_rsrc_t rD = make_rsrc(Delta + l_off(bh), (uint32_t)Nq * 4);
     if (wave == 0 && lane < BQ)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (lds_void_t*)ld, 4, lane * 4, q0 * 4, 0, 0);
     if (wave == 1 && lane < BQ)
@@ -537,8 +569,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   // dK = scale * sum dS^T Q, dV = sum P^T dO.  Accumulator register r of
   // block (kb, db) holds key kbase + 32*kb + 8*(r/4) + 4*hf + r%4 at head dim
   // 32*db + l32.
-  uint16_t* dkp = dK + (size_t)bhk * Nk * D;
-  uint16_t* dvp = dV + (size_t)bhk * Nk * D;
+  uint16_t* dkp = dK + kv_off;
+  uint16_t* dvp = dV + kv_off;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -554,7 +586,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) {
         const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
         if (key < Nk) {
-          const size_t off = (size_t)key * D + db * 32 + l32;
+          const size_t off = (size_t)key * SK + db * 32 + l32;
           dkp[off] = (uint16_t)(pack_bf16(dk[kb][db][r] * scale, 0.f) & 0xffff);
           dvp[off] = (uint16_t)(pack_bf16(dv[kb][db][r], 0.f) & 0xffff);
         }
@@ -569,13 +601,15 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 // row-major K tile.  K/V tiles of 64 keys are double-buffered in LDS.
 // WIN: sliding window as for bwd_dkdv_kernel; only the key tiles that some
 // row's window reaches are visited.
-template <int D, bool CAUSAL, bool WIN = false>
+template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, float scale, float scale_log2,
-    int BH, int nqt, int win_l = -1, int win_r = -1) {
+    uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale,
+    float scale_log2, int BH, int nqt, int win_l = -1, int win_r = -1,
+    const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
+    int total_q = 0) {
   constexpr int NW = kDqWaves;
   constexpr int BR = kDqBr;
   constexpr int BC = kDqBc;
@@ -600,25 +634,40 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int hk = h / (Hq / Hkv);
-  const size_t kv_off = (size_t)(b * Hkv + hk) * Nk * D;
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kv_off, (uint32_t)Nk * ROWB);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * ROWB);
-
   const int q0 = qt * BR;
+  // Sequence lengths, element offsets and row strides of this unit (as in
+  // bwd_dkdv_kernel).
+  int Nq = Nq_arg, Nk = Nk_arg;
+  size_t q_off = (size_t)bh * Nq * D, kv_off = (size_t)(b * Hkv + hk) * Nk * D;
+  size_t l_off = (size_t)bh * Nq;
+  const int SQ = VARLEN ? Hq * D : D;
+  const int SK = VARLEN ? Hkv * D : D;
+  if constexpr (VARLEN) {
+    const int qs0 = cu_q[b], ks0 = cu_k[b];
+    Nq = cu_q[b + 1] - qs0;
+    Nk = cu_k[b + 1] - ks0;
+    if (q0 >= Nq) return;  // the whole workgroup: past this sequence's rows
+    q_off = ((size_t)qs0 * Hq + h) * D;
+    kv_off = ((size_t)ks0 * Hkv + hk) * D;
+    l_off = (size_t)h * total_q + qs0;
+  }
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kv_off, (uint32_t)Nk * SK * 2);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * SK * 2);
+
   const int qrow = q0 + wave * 32 + l32;
   const int qrow_c = qrow < Nq ? qrow : Nq - 1;
   u32x4 qf[KSTEPS], gf[KSTEPS];
   {
-    const uint16_t* qr = Q + ((size_t)bh * Nq + qrow_c) * D;
-    const uint16_t* gr = dO + ((size_t)bh * Nq + qrow_c) * D;
+    const uint16_t* qr = Q + q_off + (size_t)qrow_c * SQ;
+    const uint16_t* gr = dO + q_off + (size_t)qrow_c * SQ;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       qf[ks] = ldg<u32x4>(qr + ks * 16 + hf * 8);
       gf[ks] = ldg<u32x4>(gr + ks * 16 + hf * 8);
     }
   }
-  const float lse2 = LSE[(size_t)bh * Nq + qrow_c] * kLog2e;
-  const float dlt = Delta[(size_t)bh * Nq + qrow_c];
+  const float lse2 = LSE[l_off + qrow_c] * kLog2e;
+  const float dlt = Delta[l_off + qrow_c];
 
   int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
   int jf = 0;  // first key tile visited
@@ -630,14 +679,14 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
 
   int ldo[LPW];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) ldo[i] = swz_src_offset<ROWB>(lane, wave * LPW + i);
+  for (int i = 0; i < LPW; ++i) ldo[i] = swz_src_offset<ROWB>(lane, wave * LPW + i, SK * 2);
   auto issue = [&](int j, int slot) {
     char* dk_ = kslot(slot) + wave * LPW * 1024;
     char* dv_ = vslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      buffer_load_lds16(rK, dk_ + i * 1024, ldo[i], (jf + j) * TILE);
-      buffer_load_lds16(rV, dv_ + i * 1024, ldo[i], (jf + j) * TILE);
+      buffer_load_lds16(rK, dk_ + i * 1024, ldo[i], (jf + j) * BC * SK * 2);
+      buffer_load_lds16(rV, dv_ + i * 1024, ldo[i], (jf + j) * BC * SK * 2);
     }
   };
   // A operands of S^T / dP^T (b128): key row kb*32 + l32, chunk 2*ks + hf.
@@ -778,7 +827,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
 
   // dQ = scale * dQ^T, written as bf16 rows.
   if (qrow < Nq) {
-    uint16_t* op = dQ + ((size_t)bh * Nq + qrow) * D;
+    uint16_t* op = dQ + q_off + (size_t)qrow * SQ;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -798,7 +847,7 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
                           bool causal, hipStream_t stream) {
   const int rows = B * Hq * Nq;
   hipLaunchKernelGGL((bwd_delta_kernel<float, 64>), dim3((rows + 15) / 16), dim3(256), 0,
-                     stream, o, dout, delta, rows);
+                     stream, o, dout, delta, rows, 1);
   hipLaunchKernelGGL(bwd_f32_dq_kernel, dim3((Nq + kBF32T - 1) / kBF32T, B * Hq), dim3(64), 0,
                      stream, q, k, v, dout, lse, delta, dq, Hq, Hkv, Nq, Nk, scale,
                      causal ? 1 : 0);
@@ -808,16 +857,16 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
 }
 
 hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int B, int Hq, int Nq,
-                          int d, hipStream_t stream) {
+                          int d, hipStream_t stream, int heads) {
   const int rows = B * Hq * Nq;
   const __bf16* ob = (const __bf16*)o;
   const __bf16* gb = (const __bf16*)dout;
   if (d == 128)
     hipLaunchKernelGGL((bwd_delta_kernel<__bf16, 128>), dim3((rows + 15) / 16), dim3(256), 0,
-                       stream, ob, gb, delta, rows);
+                       stream, ob, gb, delta, rows, heads);
   else
     hipLaunchKernelGGL((bwd_delta_kernel<__bf16, 64>), dim3((rows + 15) / 16), dim3(256), 0,
-                       stream, ob, gb, delta, rows);
+                       stream, ob, gb, delta, rows, heads);
   return hipGetLastError();
 }
 
@@ -895,6 +944,63 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
     }
   }
 #undef FA_LAUNCH_DQ
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_varlen(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* lse, const float* delta, void* dk, void* dv,
+                                  const int* cu_q, const int* cu_k, int batch, int Hq, int Hkv,
+                                  int total_q, int max_seqlen_k, int d, float scale, bool causal,
+                                  hipStream_t stream) {
+  const int BHkv = batch * Hkv;
+  dim3 grid(BHkv * ((max_seqlen_k + kKvBkv - 1) / kKvBkv)), block(kKvWaves * 64);
+  auto Q = (const uint16_t*)q;
+  auto K = (const uint16_t*)k;
+  auto V = (const uint16_t*)v;
+  auto G = (const uint16_t*)dout;
+  auto dK = (uint16_t*)dk;
+  auto dV = (uint16_t*)dv;
+  const float sl2 = scale * kLog2e;
+#define FA_LAUNCH_DKDV_VL(DD, CC)                                                            \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC, false, true>), grid, block, dkdv_vbuf_bytes(DD), \
+                     stream, Q, K, V, G, lse, delta, dK, dV, Hq, Hkv, 0, 0, scale, sl2, BHkv,   \
+                     -1, -1, cu_q, cu_k, total_q)
+  if (d == 128) {
+    if (causal) FA_LAUNCH_DKDV_VL(128, true);
+    else FA_LAUNCH_DKDV_VL(128, false);
+  } else {
+    if (causal) FA_LAUNCH_DKDV_VL(64, true);
+    else FA_LAUNCH_DKDV_VL(64, false);
+  }
+#undef FA_LAUNCH_DKDV_VL
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_varlen(const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* delta, void* dq, const int* cu_q,
+                                const int* cu_k, int batch, int Hq, int Hkv, int total_q,
+                                int max_seqlen_q, int d, float scale, bool causal,
+                                hipStream_t stream) {
+  const int BH = batch * Hq;
+  const int nqt = (max_seqlen_q + kDqBr - 1) / kDqBr;
+  dim3 grid(BH * nqt), block(kDqWaves * 64);
+  auto Q = (const uint16_t*)q;
+  auto K = (const uint16_t*)k;
+  auto V = (const uint16_t*)v;
+  auto G = (const uint16_t*)dout;
+  auto dQ = (uint16_t*)dq;
+  const float sl2 = scale * kLog2e;
+#define FA_LAUNCH_DQ_VL(DD, CC)                                                                  \
+  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, false, true>), grid, block, 0, stream, Q, K, V, G, lse, \
+                     delta, dQ, Hq, Hkv, 0, 0, scale, sl2, BH, nqt, -1, -1, cu_q, cu_k, total_q)
+  if (d == 128) {
+    if (causal) FA_LAUNCH_DQ_VL(128, true);
+    else FA_LAUNCH_DQ_VL(128, false);
+  } else {
+    if (causal) FA_LAUNCH_DQ_VL(64, true);
+    else FA_LAUNCH_DQ_VL(64, false);
+  }
+#undef FA_LAUNCH_DQ_VL
   return hipGetLastError();
 }
 

@@ -30,8 +30,11 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
                           const float* dout, const float* lse, float* dq, float* dk, float* dv,
                           float* delta, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
                           bool causal, hipStream_t stream);
+// heads > 1: the rows are a packed token-major [tokens][heads][d] batch and
+// delta is written head-major [heads][tokens] (call with B = Hq = 1, Nq =
+// tokens * heads).
 hipError_t launch_bwd_pre(const void* o, const void* dout, float* delta, int B, int Hq, int Nq,
-                          int d, hipStream_t stream);
+                          int d, hipStream_t stream, int heads = 1);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                            const float* lse, const float* delta, void* dk, void* dv, int B,
                            int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal,
@@ -40,6 +43,16 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
                          int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream,
                          int win_l = -1, int win_r = -1);
+hipError_t launch_bwd_dkdv_varlen(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* lse, const float* delta, void* dk, void* dv,
+                                  const int* cu_q, const int* cu_k, int batch, int Hq, int Hkv,
+                                  int total_q, int max_seqlen_k, int d, float scale, bool causal,
+                                  hipStream_t stream);
+hipError_t launch_bwd_dq_varlen(const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* delta, void* dq, const int* cu_q,
+                                const int* cu_k, int batch, int Hq, int Hkv, int total_q,
+                                int max_seqlen_q, int d, float scale, bool causal,
+                                hipStream_t stream);
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
                                float* lse_part, int B, int Hq, int Hkv, int Nk, int d,

@@ -187,6 +187,29 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
                         hipStream_t stream);
 
 /*
+ * Backward over a packed variable-length batch (the gradients of
+ * fa_fwd_varlen, [CH18] §18.7.1 for the packing, §18.4.4 for the gradients):
+ * q, o, dout, dq [total_q][Hq][d] and k, v, dk, dv [total_k][Hkv][d], bf16,
+ * token-major; lse [Hq][total_q] as written by fa_fwd_varlen for the same
+ * inputs; cu_seqlens_q / cu_seqlens_k and max_seqlen_q / max_seqlen_k as for
+ * fa_fwd_varlen (device int32 offsets, not checked on the host).
+ *   workspace: at least fa_bwd_workspace_size(1, Hq, total_q, d) bytes,
+ *   16-byte aligned (delta, head-major like lse).
+ * Gradients never cross a sequence boundary; a key with no visible query
+ * (e.g. a sequence with keys but no queries) gets dK = dV = 0, a query with
+ * no key dQ = 0.  Same three launches as fa_bwd; deterministic.
+ *   d in {64, 128}; total_q * Hq * d * 2 and total_k * Hkv * d * 2 < 2^31.
+ */
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k,
+                        int batch, int Hq, int Hkv, int total_q, int total_k,
+                        int max_seqlen_q, int max_seqlen_k, int d,
+                        float scale, int causal, hipStream_t stream);
+
+/*
  * The three stages of fa_bwd as separate calls, for callers that schedule or
  * time them individually.  Same arguments and workspace as fa_bwd; fa_bwd_pre
  * must precede the other two on the stream (or be ordered before them), which

@@ -200,6 +200,30 @@ def test_varlen_validation(lib):
     assert call(tk=1 << 20, mk=1 << 20, Hkv=16, Hq=16) == fa.FA_ERR_UNSUPPORTED
 
 
+def test_varlen_backward_validation(lib):
+    """fa_bwd_varlen: the forward's checks, the query-side byte range, and the
+    workspace (delta for every (head, token) row)."""
+    need = lib.fa_bwd_workspace_size(1, 4, 100, 128)
+    assert need >= 4 * 100 * 4
+
+    def call(cq=FAKE, ck=FAKE, batch=2, Hq=4, Hkv=2, tq=100, tk=100, mq=60, mk=60, d=128,
+             ws=FAKE, wsb=None, dq=FAKE):
+        return lib.fa_bwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, ws,
+                                 need if wsb is None else wsb, cq, ck, batch, Hq, Hkv, tq, tk,
+                                 mq, mk, d, 0.1, 1, None)
+    assert call(cq=None) == fa.FA_ERR_INVALID_ARG
+    assert call(ck=FAKE + 2) == fa.FA_ERR_INVALID_ARG
+    assert call(dq=MIS) == fa.FA_ERR_INVALID_ARG
+    assert call(batch=0) == fa.FA_ERR_INVALID_ARG
+    assert call(mq=101) == fa.FA_ERR_INVALID_ARG
+    assert call(Hq=3) == fa.FA_ERR_INVALID_ARG
+    assert call(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert call(tq=1 << 20, mq=1 << 20, Hq=16, Hkv=16) == fa.FA_ERR_UNSUPPORTED
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(ws=MIS) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=need - 1) == fa.FA_ERR_WORKSPACE
+
+
 def test_paged_decode_validation(lib):
     """fa_decode_splitkv_paged: page sizes (powers of two, 16..4096), table
     capacity against max_seqlen, pointers, splits, group size."""

@@ -514,6 +514,104 @@ def test_varlen_config_sampled(fa_gpu):
         assert maxabs(got_l, rl[0]) <= BF16_LSE, b
 
 
+# --------------------------------------------------------- varlen backward
+
+def varlen_grad_case(lens_q, Hq, Hkv, d, seed, lens_k=None):
+    q, k, v, cq, ck = varlen_case(lens_q, Hq, Hkv, d, seed, lens_k)
+    g = torch.Generator("cpu").manual_seed(seed + 1000)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16).cuda()
+    return q, k, v, do, cq, ck
+
+
+_VARLEN_EQUAL = [
+    ((5, 300, 1, 257), None, 4, 2, 128),     # ragged tails, a single-token sequence
+    ((40, 0, 77, 513), None, 8, 1, 128),     # an empty sequence; G = 8
+    ((256, 255, 257), None, 2, 2, 64),
+    ((1000,), None, 2, 1, 64),
+]
+# unequal query and key lengths: non-causal only (causal packs are square)
+_VARLEN_UNEQUAL = [
+    ((5, 9, 70), (0, 33, 100), 2, 2, 128),   # queries without keys
+    ((0, 50, 64), (30, 50, 300), 4, 4, 128),  # keys without queries
+]
+
+
+@pytest.mark.parametrize("lens_q,lens_k,Hq,Hkv,d,causal",
+                         [c + (cz,) for c in _VARLEN_EQUAL for cz in (False, True)] +
+                         [c + (False,) for c in _VARLEN_UNEQUAL])
+def test_varlen_backward_small(fa_gpu, lens_q, lens_k, Hq, Hkv, d, causal):
+    q, k, v, do, cq, ck = varlen_grad_case(lens_q, Hq, Hkv, d, seed=74, lens_k=lens_k)
+    lk = lens_q if lens_k is None else lens_k
+    say(f"varlen backward lens_q={lens_q} lens_k={lk} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    cqd = torch.tensor(cq, dtype=torch.int32, device="cuda")
+    ckd = torch.tensor(ck, dtype=torch.int32, device="cuda")
+    mq, mk = max(max(lens_q), 1), max(max(lk), 1)
+    o, lse = fa_gpu.forward_varlen(q, k, v, cqd, ckd, mq, mk, causal=causal)
+    grads = fa_gpu.backward_varlen(q, k, v, o, lse, do, cqd, ckd, mq, mk, causal=causal)
+    torch.cuda.synchronize()
+    ref = A.backward_varlen(to_f64(q), to_f64(k), to_f64(v), to_f64(do), cq, ck,
+                            1 / math.sqrt(d), causal)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        e = rel_l2(to_f64(got), want)
+        assert e <= BF16_GRAD, (name, e)
+    dq, dk, dv = (to_f64(t) for t in grads)
+    for b in range(len(lens_q)):
+        if lk[b] == 0:
+            assert not dq[cq[b]:cq[b + 1]].any()
+        if lens_q[b] == 0:
+            assert not dk[ck[b]:ck[b + 1]].any() and not dv[ck[b]:ck[b + 1]].any()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_backward_equals_dense(fa_gpu, causal):
+    """Equal-length sequences packed token-major run the same arithmetic as
+    the [B][H][N][d] backward: gradients agree bit for bit."""
+    B, N, Hq, Hkv, d = 3, 1000, 4, 2, 128
+    q, k, v, do, cq, _ = varlen_grad_case((N,) * B, Hq, Hkv, d, seed=75)
+    say(f"varlen backward vs dense causal={causal}")
+    cqd = torch.tensor(cq, dtype=torch.int32, device="cuda")
+    o, lse = fa_gpu.forward_varlen(q, k, v, cqd, cqd, N, N, causal=causal)
+    dq, dk, dv = fa_gpu.backward_varlen(q, k, v, o, lse, do, cqd, cqd, N, N, causal=causal)
+
+    def dense(t, H):
+        return t.view(B, N, H, d).permute(0, 2, 1, 3).contiguous()
+
+    od = dense(o, Hq)
+    lsed = lse.view(Hq, B, N).permute(1, 0, 2).contiguous()
+    gd = fa_gpu.backward(dense(q, Hq), dense(k, Hkv), dense(v, Hkv), od, lsed, dense(do, Hq),
+                         causal=causal)
+    torch.cuda.synchronize()
+    for got, want, H in zip((dq, dk, dv), gd, (Hq, Hkv, Hkv)):
+        assert torch.equal(dense(got, H), want)
+
+
+def test_varlen_backward_config_sampled(fa_gpu):
+    """The packed workload (10 sequences, 31706 tokens, H=16, d=128, causal)
+    backward in the benchmark's launch configuration: complete dQ/dK/dV of
+    one head of the longest sequence and of two heads of two short ones,
+    against the oracle's per-head backward."""
+    from workloads import VARLEN, make_varlen_inputs
+    w = VARLEN["varlen_bf16"]
+    x = make_varlen_inputs(w, device="cuda")
+    say("varlen_bf16 backward full size")
+    mx = max(w.seqlens)
+    o, lse = fa_gpu.forward_varlen(x["q"], x["k"], x["v"], x["cu"], x["cu"], mx, mx,
+                                   causal=w.causal)
+    dq, dk, dv = fa_gpu.backward_varlen(x["q"], x["k"], x["v"], o, lse, x["do"], x["cu"],
+                                        x["cu"], mx, mx, causal=w.causal)
+    torch.cuda.synchronize()
+    dq, dk, dv = to_f64(dq), to_f64(dk), to_f64(dv)
+    cu = x["cu"].tolist()
+    for b, h in ((0, 3), (1, 0), (1, 15), (5, 0), (5, 15)):
+        sl = slice(cu[b], cu[b + 1])
+        qq, kk, vv, gg = (to_f64(x[n][sl, h]) for n in ("q", "k", "v", "do"))
+        rq, rk, rv, _ = A.head_backward(qq, kk, vv, gg, w.scale, w.causal)
+        for name, got, want in (("dq", dq[sl, h], rq), ("dk", dk[sl, h], rk),
+                                ("dv", dv[sl, h], rv)):
+            e = rel_l2(got, want)
+            assert e <= BF16_GRAD, (b, h, name, e)
+
+
 # ------------------------------------------------------------- paged decode
 
 def paged_case(B, Hq, Hkv, seqlens, page, d, splits, seed, spare=3):

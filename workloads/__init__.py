@@ -202,20 +202,24 @@ class Varlen:
         f = sum(4.0 * self.Hq * n * n * self.d for n in self.seqlens)
         return f * 0.5 if self.causal else f
 
+    def bwd_flops(self) -> float:
+        return 2.5 * self.fwd_flops()
+
 
 def make_varlen_inputs(w: Varlen, device: str = "cpu"):
-    """q [total][Hq][d], k/v [total][Hkv][d] (bf16) and cu int32 [len+1].
-    Draw order: Q, K, V."""
+    """q, do [total][Hq][d], k/v [total][Hkv][d] (bf16) and cu int32 [len+1].
+    Draw order: Q, K, V, dO."""
     gen = _gen(w.seed, device)
     T = w.total
     q = _randn((T, w.Hq, w.d), gen, device).to(torch.bfloat16)
     k = _randn((T, w.Hkv, w.d), gen, device).to(torch.bfloat16)
     v = _randn((T, w.Hkv, w.d), gen, device).to(torch.bfloat16)
+    do = _randn((T, w.Hq, w.d), gen, device).to(torch.bfloat16)
     cu = [0]
     for n in w.seqlens:
         cu.append(cu[-1] + n)
     return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(),
-            "cu": torch.tensor(cu, dtype=torch.int32, device=device)}
+            "do": do.contiguous(), "cu": torch.tensor(cu, dtype=torch.int32, device=device)}
 
 
 PAGED = {
