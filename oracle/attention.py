@@ -338,3 +338,33 @@ def forward_block_sparse(q, k, v, scale, q_ptr, kv_idx, block_q, block_k, causal
             o[b, h][live] = p @ v[b, hk]
             lse[b, h][live] = m + np.log(l)
     return o, lse
+
+
+def backward_block_sparse(q, k, v, do, scale, q_ptr, kv_idx, block_q, block_k, causal=False):
+    """Gradients of forward_block_sparse ([CH18] §18.2.4 (2) with the
+    block-sparse visible set of [CH18] §18.8.1; skipped blocks have P = 0, so
+    they receive no gradient).  Returns (dQ, dK, dV) fp64; a row that sees no
+    key gets dQ = 0 and a key that no row sees dK = dV = 0."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    do = _f64(do)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    ok = block_sparse_allowed(Nq, Nk, q_ptr, kv_idx, block_q, block_k, causal)
+    live = ok.any(axis=1)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head(h, Hq, Hkv)
+            s = np.where(ok[live], scale * (q[b, h][live] @ k[b, hk].T), -np.inf)
+            p, _, _ = softmax_rows(s)
+            dp = do[b, h][live] @ v[b, hk].T
+            ds = softmax_backward(p, dp)
+            dq[b, h][live] = scale * (ds @ k[b, hk])
+            dk[b, hk] += scale * (ds.T @ q[b, h][live])
+            dv[b, hk] += p.T @ do[b, h][live]
+    return dq, dk, dv
+

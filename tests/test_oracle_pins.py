@@ -679,3 +679,51 @@ def test_block_sparse_all_blocks_is_dense(causal):
     o, lse = A.forward_block_sparse(q, k, v, 0.4, ptr, idx, bq, bk, causal)
     od, ld = A.forward(q, k, v, 0.4, causal)
     assert np.allclose(o, od, atol=1e-14) and np.allclose(lse, ld, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal,rows", [
+    (False, [[0, 2], [], [1]]),         # an empty query block; key block 3 never listed
+    (True, [[1], [0, 2], [3, 1, 0]]),   # causal: rows 0..3 list only block 1 (all after them)
+])
+def test_block_sparse_backward_finite_differences(causal, rows):
+    """Central differences of L = sum(O * G) over the block-sparse forward
+    match backward_block_sparse (GQA), including exactly-zero gradients for
+    rows that see no key and for keys in no visible block."""
+    N, d, bq, bk, scale, h = 12, 3, 4, 3, 0.6, 1e-6
+    ptr, idx = _csr(rows)
+    q, k, v, g = rnd(1, 2, N, d), rnd(1, 1, N, d), rnd(1, 1, N, d), rnd(1, 2, N, d)
+    dq, dk, dv = A.backward_block_sparse(q, k, v, g, scale, ptr, idx, bq, bk, causal)
+
+    def loss(q_, k_, v_):
+        return float((A.forward_block_sparse(q_, k_, v_, scale, ptr, idx, bq, bk, causal)[0]
+                      * g).sum())
+
+    for x, dx in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[i] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.linalg.norm(num - dx) <= 1e-7 * max(1.0, np.linalg.norm(dx))
+    ok = A.block_sparse_allowed(N, N, ptr, idx, bq, bk, causal)
+    assert not dq[:, :, ~ok.any(axis=1)].any()
+    assert not dk[:, :, ~ok.any(axis=0)].any() and not dv[:, :, ~ok.any(axis=0)].any()
+    assert (~ok.any(axis=1)).any() and (~ok.any(axis=0)).any()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_backward_all_blocks_is_dense(causal):
+    """Listing every key block reproduces the dense (or causal) backward."""
+    N, d, bq, bk = 20, 4, 8, 6
+    q, k, v, g = rnd(2, 2, N, d), rnd(2, 1, N, d), rnd(2, 1, N, d), rnd(2, 2, N, d)
+    nb = -(-N // bk)
+    ptr, idx = _csr([list(range(nb))] * (-(-N // bq)))
+    got = A.backward_block_sparse(q, k, v, g, 0.4, ptr, idx, bq, bk, causal)
+    want = A.backward(q, k, v, g, 0.4, causal)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b, atol=1e-13)
