@@ -324,7 +324,22 @@ def main(argv=None):
                                      "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                                      "density": round(wsp.visible_pairs() / (wsp.Nq * wsp.Nk), 4)}
         log(f"block-sparse fwd {t:.3f} ms {tf:.0f} TF")
-        del xs, osp, lsp
+        dqs, dks, dvs = (torch.empty_like(xs[n]) for n in ("q", "k", "v"))
+        wss_bytes = fa.fa_bwd_block_sparse_workspace_size(wsp.B, wsp.Hq, wsp.Nq, wsp.Nk, wsp.d)
+        wss = torch.empty(wss_bytes, dtype=torch.uint8, device="cuda")
+
+        def spb():
+            fa.fa_bwd_block_sparse(xs["q"], xs["k"], xs["v"], osp, xs["do"], lsp, dqs, dks, dvs,
+                                   wss, wss_bytes, wsp.B, wsp.Hq, wsp.Hkv, wsp.Nq, wsp.Nk, wsp.d,
+                                   wsp.scale, wsp.causal, pd, idd, mb, sh)
+
+        spb()
+        tb = timed(spb, iters, stream)
+        tfb = wsp.bwd_flops() / (tb * 1e-3) / 1e12
+        parts["fwd_block_sparse"].update({"bwd_ms": round(tb, 4), "bwd_tflops": round(tfb, 1),
+                                          "bwd_frac_peak": round(tfb / PEAK_BF16_TFLOPS, 4)})
+        log(f"block-sparse bwd {tb:.3f} ms {tfb:.0f} TF")
+        del xs, osp, lsp, dqs, dks, dvs, wss
 
     if not only or "decode_paged" in only:
         from workloads import PAGED, make_paged_inputs

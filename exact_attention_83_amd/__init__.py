@@ -46,6 +46,9 @@ _SIGS = {
                                      _I, _F, _I, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                            _P]),
+    "fa_bwd_block_sparse_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "fa_bwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                                 _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
     "fa_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P,
                            _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
@@ -191,6 +194,19 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, Hq, Hkv, total_q, total_k,
                   max_seqlen_k, d, scale, causal, stream=None):
     _call("fa_fwd_varlen", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_q), _ptr(cu_k),
           batch, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, scale, int(causal),
+          _stream(stream))
+
+
+def fa_bwd_block_sparse_workspace_size(B, Hq, Nq, Nk, d):
+    return load().fa_bwd_block_sparse_workspace_size(B, Hq, Nq, Nk, d)
+
+
+def fa_bwd_block_sparse(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                        Nq, Nk, d, scale, causal, q_tile_ptr, kv_block_idx, max_blocks_per_tile,
+                        stream=None):
+    _call("fa_bwd_block_sparse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+          scale, int(causal), _ptr(q_tile_ptr), _ptr(kv_block_idx), max_blocks_per_tile,
           _stream(stream))
 
 
@@ -372,6 +388,26 @@ def forward_block_sparse(q, k, v, q_tile_ptr, kv_block_idx, causal=False, scale=
     fa_fwd_block_sparse(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, s, causal, q_tile_ptr,
                         kv_block_idx, max_blocks_per_tile, stream)
     return o, lse
+
+
+def backward_block_sparse(q, k, v, o, lse, dout, q_tile_ptr, kv_block_idx, causal=False,
+                          scale=None, max_blocks_per_tile=None, workspace=None, stream=None):
+    """dQ, dK, dV of forward_block_sparse for the same inputs and pattern."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    s = _default_scale(d, scale)
+    if max_blocks_per_tile is None:
+        max_blocks_per_tile = int((q_tile_ptr[1:] - q_tile_ptr[:-1]).max().item())
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws_bytes = fa_bwd_block_sparse_workspace_size(B, Hq, Nq, Nk, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    fa_bwd_block_sparse(q, k, v, o, dout, lse, dq, dk, dv, ws, ws.numel() * ws.element_size(), B,
+                        Hq, Hkv, Nq, Nk, d, s, causal, q_tile_ptr, kv_block_idx,
+                        max_blocks_per_tile, stream)
+    return dq, dk, dv
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seqlens, num_splits, max_seqlen=None,

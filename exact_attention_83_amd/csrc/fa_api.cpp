@@ -231,6 +231,43 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   return hip_status(e);
 }
 
+size_t fa_bwd_block_sparse_workspace_size(int B, int Hq, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+  const size_t nqb = (size_t)(Nq + FA_SPARSE_BLOCK_Q - 1) / FA_SPARSE_BLOCK_Q;
+  const size_t nkb = (size_t)(Nk + FA_SPARSE_BLOCK_K - 1) / FA_SPARSE_BLOCK_K;
+  return fa_bwd_workspace_size(B, Hq, Nq, d) + round256(nqb * nkb);
+}
+
+fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                              int Nq, int Nk, int d, float scale, int causal,
+                              const int* q_tile_ptr, const int* kv_block_idx,
+                              int max_blocks_per_tile, hipStream_t stream) {
+  if (q_tile_ptr == nullptr || kv_block_idx == nullptr ||
+      (reinterpret_cast<uintptr_t>(q_tile_ptr) & 3u) ||
+      (reinterpret_cast<uintptr_t>(kv_block_idx) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
+                               Hq, Hkv, Nq, Nk, d, scale, causal))
+    return s;
+  if (max_blocks_per_tile < 0) return FA_ERR_INVALID_ARG;
+  if (max_blocks_per_tile > 256) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // the dK/dV work units hold the list of query tiles they visit in 256 slots
+  if ((Nq + FA_SPARSE_BLOCK_Q - 1) / FA_SPARSE_BLOCK_Q > 256) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa_bwd_block_sparse_workspace_size(B, Hq, Nq, Nk, d))
+    return FA_ERR_WORKSPACE;
+  float* delta = static_cast<float*>(workspace);
+  uint8_t* map = static_cast<uint8_t*>(workspace) + fa_bwd_workspace_size(B, Hq, Nq, d);
+  hipError_t e = fa::launch_bwd_pre(o, dout, delta, B, Hq, Nq, d, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_bf16_sparse(q, k, v, dout, lse, delta, map, dq, dk, dv, q_tile_ptr,
+                                   kv_block_idx, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0,
+                                   stream);
+  return hip_status(e);
+}
+
 fa_status fa_bwd_pre(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Nq, int d, hipStream_t stream) {
   if (!aligned16(o) || !aligned16(dout)) return FA_ERR_INVALID_ARG;

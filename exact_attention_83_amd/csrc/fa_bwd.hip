@@ -190,6 +190,8 @@ constexpr int kKvBq = 32;              // query rows per inner tile
 constexpr int kDqWaves = 8;
 constexpr int kDqBr = 32 * kDqWaves;   // query rows per dQ work unit
 constexpr int kDqBc = 64;              // keys per KV tile
+constexpr int kSpBq = 256;             // query rows per block of a sparse pattern
+constexpr int kSpBk = 64;              // keys per block of a sparse pattern
 }  // namespace
 
 // Chunk swizzle of an LDS tile with ROWB-byte rows: chunk c of row r sits at
@@ -241,7 +243,7 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk, int stride = RO
 // WIN: sliding window (key j visible to query i iff i - win_l <= j <= i +
 // win_r; negative = unbounded): only the query tiles whose windows reach this
 // work unit's keys are visited.
-template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false>
+template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false>
 __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq_arg,
     int Nk_arg, float scale, float scale_log2, int BHkv, int win_l = -1, int win_r = -1,
     const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
-    int total_q = 0) {
+    int total_q = 0, const uint8_t* __restrict__ sp_map = nullptr, int sp_nkb = 0) {
   constexpr int NW = kKvWaves;
   constexpr int KB = kKvKb;
   constexpr int BQ = kKvBq;
@@ -339,12 +341,56 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     if (win_r >= 0) qt_begin = max(qt_begin, max(0, kv0 - win_r) / BQ);
     if (win_l >= 0) qt_end = min(qt_end, (kv0 + BKV - 1 + win_l) / BQ + 1);
   }
-  const int per_head = max(0, qt_end - qt_begin);
+  // SPARSE: the query blocks (kSpBq rows) whose list holds one of this
+  // unit's four key blocks (wave w's 64 keys are key block kv0/64 + w),
+  // compacted into LDS as block | (4-bit set of listed waves) << 16.
+  __shared__ int sp_list[SPARSE ? 256 : 1];
+  __shared__ int sp_cnt[SPARSE ? NW : 1];
+  int nact = 0;
+  if constexpr (SPARSE) {
+    static_assert(BKV == kSpBq && 32 * KB == kSpBk && NW * 64 == 256, "sparse block shapes");
+    const int nqb = (Nq + kSpBq - 1) / kSpBq;  // <= 256, checked on the host
+    const int kc0 = kv0 / kSpBk;
+    int bits = 0;
+    // causal: query blocks before this unit's keys see none of them
+    if (tid < nqb && (!CAUSAL || tid >= jt)) {
+      const uint8_t* row = sp_map + (size_t)tid * sp_nkb;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (kc0 + w < sp_nkb && row[kc0 + w]) bits |= 1 << w;
+    }
+    const uint64_t act = __builtin_amdgcn_ballot_w64(bits != 0);
+    if (lane == 0) sp_cnt[wave] = __builtin_popcountll(act);
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = sp_cnt[w];
+      if (w < wave) before += c;
+      nact += c;
+    }
+    nact = __builtin_amdgcn_readfirstlane(nact);
+    if (bits) {
+      const int pos = before + (int)__builtin_amdgcn_mbcnt_hi(
+                                   (uint32_t)(act >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0));
+      sp_list[pos] = tid | (bits << 16);
+    }
+    __syncthreads();
+  }
+  const int per_head = SPARSE ? nact * (kSpBq / BQ) : max(0, qt_end - qt_begin);
   const int total = per_head * G;
-  auto tile_head = [&](int it, int* bh, int* q0) {
+  // query tile `it` of the loop: head bh, first row q0, and (SPARSE) whether
+  // this wave's key block is listed for it
+  auto tile_head = [&](int it, int* bh, int* q0, bool* listed = nullptr) {
     const int gi = it / per_head;
+    const int x = it - gi * per_head;
     *bh = b * Hq + hk * G + gi;
-    *q0 = (qt_begin + (it - gi * per_head)) * BQ;
+    if constexpr (SPARSE) {
+      const int e = __builtin_amdgcn_readfirstlane(sp_list[x / (kSpBq / BQ)]);
+      *q0 = (e & 0xffff) * kSpBq + (x % (kSpBq / BQ)) * BQ;
+      if (listed) *listed = (e >> (16 + wave)) & 1;
+    } else {
+      *q0 = (qt_begin + x) * BQ;
+    }
   };
   int qoff[LPW];
 #pragma unroll
@@ -405,7 +451,8 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   auto body = [&](int it, auto S) {
     constexpr int slot = decltype(S)::value;
     int bh, q0;
-    tile_head(it, &bh, &q0);
+    bool listed = true;
+    tile_head(it, &bh, &q0, &listed);
     wait_vmem();
     lds_barrier();
     if (it + 1 < total) issue(it + 1, slot ^ 1);
@@ -449,6 +496,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       const int key = kbase + kb * 32 + l32;
       const int kb0 = kbase + kb * 32;
       bool need = (kb0 + 32 > Nk) || (q0 + BQ > Nq) || (CAUSAL && kb0 + 31 > q0);
+      if constexpr (SPARSE) need = need || !listed;
       if constexpr (WIN)
         need = need || (win_l >= 0 && kb0 < q0 + BQ - 1 - win_l) ||
                (win_r >= 0 && kb0 + 31 > q0 + win_r);
@@ -459,6 +507,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
           bool out = key >= Nk || qi >= Nq || (CAUSAL && key > qi);
           if constexpr (WIN)
             out = out || (win_l >= 0 && key < qi - win_l) || (win_r >= 0 && key > qi + win_r);
+          if constexpr (SPARSE) out = out || !listed;
           if (out) sb[kb][r] = -INFINITY;
         }
       }
@@ -499,7 +548,12 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
             const int x = EPP * m + t, gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
             if ((x & 7) == 0) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) nl[q] = -lvn[q] * kLog2e;
+              for (int q = 0; q < 4; ++q) {
+                nl[q] = -lvn[q] * kLog2e;
+                // a row that sees no key (lse = -inf, possible only with a
+                // sparse pattern) gets P = 0 rather than exp(-inf + inf)
+                if constexpr (SPARSE) nl[q] = lvn[q] == -INFINITY ? -INFINITY : nl[q];
+              }
               if (gr < 3) lvn = lds_read<f32x4>(ls, ((gr + 1) * 8 + hf * 4) * 4);
             }
             sb[kbe][r] = fast_exp2(fmaf(sb[kbe][r], scale_log2, nl[e]));
@@ -601,7 +655,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 // row-major K tile.  K/V tiles of 64 keys are double-buffered in LDS.
 // WIN: sliding window as for bwd_dkdv_kernel; only the key tiles that some
 // row's window reaches are visited.
-template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false>
+template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -609,7 +663,8 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale,
     float scale_log2, int BH, int nqt, int win_l = -1, int win_r = -1,
     const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
-    int total_q = 0) {
+    int total_q = 0, const int* __restrict__ sp_ptr = nullptr,
+    const int* __restrict__ sp_idx = nullptr) {
   constexpr int NW = kDqWaves;
   constexpr int BR = kDqBr;
   constexpr int BC = kDqBc;
@@ -666,7 +721,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
       gf[ks] = ldg<u32x4>(gr + ks * 16 + hf * 8);
     }
   }
-  const float lse2 = LSE[l_off + qrow_c] * kLog2e;
+  float lse2 = LSE[l_off + qrow_c] * kLog2e;
+  // a row that sees no key (lse = -inf, possible only with a sparse pattern)
+  // gets P = 0: every score of it is masked, and -inf - (+inf) = -inf
+  if constexpr (SPARSE) lse2 = lse2 == -INFINITY ? INFINITY : lse2;
   const float dlt = Delta[l_off + qrow_c];
 
   int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
@@ -675,7 +733,27 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     if (win_r >= 0) kv_end = min(kv_end, q0 + BR + win_r);
     if (win_l >= 0) jf = max(0, q0 - win_l) / BC;
   }
-  const int ntiles = (kv_end + BC - 1) / BC - jf;
+  int ntiles = (kv_end + BC - 1) / BC - jf;
+  // SPARSE: this query tile's list of key blocks, one entry per lane and
+  // register, read back with readlane (as in the forward).
+  int spc[4] = {0, 0, 0, 0};
+  if constexpr (SPARSE) {
+    static_assert(BR == kSpBq && BC == kSpBk, "sparse block shapes");
+    const int lo = sp_ptr[qt];
+    ntiles = min(max(sp_ptr[qt + 1] - lo, 0), 256);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r * 64 + lane < ntiles) spc[r] = sp_idx[lo + r * 64 + lane];
+  }
+  // key tile visited at loop position j
+  auto tile_of = [&](int j) -> int {
+    if constexpr (SPARSE) {
+      const int v = j < 64 ? spc[0] : j < 128 ? spc[1] : j < 192 ? spc[2] : spc[3];
+      return __builtin_amdgcn_readlane(v, j & 63);
+    } else {
+      return jf + j;
+    }
+  };
 
   int ldo[LPW];
 #pragma unroll
@@ -685,8 +763,8 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     char* dv_ = vslot(slot) + wave * LPW * 1024;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      buffer_load_lds16(rK, dk_ + i * 1024, ldo[i], (jf + j) * BC * SK * 2);
-      buffer_load_lds16(rV, dv_ + i * 1024, ldo[i], (jf + j) * BC * SK * 2);
+      buffer_load_lds16(rK, dk_ + i * 1024, ldo[i], tile_of(j) * BC * SK * 2);
+      buffer_load_lds16(rV, dv_ + i * 1024, ldo[i], tile_of(j) * BC * SK * 2);
     }
   };
   // A operands of S^T / dP^T (b128): key row kb*32 + l32, chunk 2*ks + hf.
@@ -722,7 +800,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     lds_barrier();
     const char* ks_ = kslot(slot);
     const char* vs_ = vslot(slot);
-    const int kv0 = (jf + j) * BC;
+    const int kv0 = tile_of(j) * BC;
 
     // Three phases so that the elementwise work runs beside matrix products:
     // (A) S^T = K Q^T; (B) dP^T = V dO^T with P = exp(S*scale - lse) of the
@@ -756,6 +834,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     if constexpr (WIN)
       need_mask = need_mask || (win_l >= 0 && kv0 < rw0 + 31 - win_l) ||
                   (win_r >= 0 && kv0 + BC - 1 > rw0 + win_r);
+    if constexpr (SPARSE) need_mask = need_mask || kv0 < 0;  // a bad list entry
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -765,6 +844,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
           bool out = key >= Nk || (CAUSAL && key > qrow);
           if constexpr (WIN)
             out = out || (win_l >= 0 && key < qrow - win_l) || (win_r >= 0 && key > qrow + win_r);
+          if constexpr (SPARSE) out = out || key < 0;
           if (out) s[kb][r] = -INFINITY;
         }
     }
@@ -1001,6 +1081,77 @@ hipError_t launch_bwd_dq_varlen(const void* q, const void* k, const void* v, con
     else FA_LAUNCH_DQ_VL(64, false);
   }
 #undef FA_LAUNCH_DQ_VL
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block-sparse backward.  The dQ kernel walks each query tile's list as the
+// forward does; the dK/dV kernel needs the opposite direction (which query
+// blocks list a key block), read from a byte map map[t][c] = 1 iff key block
+// c is in query tile t's list (entries past 256 and outside [0, nkb) are
+// ignored, as the forward ignores them).  One workgroup per query tile.
+__global__ __launch_bounds__(256) void sparse_block_map_kernel(const int* __restrict__ sp_ptr,
+                                                               const int* __restrict__ sp_idx,
+                                                               uint8_t* __restrict__ map,
+                                                               int nkb) {
+  const int t = blockIdx.x;
+  uint8_t* row = map + (size_t)t * nkb;
+  for (int c = threadIdx.x; c < nkb; c += 256) row[c] = 0;
+  __syncthreads();  // the zeros land before any entry is set
+  const int lo = sp_ptr[t];
+  const int n = min(max(sp_ptr[t + 1] - lo, 0), 256);
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int c = sp_idx[lo + e];
+    if (c >= 0 && c < nkb) row[c] = 1;
+  }
+}
+
+hipError_t launch_bwd_bf16_sparse(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* lse, const float* delta, uint8_t* map, void* dq,
+                                  void* dk, void* dv, const int* sp_ptr, const int* sp_idx, int B,
+                                  int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                                  bool causal, hipStream_t stream) {
+  const int nqb = (Nq + kSpBq - 1) / kSpBq;
+  const int nkb = (Nk + kSpBk - 1) / kSpBk;
+  hipLaunchKernelGGL(sparse_block_map_kernel, dim3(nqb), dim3(256), 0, stream, sp_ptr, sp_idx,
+                     map, nkb);
+  auto Q = (const uint16_t*)q;
+  auto K = (const uint16_t*)k;
+  auto V = (const uint16_t*)v;
+  auto G = (const uint16_t*)dout;
+  const float sl2 = scale * kLog2e;
+  const int BHkv = B * Hkv;
+  dim3 grid_kv(BHkv * ((Nk + kKvBkv - 1) / kKvBkv)), block_kv(kKvWaves * 64);
+  auto dK = (uint16_t*)dk;
+  auto dV = (uint16_t*)dv;
+#define FA_LAUNCH_DKDV_SP(DD, CC)                                                              \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC, false, false, true>), grid_kv, block_kv,          \
+                     dkdv_vbuf_bytes(DD), stream, Q, K, V, G, lse, delta, dK, dV, Hq, Hkv, Nq, \
+                     Nk, scale, sl2, BHkv, -1, -1, nullptr, nullptr, 0, map, nkb)
+  if (d == 128) {
+    if (causal) FA_LAUNCH_DKDV_SP(128, true);
+    else FA_LAUNCH_DKDV_SP(128, false);
+  } else {
+    if (causal) FA_LAUNCH_DKDV_SP(64, true);
+    else FA_LAUNCH_DKDV_SP(64, false);
+  }
+#undef FA_LAUNCH_DKDV_SP
+  const int BH = B * Hq;
+  const int nqt = (Nq + kDqBr - 1) / kDqBr;
+  dim3 grid_q(BH * nqt), block_q(kDqWaves * 64);
+  auto dQ = (uint16_t*)dq;
+#define FA_LAUNCH_DQ_SP(DD, CC)                                                                 \
+  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, false, false, true>), grid_q, block_q, 0, stream, Q, \
+                     K, V, G, lse, delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, -1, -1,      \
+                     nullptr, nullptr, 0, sp_ptr, sp_idx)
+  if (d == 128) {
+    if (causal) FA_LAUNCH_DQ_SP(128, true);
+    else FA_LAUNCH_DQ_SP(128, false);
+  } else {
+    if (causal) FA_LAUNCH_DQ_SP(64, true);
+    else FA_LAUNCH_DQ_SP(64, false);
+  }
+#undef FA_LAUNCH_DQ_SP
   return hipGetLastError();
 }
 

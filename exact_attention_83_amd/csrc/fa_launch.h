@@ -53,6 +53,12 @@ hipError_t launch_bwd_dq_varlen(const void* q, const void* k, const void* v, con
                                 const int* cu_k, int batch, int Hq, int Hkv, int total_q,
                                 int max_seqlen_q, int d, float scale, bool causal,
                                 hipStream_t stream);
+// map: nqb * nkb bytes of scratch (query tiles of 256 rows x key blocks of 64).
+hipError_t launch_bwd_bf16_sparse(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* lse, const float* delta, uint8_t* map, void* dq,
+                                  void* dk, void* dv, const int* sp_ptr, const int* sp_idx, int B,
+                                  int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                                  bool causal, hipStream_t stream);
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
                                float* lse_part, int B, int Hq, int Hkv, int Nk, int d,

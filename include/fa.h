@@ -187,6 +187,30 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
                         hipStream_t stream);
 
 /*
+ * Backward of the block-sparse forward (the gradients of fa_fwd_block_sparse
+ * for the same inputs and pattern; [CH18] §18.8.1 for the pattern, §18.4.4
+ * for the gradients; skipped blocks have P = 0 and get no gradient).  Same
+ * tensors as fa_bwd, pattern arguments as fa_fwd_block_sparse (the lists
+ * must hold distinct blocks, as the forward requires).
+ *   workspace: at least fa_bwd_block_sparse_workspace_size(B,Hq,Nq,Nk,d)
+ *   bytes, 16-byte aligned: delta, then a byte map of the pattern (query
+ *   tiles x key blocks) that the call rebuilds from the lists each time.
+ * A row that sees no key gets dQ = 0; a key that no row sees dK = dV = 0.
+ * Four launches on `stream` (delta, the map, dK/dV, dQ); deterministic.
+ *   d in {64, 128}; ceil(Nq / FA_SPARSE_BLOCK_Q) <= 256 (FA_ERR_UNSUPPORTED
+ *   above: a dK/dV work unit keeps the query tiles it visits in 256 slots).
+ */
+size_t fa_bwd_block_sparse_workspace_size(int B, int Hq, int Nq, int Nk, int d);
+fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse,
+                              void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                              float scale, int causal, const int* q_tile_ptr,
+                              const int* kv_block_idx, int max_blocks_per_tile,
+                              hipStream_t stream);
+
+/*
  * Backward over a packed variable-length batch (the gradients of
  * fa_fwd_varlen, [CH18] §18.7.1 for the packing, §18.4.4 for the gradients):
  * q, o, dout, dq [total_q][Hq][d] and k, v, dk, dv [total_k][Hkv][d], bf16,

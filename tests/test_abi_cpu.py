@@ -255,3 +255,27 @@ def test_block_sparse_validation(lib):
     assert call(mb=257) == fa.FA_ERR_UNSUPPORTED
     assert call(causal=1, Nk=640) == fa.FA_ERR_UNSUPPORTED
     assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_block_sparse_backward_validation(lib):
+    """fa_bwd_block_sparse: the forward's checks, the workspace (delta and the
+    pattern's byte map), and the 256-query-tile bound of the dK/dV units."""
+    need = lib.fa_bwd_block_sparse_workspace_size(1, 2, 512, 640, 128)
+    assert need >= lib.fa_bwd_workspace_size(1, 2, 512, 128) + 2 * 10
+
+    def call(ptr=FAKE, idx=FAKE, mb=8, causal=0, Nq=512, Nk=640, d=128, ws=FAKE, wsb=None):
+        n = need if wsb is None else wsb
+        return lib.fa_bwd_block_sparse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, n,
+                                       1, 2, 2, Nq, Nk, d, 0.1, causal, ptr, idx, mb, None)
+    assert call(ptr=None) == fa.FA_ERR_INVALID_ARG
+    assert call(idx=FAKE + 1) == fa.FA_ERR_INVALID_ARG
+    assert call(mb=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(mb=257) == fa.FA_ERR_UNSUPPORTED
+    assert call(causal=1) == fa.FA_ERR_UNSUPPORTED            # Nq != Nk
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=need - 1) == fa.FA_ERR_WORKSPACE
+    big = 257 * 256
+    nb = lib.fa_bwd_block_sparse_workspace_size(1, 2, big, 640, 128)
+    assert call(Nq=big, wsb=nb) == fa.FA_ERR_UNSUPPORTED
+

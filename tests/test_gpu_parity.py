@@ -339,6 +339,107 @@ def test_block_sparse_config_sampled(fa_gpu):
     assert maxabs(to_f64(lse)[:, :, rows], rl) <= BF16_LSE
 
 
+@pytest.mark.parametrize("shape,causal", [((1, 4, 2, 700, 700, 128), False),
+                                          ((1, 4, 2, 700, 700, 128), True),
+                                          ((2, 2, 1, 513, 600, 64), False),
+                                          ((1, 2, 2, 1100, 1100, 128), True)])
+def test_block_sparse_backward_small(fa_gpu, shape, causal):
+    """Random shuffled lists with empty query tiles and ragged ends (rows that
+    see no key: dQ = 0; keys no row sees: dK = dV = 0), against the oracle."""
+    B, Hq, Hkv, Nq, Nk, d = shape
+    x = gen(B, Hq, Hkv, Nq, Nk, d, "bf16", 103, grad=True)
+    nq, nk = -(-Nq // fa_gpu.SPARSE_BLOCK_Q), -(-Nk // fa_gpu.SPARSE_BLOCK_K)
+    ptr, idx = random_pattern(nq, nk, 11 + Nq)
+    say(f"block-sparse bwd shape={shape} causal={causal} nnz={len(idx)}")
+    pd = torch.tensor(ptr, dtype=torch.int32, device="cuda")
+    idd = torch.tensor(idx if idx else [0], dtype=torch.int32, device="cuda")
+    o, lse = fa_gpu.forward_block_sparse(x["q"], x["k"], x["v"], pd, idd, causal=causal)
+    grads = fa_gpu.backward_block_sparse(x["q"], x["k"], x["v"], o, lse, x["do"], pd, idd,
+                                         causal=causal)
+    torch.cuda.synchronize()
+    ref = A.backward_block_sparse(*(to_f64(x[n]) for n in ("q", "k", "v", "do")),
+                                  1 / math.sqrt(d), ptr, idx, fa_gpu.SPARSE_BLOCK_Q,
+                                  fa_gpu.SPARSE_BLOCK_K, causal)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        g = to_f64(got)
+        assert np.all(np.isfinite(g)), name
+        e = rel_l2(g, want)
+        assert e <= BF16_GRAD, (name, e)
+    ok = A.block_sparse_allowed(Nq, Nk, ptr, idx, fa_gpu.SPARSE_BLOCK_Q, fa_gpu.SPARSE_BLOCK_K,
+                                causal)
+    dq, dk, dv = (to_f64(t) for t in grads)
+    assert not dq[:, :, ~ok.any(axis=1)].any()
+    assert not dk[:, :, ~ok.any(axis=0)].any() and not dv[:, :, ~ok.any(axis=0)].any()
+
+
+def test_block_sparse_backward_rows_without_keys(fa_gpu):
+    """Causal pattern whose first query tile lists only a later key block:
+    rows before that block see nothing (LSE = -inf) and must get dQ = 0 with
+    no NaN, while the block's keys still get gradients from later rows."""
+    N, d = 700, 128
+    x = gen(1, 2, 2, N, N, d, "bf16", 104, grad=True)
+    ptr, idx = [0, 1, 3, 5], [2, 0, 5, 8, 10]     # tile 0 -> keys 128..191 only
+    pd = torch.tensor(ptr, dtype=torch.int32, device="cuda")
+    idd = torch.tensor(idx, dtype=torch.int32, device="cuda")
+    say("block-sparse bwd rows without keys")
+    o, lse = fa_gpu.forward_block_sparse(x["q"], x["k"], x["v"], pd, idd, causal=True)
+    grads = fa_gpu.backward_block_sparse(x["q"], x["k"], x["v"], o, lse, x["do"], pd, idd,
+                                         causal=True)
+    torch.cuda.synchronize()
+    assert np.isneginf(to_f64(lse)[0, 0, 0])
+    ref = A.backward_block_sparse(*(to_f64(x[n]) for n in ("q", "k", "v", "do")),
+                                  1 / math.sqrt(d), ptr, idx, 256, 64, True)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        g = to_f64(got)
+        assert np.all(np.isfinite(g)), name
+        assert rel_l2(g, want) <= BF16_GRAD, name
+    assert not to_f64(grads[0])[:, :, :128].any()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_backward_all_blocks_equals_dense(fa_gpu, causal):
+    """Every key block listed in ascending order: dQ visits the same tiles in
+    the same order as the dense kernel, and every dK/dV unit the same query
+    tiles, so the gradients agree bit for bit."""
+    N = 1000
+    x = gen(2, 4, 2, N, N, 128, "bf16", 105, grad=True)
+    nq, nk = -(-N // fa_gpu.SPARSE_BLOCK_Q), -(-N // fa_gpu.SPARSE_BLOCK_K)
+    pd = torch.tensor([t * nk for t in range(nq + 1)], dtype=torch.int32, device="cuda")
+    idd = torch.tensor(list(range(nk)) * nq, dtype=torch.int32, device="cuda")
+    say(f"block-sparse bwd all blocks causal={causal}")
+    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=causal)
+    gs = fa_gpu.backward_block_sparse(x["q"], x["k"], x["v"], o, lse, x["do"], pd, idd,
+                                      causal=causal)
+    gd = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip(gs, gd):
+        assert torch.equal(a, b)
+
+
+def test_block_sparse_backward_config_sampled(fa_gpu):
+    """The local + global pattern at B=2 H=16 N=8192 d=128, in the
+    benchmark's launch configuration: complete gradients of two heads
+    against the oracle (its backward restricted to one head)."""
+    from workloads import SPARSE
+    w = SPARSE["sparse_bf16"]
+    x = {n: t.cuda() for n, t in make_inputs(w).items()}
+    ptr, idx = w.pattern()
+    pd = torch.tensor(ptr, dtype=torch.int32, device="cuda")
+    idd = torch.tensor(idx, dtype=torch.int32, device="cuda")
+    say("block-sparse backward full size")
+    o, lse = fa_gpu.forward_block_sparse(x["q"], x["k"], x["v"], pd, idd)
+    dq, dk, dv = fa_gpu.backward_block_sparse(x["q"], x["k"], x["v"], o, lse, x["do"], pd, idd)
+    torch.cuda.synchronize()
+    dq, dk, dv = to_f64(dq), to_f64(dk), to_f64(dv)
+    for b, h in ((0, 0), (1, 15)):
+        one = [to_f64(x[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v", "do")]
+        rq, rk, rv = A.backward_block_sparse(*one, w.scale, ptr, idx, w.block_q, w.block_k)
+        for name, got, want in (("dq", dq[b, h], rq[0, 0]), ("dk", dk[b, h], rk[0, 0]),
+                                ("dv", dv[b, h], rv[0, 0])):
+            e = rel_l2(got, want)
+            assert e <= BF16_GRAD, (b, h, name, e)
+
+
 # ------------------------------------------------------------------- decode
 
 def check_decode(fa, B, Hq, Hkv, Nk, d, splits, seed):

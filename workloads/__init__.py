@@ -304,5 +304,5 @@ class BlockSparse(Workload):
 
 SPARSE = {
     "sparse_bf16": BlockSparse("sparse_bf16", 2, 16, 16, 8192, 8192, 128, "bf16", causal=False,
-                               seed=8309),
+                               backward=True, seed=8309),
 }
