@@ -59,11 +59,26 @@ __global__ __launch_bounds__(128) void quantize_fp8_kernel(const uint16_t* __res
   const uint16_t* xp = X + ((size_t)bh * N + r0) * D;
   uint8_t* yp = X8 + ((size_t)bh * N + r0) * D;
 
-  // coalesced block load: 16 chunks of 16 bytes per row
-  for (int c = tid; c < kQBlk * 16; c += 128) {
+  // Coalesced block load, 16 chunks of 16 bytes per row, and the sign vector:
+  // every load of the thread is issued before the first is used, so the
+  // block's 32 KB are in flight together.
+  constexpr int NLD = kQBlk * 16 / 128;
+  u32x4 ld[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int c = tid + i * 128;
     const int r = c >> 4, col = c & 15;
-    u32x4 v = r < rows ? ldg<u32x4>(xp + (size_t)r * D + col * 8) : u32x4{0, 0, 0, 0};
-    lds_write<u32x4>(stage, r * IP + col * 16, v);
+    ld[i] = r < rows ? ldg<u32x4>(xp + (size_t)r * D + col * 8) : u32x4{0, 0, 0, 0};
+  }
+  u32x4 sg[D / 16];
+  if (signs) {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) sg[i] = ldg<u32x4>(signs + 16 * i);
+  }
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int c = tid + i * 128;
+    lds_write<u32x4>(stage, (c >> 4) * IP + (c & 15) * 16, ld[i]);
   }
   __syncthreads();
 
@@ -79,7 +94,10 @@ __global__ __launch_bounds__(128) void quantize_fp8_kernel(const uint16_t* __res
   }
   if (signs) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) x[i] = signs[i] < 0 ? -x[i] : x[i];
+    for (int i = 0; i < D; ++i) {
+      const int8_t sgn = (int8_t)(sg[i / 16][(i / 4) % 4] >> (8 * (i % 4)));
+      x[i] = sgn < 0 ? -x[i] : x[i];
+    }
     // natural-order fast Walsh-Hadamard transform (Sylvester H_128)
 #pragma unroll
     for (int len = 1; len < D; len <<= 1)
