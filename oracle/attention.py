@@ -142,6 +142,19 @@ def head_backward(q, k, v, do, scale, causal, window=None):
     return dq, dk, dv, delta
 
 
+def head_dq_rows(q, k, v, do, scale, causal, rows):
+    """dQ of the listed query rows of one head, row by row ([CH18] §18.2.4
+    (2) restricted to row i: P_i = softmax of row i's visible scores,
+    dP_i = dO_i V^T, dS_i = P_i * (dP_i - sum(P_i * dP_i)), dQ_i = scale dS_i K),
+    for sizes where the whole matrices do not fit.  q/do [Nq][d], k/v [Nk][d]."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    r = np.asarray(rows)
+    s = scores(q, k, scale, causal, rows=r)
+    p, _, _ = softmax_rows(s)
+    dp = do[r] @ v.T
+    return scale * (softmax_backward(p, dp) @ k)
+
+
 def backward(q, k, v, do, scale, causal=False, window=None):
     """Batched backward -> (dQ, dK, dV) fp64.  A KV head's gradient is the sum
     over the query heads that read it (GQA broadcast, [CH18] §18.2.2)."""

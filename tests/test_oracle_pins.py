@@ -195,6 +195,27 @@ def test_backward_finite_differences(causal, N):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_match_finite_differences(causal):
+    """The row-by-row dQ (for sizes where whole matrices do not fit) against
+    central differences of L = sum(O * G) with respect to the listed rows of Q."""
+    N, d, scale, h = 7, 3, 0.8, 1e-6
+    q, k, v, g = rnd(N, d), rnd(N, d), rnd(N, d), rnd(N, d)
+    rows = [0, 3, 6]
+    got = A.head_dq_rows(q, k, v, g, scale, causal, rows)
+
+    def loss(q_):
+        return float((A.head_forward(q_, k, v, scale, causal)[0] * g).sum())
+
+    for a, i in enumerate(rows):
+        for c in range(d):
+            qp, qm = q.copy(), q.copy()
+            qp[i, c] += h
+            qm[i, c] -= h
+            num = (loss(qp) - loss(qm)) / (2 * h)
+            assert abs(num - got[a, c]) <= 1e-7 * max(1.0, abs(num))
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_backward_matches_torch_autograd_fp64(causal):
     B, Hq, Hkv, N, d, scale = 2, 4, 2, 33, 16, 0.25
     q, k, v, g = rnd(B, Hq, N, d), rnd(B, Hkv, N, d), rnd(B, Hkv, N, d), rnd(B, Hq, N, d)
