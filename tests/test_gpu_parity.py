@@ -166,6 +166,34 @@ def test_causal_config_sampled(fa_gpu):
             assert e <= BF16_GRAD, (b, h, name, e)
 
 
+def test_long_sequence_causal(fa_gpu):
+    """N = 65536 (eight times the benchmark length; GQA 2:1, d = 128, causal):
+    sampled forward rows and dQ rows against the oracle row by row, and two
+    identities that hold at any size and test every dK and dV: the keys' dK
+    sum to zero (each row of dS sums to zero) and the keys' dV sum to the
+    sum of dO over the query rows and heads (each row of P sums to one)."""
+    N, d = 65536, 128
+    x = gen(1, 2, 1, N, N, d, "bf16", 95, grad=True)
+    say("long sequence N=65536 forward")
+    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=True)
+    say("long sequence N=65536 backward")
+    dq, dk, dv = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=True)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    rows = np.array([0, 1, 255, 256, 12345, 32767, 40000, 65535])
+    ro, rl = A.forward(q, k, v, scale, True, rows=rows)
+    assert maxabs(to_f64(o)[:, :, rows], ro) <= BF16_O
+    assert maxabs(to_f64(lse)[:, :, rows], rl) <= BF16_LSE
+    dq = to_f64(dq)
+    for h in range(2):
+        want = A.head_dq_rows(q[0, h], k[0, 0], v[0, 0], do[0, h], scale, True, rows)
+        assert rel_l2(dq[0, h, rows], want) <= BF16_GRAD, h
+    dk, dv = to_f64(dk)[0, 0], to_f64(dv)[0, 0]
+    assert rel_l2(dv.sum(axis=0), do[0].sum(axis=(0, 1))) <= BF16_GRAD
+    assert np.linalg.norm(dk.sum(axis=0)) <= 2e-2 * np.linalg.norm(dk)
+
+
 def test_backward_is_deterministic(fa_gpu):
     """No atomics and a fixed accumulation order: repeated backward passes
     (plain and windowed, GQA, causal) give bit-identical gradients."""
