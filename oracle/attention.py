@@ -203,6 +203,36 @@ def decode_split(q, k, v, scale, num_splits):
     return o[:, :, None, :], lse[:, :, None], o_parts, lse_parts
 
 
+def decode_multi(q, k, v, scale, causal=False):
+    """Decode with a few query tokens against a long KV ([L21] slides 57-60:
+    decode queries are a few tokens against contexts up to 128k, and GQA
+    packing extends from one query token to any number).  The Nq
+    queries are the newest positions of each sequence, so with ``causal``
+    token t (0-based among the Nq) sees keys j <= Nk - Nq + t (the mask is
+    aligned to the end of the keys); without it every token sees all keys.
+    q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] -> O [B][Hq][Nq][d], LSE
+    [B][Hq][Nq] in fp64 (plain definition, no splitting)."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    assert Nq <= Nk
+    o = np.empty((B, Hq, Nq, v.shape[-1]))
+    lse = np.empty((B, Hq, Nq))
+    vis = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        vis = np.arange(Nk)[None, :] <= (Nk - Nq + np.arange(Nq))[:, None]
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head(h, Hq, Hkv)
+            s = np.where(vis, scale * (q[b, h] @ k[b, hk].T), -np.inf)
+            p, m, l = softmax_rows(s)
+            o[b, h] = p @ v[b, hk]
+            lse[b, h] = m + np.log(l)
+    return o, lse
+
+
 def combine(o_parts, lse_parts):
     """Merge split partials with their log-sum-exp weights ([CH18] §18.8.2 (2),
     the reduction step).  o_parts [..][S][d], lse_parts [..][S]."""

@@ -425,6 +425,51 @@ def test_flop_formula_against_table_18_5():
         assert w.bwd_flops() == 2.5 * w.fwd_flops()
 
 
+# ------------------------------------------------------- multi-token decode
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_multi_uniform_scores(causal):
+    """Closed form: Q = 0 makes token t the mean of the V rows it sees, rows
+    0 .. Nk-Nq+t when causal (all Nk otherwise), with LSE = ln(count)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 3, 11, 5
+    q = np.zeros((B, Hq, Nq, d))
+    k, v = rnd(B, Hkv, Nk, d), rnd(B, Hkv, Nk, d)
+    o, lse = A.decode_multi(q, k, v, 0.9, causal)
+    for h in range(Hq):
+        for t in range(Nq):
+            cnt = Nk - Nq + t + 1 if causal else Nk
+            assert np.allclose(o[0, h, t], v[0, h // 2, :cnt].mean(axis=0), atol=1e-13)
+            assert abs(lse[0, h, t] - math.log(cnt)) < 1e-13
+
+
+def test_decode_multi_special_cases():
+    """One token: causal or not, it is the single-query decode (the forward
+    with Nq = 1).  Nq = Nk: the end-aligned causal mask is the top-left one,
+    so it is the causal forward.  Scalar loops for a general case."""
+    B, Hq, Hkv, Nk, d, sc = 2, 2, 1, 9, 4, 0.5
+    k, v = rnd(B, Hkv, Nk, d), rnd(B, Hkv, Nk, d)
+    q1 = rnd(B, Hq, 1, d)
+    for causal in (False, True):
+        o, l = A.decode_multi(q1, k, v, sc, causal)
+        of, lf = A.forward(q1, k, v, sc, False)
+        assert np.allclose(o, of, atol=1e-14) and np.allclose(l, lf, atol=1e-14)
+    qn = rnd(B, Hq, Nk, d)
+    o, l = A.decode_multi(qn, k, v, sc, True)
+    of, lf = A.forward(qn, k, v, sc, True)
+    assert np.allclose(o, of, atol=1e-14) and np.allclose(l, lf, atol=1e-14)
+    Nq = 3
+    q = rnd(B, Hq, Nq, d)
+    o, l = A.decode_multi(q, k, v, sc, True)
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(Nq):
+                w = [math.exp(sc * float(q[b, h, t] @ k[b, 0, j])) if j <= Nk - Nq + t else 0.0
+                     for j in range(Nk)]
+                w = np.array(w)
+                assert np.allclose(o[b, h, t], (w[:, None] * v[b, 0]).sum(0) / w.sum(), atol=1e-12)
+                assert abs(l[b, h, t] - math.log(w.sum())) < 1e-12
+
+
 # ---------------------------------------------------------------- varlen pins
 
 def _pack_lengths(lens):
