@@ -265,7 +265,30 @@ def main(argv=None):
                            "GB/s": round(gbs, 1), "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
                            "split_GB/s": round(nbytes / (t_split * 1e-3) / 1e9, 1)}
         log(f"decode {t_all:.3f} ms {gbs:.0f} GB/s (split {t_split:.3f} ms)")
-        del xd, od, ld, opart, lpart
+        # the same KV with 4 query tokens per head (causal, end-aligned): 16
+        # columns of each tile instead of 4, the same K/V bytes
+        NQ = 4
+        qt = torch.randn(wd.B, wd.Hq, NQ, wd.d, device="cuda").to(torch.bfloat16)
+        ot = torch.empty_like(qt)
+        lt = torch.empty(wd.B, wd.Hq, NQ, dtype=torch.float32, device="cuda")
+        opt = torch.empty(wd.B, wd.Hq, NQ, S, wd.d, dtype=torch.float32, device="cuda")
+        lpt = torch.empty(wd.B, wd.Hq, NQ, S, dtype=torch.float32, device="cuda")
+
+        def tokens():
+            fa.fa_decode_splitkv_q(qt, xd["k"], xd["v"], opt, lpt, wd.B, wd.Hq, wd.Hkv, NQ, wd.Nk,
+                                   wd.d, wd.scale, True, S, sh)
+            fa.fa_decode_combine(opt, lpt, ot, lt, wd.B, wd.Hq * NQ, wd.d, S, sh)
+
+        tokens()
+        t_tok = timed(tokens, iters, stream)
+        nb_tok = (2 * wd.B * wd.Hkv * wd.Nk * wd.d * 2 + 2 * wd.B * wd.Hq * NQ * wd.d * 2
+                  + wd.B * wd.Hq * NQ * 4)
+        gbs_tok = nb_tok / (t_tok * 1e-3) / 1e9
+        parts["decode_tokens"] = {"ms": round(t_tok, 4), "tokens": NQ, "causal": True,
+                                  "algorithmic_bytes": nb_tok, "GB/s": round(gbs_tok, 1),
+                                  "frac_peak": round(gbs_tok / PEAK_HBM_GBS, 4)}
+        log(f"decode {NQ} tokens {t_tok:.3f} ms {gbs_tok:.0f} GB/s")
+        del xd, od, ld, opart, lpart, qt, ot, lt, opt, lpt
 
     if not only or "window" in only:
         from workloads import WINDOWED

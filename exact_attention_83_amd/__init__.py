@@ -42,6 +42,7 @@ _SIGS = {
     "fa_bwd_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                         _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_decode_splitkv_q": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_decode_splitkv_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                      _I, _F, _I, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -180,6 +181,12 @@ def fa_decode_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nk, d, scale, num_s
                       stream=None):
     _call("fa_decode_splitkv", _ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, Hq,
           Hkv, Nk, d, scale, num_splits, _stream(stream))
+
+
+def fa_decode_splitkv_q(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                        num_splits, stream=None):
+    _call("fa_decode_splitkv_q", _ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, Hq,
+          Hkv, Nq, Nk, d, scale, int(causal), num_splits, _stream(stream))
 
 
 def fa_decode_splitkv_paged(q, k_cache, v_cache, block_table, seqlens, o_part, lse_part, B, Hq,
@@ -328,6 +335,26 @@ def decode(q, k, v, num_splits, scale=None, stream=None, return_partials=False):
     fa_decode_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nk, d, s, num_splits, stream)
     fa_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream)
     assert rows == o_part.shape[0] * o_part.shape[1] * o_part.shape[2]
+    if return_partials:
+        return o, lse, o_part, lse_part
+    return o, lse
+
+
+def decode_tokens(q, k, v, num_splits, causal=False, scale=None, stream=None,
+                  return_partials=False):
+    """Split-KV decode of a few query tokens: q [B][Hq][Nq][d] (the newest Nq
+    positions), k/v [B][Hkv][Nk][d] -> (O [B][Hq][Nq][d], LSE [B][Hq][Nq])."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    s = _default_scale(d, scale)
+    o_part = torch.empty((B, Hq, Nq, num_splits, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((B, Hq, Nq, num_splits), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    fa_decode_splitkv_q(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, s, causal, num_splits,
+                        stream)
+    fa_decode_combine(o_part, lse_part, o, lse, B, Hq * Nq, d, num_splits, stream)
     if return_partials:
         return o, lse, o_part, lse_part
     return o, lse

@@ -341,6 +341,24 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v, float* 
                                             num_splits, stream));
 }
 
+fa_status fa_decode_splitkv_q(const void* q, const void* k, const void* v, float* o_part,
+                              float* lse_part, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                              float scale, int causal, int num_splits, hipStream_t stream) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) ||
+      !aligned16(lse_part))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (Nq > Nk) return FA_ERR_INVALID_ARG;
+  if (num_splits <= 0 || num_splits > Nk || Nk % num_splits != 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // the group's heads times the tokens fill at most the 32 columns of a tile
+  if ((int64_t)(Hq / Hkv) * Nq > 32) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv * num_splits > (int64_t)1 << 30) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_decode_split(q, k, v, o_part, lse_part, B, Hq, Hkv, Nk, d, scale,
+                                            num_splits, stream, Nq, causal != 0));
+}
+
 fa_status fa_decode_splitkv_paged(const void* q, const void* k_cache, const void* v_cache,
                                   const int* block_table, const int* seqlens, float* o_part,
                                   float* lse_part, int B, int Hq, int Hkv, int num_pages,

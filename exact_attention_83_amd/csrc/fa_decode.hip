@@ -7,8 +7,9 @@
 // head fill the rows of one tile, so K and V are streamed once per group).
 //
 // Split kernel, one workgroup (4 waves) per (b, KV head, chunk):
-//   * the G = Hq/Hkv query heads of the group are the n axis of S^T = K Q^T on
-//     the 32x32x16 MFMA (n = 32 >= G; columns past G hold zero queries).
+//   * the G = Hq/Hkv query heads of the group, times the Nq query tokens, are
+//     the n axis of S^T = K Q^T on the 32x32x16 MFMA (column n = g*Nq + t; n =
+//     32 >= G*Nq; the columns past it hold zero queries).
 //   * each wave streams 32-key blocks of the chunk (blocks w, w+4, ...): K
 //     goes from global memory straight into A-operand registers (each lane
 //     reads 128 contiguous bytes of one key row; the head-dim order inside a
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ V, float* __restrict__ o_part, float* __restrict__ lse_part,
     int Hq, int Hkv, int Nk, int num_splits, float scale, float scale_log2,
     const int* __restrict__ table, const int* __restrict__ seqlens, int page_shift,
-    int max_pages, int num_pages, int chunk) {
+    int max_pages, int num_pages, int chunk, int Nq = 1, int causal = 0) {
   constexpr int KS = D / 16;      // k-steps over the head dim
   constexpr int DBLK = D / 32;
   constexpr int DCH = D / 8;      // 16-byte chunks per row
@@ -60,6 +61,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int l32 = lane & 31;
   const int hf = lane >> 5;
   const int G = Hq / Hkv;
+  // Columns of the n axis in use: the G heads of the group times the Nq query
+  // tokens, column n = g * Nq + t (<= 32, checked on the host).
+  const int NC = G * Nq;
 
   const int c = blockIdx.x % num_splits;
   const int bhk = blockIdx.x / num_splits;
@@ -69,8 +73,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int key_begin = c * L;
   // (paged: the length is clamped to what the table can address and page ids
   // to the cache, so bad table data reads wrong rows but never out of bounds)
-  const int key_end =
-      PAGED ? min(key_begin + L, min(seqlens[b], max_pages << page_shift)) : key_begin + L;
+  // this entry's key count and the end of this chunk's keys
+  const int kv_len = PAGED ? min(seqlens[b], max_pages << page_shift) : Nk;
+  const int key_end = PAGED ? min(key_begin + L, kv_len) : key_begin + L;
 
   const uint16_t* Kp = PAGED ? K : K + (size_t)bhk * Nk * D;
   const uint16_t* Vp = PAGED ? V : V + (size_t)bhk * Nk * D;
@@ -94,8 +99,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   // k-step ks, element i of lane half hf is head dim hf*HALF + ks*8 + i.
   u32x4 qf[KS];
   {
-    const bool valid = l32 < G;
-    const uint16_t* qp = Q + ((size_t)b * Hq + hk * G + (valid ? l32 : 0)) * D;
+    const bool valid = l32 < NC;
+    const uint16_t* qp = Q + (((size_t)b * Hq + hk * G) * Nq + (valid ? l32 : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 x = ldg<u32x4>(qp + hf * HALF + ks * 8);
@@ -163,6 +168,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
       for (int r = 0; r < 16; ++r)
         if (k0 + 8 * (r >> 2) + 4 * hf + (r & 3) >= key_end) s[r] = -INFINITY;
     }
+    // Several query tokens, causal: they are the newest Nq positions, so token
+    // t sees keys up to kv_len - Nq + t (a mask aligned to the end of the keys).
+    if (causal && k0 + kDecBlk - 1 > kv_len - Nq) {
+      const int lim = kv_len - Nq + l32 % Nq;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k0 + 8 * (r >> 2) + 4 * hf + (r & 3) > lim) s[r] = -INFINITY;
+    }
     float mt = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
@@ -210,14 +223,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   // the merged max and sum, then the waves add into one LDS buffer in a fixed
   // order (deterministic).
   const float l_tot = l_run + xor32(l_run);
-  if (l32 < G && hf == 0) {
+  if (l32 < NC && hf == 0) {
     red_m[wave][l32] = m_run;
     red_l[wave][l32] = l_tot;
   }
   __syncthreads();
   float M = -INFINITY;
   float Lsum = 0.f;
-  if (l32 < G) {
+  if (l32 < NC) {
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red_m[w][l32]);
     const float Mr = M == -INFINITY ? 0.f : M;
@@ -231,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   }
 #pragma unroll
   for (int w = 0; w < kDecWaves; ++w) {
-    if (wave == w && l32 < G) {
+    if (wave == w && l32 < NC) {
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -242,13 +255,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     }
     __syncthreads();
   }
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int g = idx / D, dd = idx - (idx / D) * D;
-    const size_t row = ((size_t)b * Hq + hk * G + g) * num_splits + c;
-    o_part[row * D + dd] = red_o[g][dd];
+  // rows of the partials: ((b*Hq + h) * Nq + t) * num_splits + c, and the
+  // group's rows are consecutive: (b*Hq + hk*G) * Nq + n
+  for (int idx = tid; idx < NC * D; idx += 256) {
+    const int n = idx / D, dd = idx - (idx / D) * D;
+    const size_t row = (((size_t)b * Hq + hk * G) * Nq + n) * num_splits + c;
+    o_part[row * D + dd] = red_o[n][dd];
   }
-  if (wave == 0 && hf == 0 && l32 < G) {
-    const size_t row = ((size_t)b * Hq + hk * G + l32) * num_splits + c;
+  if (wave == 0 && hf == 0 && l32 < NC) {
+    const size_t row = (((size_t)b * Hq + hk * G) * Nq + l32) * num_splits + c;
     lse_part[row] = Lsum > 0.f ? M * scale + __logf(Lsum) : -INFINITY;
   }
 }
@@ -322,17 +337,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
                                float* lse_part, int B, int Hq, int Hkv, int Nk, int d,
-                               float scale, int num_splits, hipStream_t stream) {
+                               float scale, int num_splits, hipStream_t stream, int Nq,
+                               bool causal) {
   dim3 grid(B * Hkv * num_splits), block(256);
   const float sl2 = scale * kLog2e;
   if (d == 128)
     hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, block, 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part,
-                       lse_part, Hq, Hkv, Nk, num_splits, scale, sl2, nullptr, nullptr, 0, 0, 0, 0);
+                       lse_part, Hq, Hkv, Nk, num_splits, scale, sl2, nullptr, nullptr, 0, 0, 0, 0,
+                       Nq, causal ? 1 : 0);
   else
     hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, block, 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, o_part,
-                       lse_part, Hq, Hkv, Nk, num_splits, scale, sl2, nullptr, nullptr, 0, 0, 0, 0);
+                       lse_part, Hq, Hkv, Nk, num_splits, scale, sl2, nullptr, nullptr, 0, 0, 0, 0,
+                       Nq, causal ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -60,9 +60,12 @@ hipError_t launch_bwd_bf16_sparse(const void* q, const void* k, const void* v, c
                                   int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                                   bool causal, hipStream_t stream);
 
+// Nq query tokens per (b, head) ([B][Hq][Nq][d]; G*Nq <= 32), partials
+// [B][Hq][Nq][S][d] / [B][Hq][Nq][S]; causal: token t sees keys <= Nk-Nq+t.
 hipError_t launch_decode_split(const void* q, const void* k, const void* v, float* o_part,
                                float* lse_part, int B, int Hq, int Hkv, int Nk, int d,
-                               float scale, int num_splits, hipStream_t stream);
+                               float scale, int num_splits, hipStream_t stream, int Nq = 1,
+                               bool causal = false);
 hipError_t launch_decode_split_paged(const void* q, const void* k_cache, const void* v_cache,
                                      const int* block_table, const int* seqlens, float* o_part,
                                      float* lse_part, int B, int Hq, int Hkv, int page_shift,

@@ -283,6 +283,31 @@ fa_status fa_decode_splitkv(const void* q, const void* k, const void* v,
                             float scale, int num_splits, hipStream_t stream);
 
 /*
+ * Split-KV decode with a few query tokens ([L21] slides 57-60: decode
+ * queries are a few tokens against a long context, and GQA packing extends
+ * from one query token to any number): the Hq/Hkv heads of a group times the
+ * Nq tokens are packed into the columns of one tile, so K and V are still
+ * read once per group.  The tokens are the newest Nq positions of each
+ * sequence: with causal, token t (0-based) sees keys 0 .. Nk-Nq+t (a mask
+ * aligned to the end of the keys; Nq == Nk gives the causal forward's mask);
+ * without it every token sees all Nk keys.
+ *   q [B][Hq][Nq][d] bf16; k,v [B][Hkv][Nk][d] bf16.
+ *   o_part [B][Hq][Nq][num_splits][d] fp32, lse_part [B][Hq][Nq][num_splits]
+ *   fp32 (as for fa_decode_splitkv, one row per (b, hq, token)); a chunk
+ *   whose keys a token cannot see gets O_c = 0 and lse_c = -inf.
+ * Combine with fa_decode_combine(o_part, lse_part, o, lse, B, Hq * Nq, d,
+ * num_splits): o [B][Hq][Nq][d], lse [B][Hq][Nq].  fa_decode_workspace_size
+ * (B, Hq * Nq, d, num_splits) sizes the partials.
+ * Requirements: 1 <= Nq <= Nk; num_splits >= 1 divides Nk; d in {64, 128};
+ * (Hq/Hkv) * Nq <= 32 (FA_ERR_UNSUPPORTED above).  Nq == 1 is exactly
+ * fa_decode_splitkv.
+ */
+fa_status fa_decode_splitkv_q(const void* q, const void* k, const void* v,
+                              float* o_part, float* lse_part,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                              float scale, int causal, int num_splits, hipStream_t stream);
+
+/*
  * Split-KV decode over a paged KV cache ([CH18] §18.8.2 (3): Flash-Decoding
  * combined with a paged cache; §18.8.3 (1): the cache lives in fixed-size
  * physical pages and each request's page table maps its logical block j to a

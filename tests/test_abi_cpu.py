@@ -279,3 +279,19 @@ def test_block_sparse_backward_validation(lib):
     nb = lib.fa_bwd_block_sparse_workspace_size(1, 2, big, 640, 128)
     assert call(Nq=big, wsb=nb) == fa.FA_ERR_UNSUPPORTED
 
+
+def test_decode_tokens_validation(lib):
+    """fa_decode_splitkv_q: token count against the keys, splits, the 32
+    columns of a tile (group size x tokens), head dims."""
+    def call(B=2, Hq=8, Hkv=2, Nq=4, Nk=128, d=128, S=4, q=FAKE):
+        return lib.fa_decode_splitkv_q(q, FAKE, FAKE, FAKE, FAKE, B, Hq, Hkv, Nq, Nk, d, 0.1, 1,
+                                       S, None)
+    assert call(q=MIS) == fa.FA_ERR_INVALID_ARG
+    assert call(Nq=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Nq=129) == fa.FA_ERR_INVALID_ARG
+    assert call(S=3) == fa.FA_ERR_INVALID_ARG
+    assert call(S=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Hq=7) == fa.FA_ERR_INVALID_ARG
+    assert call(Nq=9) == fa.FA_ERR_UNSUPPORTED          # 4 heads x 9 tokens > 32
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+

@@ -490,6 +490,63 @@ def test_decode_small(fa_gpu, cfg):
     check_decode(fa_gpu, *cfg, seed=41)
 
 
+@pytest.mark.parametrize("cfg", [
+    # B, Hq, Hkv, Nq, Nk, d, splits
+    (2, 8, 2, 4, 4096, 128, 8),     # 4 heads x 4 tokens
+    (1, 32, 4, 4, 2000, 128, 10),   # 8 heads x 4 tokens = 32 columns, ragged chunks of 200
+    (2, 4, 4, 32, 640, 64, 5),      # one head x 32 tokens, d = 64
+    (1, 6, 2, 7, 96, 128, 3),       # 3 heads x 7 tokens, the mask crosses chunks
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_tokens(fa_gpu, cfg, causal):
+    """A few query tokens per head (the newest positions) against the keys,
+    with and without the end-aligned causal mask, against the oracle."""
+    B, Hq, Hkv, Nq, Nk, d, splits = cfg
+    x = gen(B, Hq, Hkv, Nq, Nk, d, "bf16", 43)
+    say(f"decode tokens B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} splits={splits} "
+        f"causal={causal}")
+    o, lse = fa_gpu.decode_tokens(x["q"], x["k"], x["v"], splits, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = A.decode_multi(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), 1 / math.sqrt(d),
+                            causal)
+    assert maxabs(to_f64(o), ro) <= BF16_O
+    assert maxabs(to_f64(lse), rl) <= BF16_LSE
+
+
+def test_decode_tokens_one_token_is_decode(fa_gpu):
+    """Nq = 1 runs the single-token decode's arithmetic: bit-identical."""
+    x = gen(2, 8, 2, 1, 4096, 128, "bf16", 44)
+    say("decode tokens Nq=1 vs decode")
+    a = fa_gpu.decode_tokens(x["q"], x["k"], x["v"], 8, causal=True)
+    b = fa_gpu.decode(x["q"], x["k"], x["v"], 8)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_tokens_config_sampled(fa_gpu):
+    """The decode workload's KV (B=8 Hkv=8, 131072 keys, d=128, 64 splits)
+    with 4 causal query tokens per head (Hq=32: 16 columns per tile): every
+    output against the oracle."""
+    w = WORKLOADS["decode_gqa"]
+    g = torch.Generator("cuda").manual_seed(45)
+    k = torch.randn(w.B, w.Hkv, w.Nk, w.d, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(w.B, w.Hkv, w.Nk, w.d, device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn(w.B, w.Hq, 4, w.d, device="cuda", generator=g).to(torch.bfloat16)
+    say("decode tokens full size")
+    o, lse = fa_gpu.decode_tokens(q, k, v, 64, causal=True)
+    torch.cuda.synchronize()
+    o, lse, qh = to_f64(o), to_f64(lse), to_f64(q)
+    G = w.Hq // w.Hkv
+    for b in range(w.B):   # the oracle widens one (b, KV head) slab at a time
+        for hk in range(w.Hkv):
+            kk = k[b:b + 1, hk:hk + 1].float().cpu().numpy()
+            vv = v[b:b + 1, hk:hk + 1].float().cpu().numpy()
+            hs = slice(hk * G, (hk + 1) * G)
+            ro, rl = A.decode_multi(qh[b:b + 1, hs], kk, vv, w.scale, True)
+            assert maxabs(o[b:b + 1, hs], ro) <= BF16_O, (b, hk)
+            assert maxabs(lse[b:b + 1, hs], rl) <= BF16_LSE, (b, hk)
+
+
 def test_decode_split_count_invariance(fa_gpu):
     x = gen(2, 8, 2, 1, 8192, 128, "bf16", 42)
     outs = []
