@@ -338,6 +338,25 @@ def decode_paged(q, k_cache, v_cache, block_table, seqlens, scale):
     return o, lse
 
 
+def decode_paged_multi(q, k_cache, v_cache, block_table, seqlens, scale, causal=False):
+    """decode_multi over a paged KV cache: entry b's keys are the logical rows
+    0 .. seqlens[b]-1 gathered through block_table[b] (as in decode_paged),
+    and its Nq query tokens are the newest positions (each seqlens[b] >= Nq).
+    q [B][Hq][Nq][d] -> O [B][Hq][Nq][d], LSE [B][Hq][Nq] (fp64)."""
+    q = _f64(q)
+    B, Hq, Nq, d = q.shape
+    Hkv = k_cache.shape[2]
+    o = np.empty((B, Hq, Nq, v_cache.shape[-1]))
+    lse = np.empty((B, Hq, Nq))
+    for b in range(B):
+        n = int(seqlens[b])
+        assert n >= Nq
+        kb = np.stack([gather_pages(k_cache, block_table[b], n, hk) for hk in range(Hkv)])[None]
+        vb = np.stack([gather_pages(v_cache, block_table[b], n, hk) for hk in range(Hkv)])[None]
+        o[b:b + 1], lse[b:b + 1] = decode_multi(q[b:b + 1], kb, vb, scale, causal)
+    return o, lse
+
+
 def block_sparse_allowed(Nq, Nk, q_ptr, kv_idx, block_q, block_k, causal=False):
     """Boolean [Nq][Nk] mask of a block-sparse pattern ([CH18] §18.8.1: query
     block i attends only to the key blocks kv_idx[q_ptr[i] .. q_ptr[i+1]-1];

@@ -470,6 +470,29 @@ def test_decode_multi_special_cases():
                 assert abs(l[b, h, t] - math.log(w.sum())) < 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_paged_multi_uniform_scores(causal):
+    """Closed form through the page table: Q = 0 makes token t of entry b the
+    mean of its logical V rows 0 .. seqlen-Nq+t (all seqlen rows when not
+    causal), with LSE = ln(count); the pages are randomly permuted."""
+    page, Hkv, Hq, d, Nq = 4, 2, 4, 3, 3
+    lens = [9, 14]
+    npages = 10
+    cache_k, cache_v = rnd(npages, page, Hkv, d), rnd(npages, page, Hkv, d)
+    perm = rng.permutation(npages)
+    table = np.stack([perm[:4], perm[4:8]])
+    q = np.zeros((2, Hq, Nq, d))
+    o, lse = A.decode_paged_multi(q, cache_k, cache_v, table, lens, 0.7, causal)
+    for b, n in enumerate(lens):
+        for h in range(Hq):
+            hk = h // 2
+            rows = np.stack([cache_v[table[b][j // page], j % page, hk] for j in range(n)])
+            for t in range(Nq):
+                cnt = n - Nq + t + 1 if causal else n
+                assert np.allclose(o[b, h, t], rows[:cnt].mean(axis=0), atol=1e-13)
+                assert abs(lse[b, h, t] - math.log(cnt)) < 1e-13
+
+
 # ---------------------------------------------------------------- varlen pins
 
 def _pack_lengths(lens):
