@@ -43,6 +43,8 @@ _SIGS = {
                         _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv_q": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_decode_splitkv_paged_q": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       _I, _I, _I, _F, _I, _I, _P]),
     "fa_decode_splitkv_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                      _I, _F, _I, _P]),
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -195,6 +197,14 @@ def fa_decode_splitkv_paged(q, k_cache, v_cache, block_table, seqlens, o_part, l
     _call("fa_decode_splitkv_paged", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
           _ptr(seqlens), _ptr(o_part), _ptr(lse_part), B, Hq, Hkv, num_pages, page_size,
           max_pages, max_seqlen, d, scale, num_splits, _stream(stream))
+
+
+def fa_decode_splitkv_paged_q(q, k_cache, v_cache, block_table, seqlens, o_part, lse_part, B, Hq,
+                              Hkv, Nq, num_pages, page_size, max_pages, max_seqlen, d, scale,
+                              causal, num_splits, stream=None):
+    _call("fa_decode_splitkv_paged_q", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+          _ptr(seqlens), _ptr(o_part), _ptr(lse_part), B, Hq, Hkv, Nq, num_pages, page_size,
+          max_pages, max_seqlen, d, scale, int(causal), num_splits, _stream(stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, Hq, Hkv, total_q, total_k, max_seqlen_q,
@@ -458,6 +468,27 @@ def decode_paged(q, k_cache, v_cache, block_table, seqlens, num_splits, max_seql
     fa_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream)
     if return_partials:
         return o, lse, o_part, lse_part
+    return o, lse
+
+
+def decode_paged_tokens(q, k_cache, v_cache, block_table, seqlens, num_splits, causal=False,
+                        max_seqlen=None, scale=None, stream=None):
+    """decode_paged for a few query tokens per head: q [B][Hq][Nq][d] (the
+    newest Nq positions of each entry) -> (O [B][Hq][Nq][d], LSE [B][Hq][Nq])."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    num_pages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    max_pages = block_table.shape[1]
+    ms = max_pages * page_size if max_seqlen is None else int(max_seqlen)
+    s = _default_scale(d, scale)
+    o_part = torch.empty((B, Hq, Nq, num_splits, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((B, Hq, Nq, num_splits), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    fa_decode_splitkv_paged_q(q, k_cache, v_cache, block_table, seqlens, o_part, lse_part, B, Hq,
+                              Hkv, Nq, num_pages, page_size, max_pages, ms, d, s, causal,
+                              num_splits, stream)
+    fa_decode_combine(o_part, lse_part, o, lse, B, Hq * Nq, d, num_splits, stream)
     return o, lse
 
 

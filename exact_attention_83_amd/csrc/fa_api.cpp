@@ -359,11 +359,11 @@ fa_status fa_decode_splitkv_q(const void* q, const void* k, const void* v, float
                                             num_splits, stream, Nq, causal != 0));
 }
 
-fa_status fa_decode_splitkv_paged(const void* q, const void* k_cache, const void* v_cache,
-                                  const int* block_table, const int* seqlens, float* o_part,
-                                  float* lse_part, int B, int Hq, int Hkv, int num_pages,
-                                  int page_size, int max_pages, int max_seqlen, int d, float scale,
-                                  int num_splits, hipStream_t stream) {
+static fa_status decode_paged_impl(const void* q, const void* k_cache, const void* v_cache,
+                                   const int* block_table, const int* seqlens, float* o_part,
+                                   float* lse_part, int B, int Hq, int Hkv, int Nq, int num_pages,
+                                   int page_size, int max_pages, int max_seqlen, int d,
+                                   float scale, int causal, int num_splits, hipStream_t stream) {
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) ||
       !aligned16(lse_part) || block_table == nullptr || seqlens == nullptr ||
       (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seqlens) & 3u))
@@ -378,7 +378,8 @@ fa_status fa_decode_splitkv_paged(const void* q, const void* k_cache, const void
   if ((int64_t)max_pages * page_size < max_seqlen) return FA_ERR_INVALID_ARG;
   if ((int64_t)num_pages * page_size * Hkv * d >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 32) return FA_ERR_UNSUPPORTED;
+  if (Nq <= 0 || Nq > max_seqlen) return FA_ERR_INVALID_ARG;
+  if ((int64_t)(Hq / Hkv) * Nq > 32) return FA_ERR_UNSUPPORTED;
   if ((int64_t)B * Hkv * num_splits > (int64_t)1 << 30) return FA_ERR_UNSUPPORTED;
   // Keys per chunk: the longest sequence cut in num_splits pieces, rounded up
   // to the kernel's 32-key block (trailing chunks of shorter sequences are
@@ -387,7 +388,29 @@ fa_status fa_decode_splitkv_paged(const void* q, const void* k_cache, const void
   const int chunk = (per + 31) / 32 * 32;
   return hip_status(fa::launch_decode_split_paged(q, k_cache, v_cache, block_table, seqlens,
                                                   o_part, lse_part, B, Hq, Hkv, shift, max_pages,
-                                                  num_pages, chunk, d, scale, num_splits, stream));
+                                                  num_pages, chunk, d, scale, num_splits, stream, Nq,
+                                                  causal != 0));
+}
+
+fa_status fa_decode_splitkv_paged(const void* q, const void* k_cache, const void* v_cache,
+                                  const int* block_table, const int* seqlens, float* o_part,
+                                  float* lse_part, int B, int Hq, int Hkv, int num_pages,
+                                  int page_size, int max_pages, int max_seqlen, int d, float scale,
+                                  int num_splits, hipStream_t stream) {
+  return decode_paged_impl(q, k_cache, v_cache, block_table, seqlens, o_part, lse_part, B, Hq,
+                           Hkv, 1, num_pages, page_size, max_pages, max_seqlen, d, scale, 0,
+                           num_splits, stream);
+}
+
+fa_status fa_decode_splitkv_paged_q(const void* q, const void* k_cache, const void* v_cache,
+                                    const int* block_table, const int* seqlens, float* o_part,
+                                    float* lse_part, int B, int Hq, int Hkv, int Nq,
+                                    int num_pages, int page_size, int max_pages, int max_seqlen,
+                                    int d, float scale, int causal, int num_splits,
+                                    hipStream_t stream) {
+  return decode_paged_impl(q, k_cache, v_cache, block_table, seqlens, o_part, lse_part, B, Hq,
+                           Hkv, Nq, num_pages, page_size, max_pages, max_seqlen, d, scale, causal,
+                           num_splits, stream);
 }
 
 fa_status fa_decode_combine(const float* o_part, const float* lse_part, void* o, float* lse,

@@ -358,19 +358,19 @@ hipError_t launch_decode_split_paged(const void* q, const void* k_cache, const v
                                      const int* block_table, const int* seqlens, float* o_part,
                                      float* lse_part, int B, int Hq, int Hkv, int page_shift,
                                      int max_pages, int num_pages, int chunk, int d, float scale,
-                                     int num_splits, hipStream_t stream) {
+                                     int num_splits, hipStream_t stream, int Nq, bool causal) {
   dim3 grid(B * Hkv * num_splits), block(256);
   const float sl2 = scale * kLog2e;
   if (d == 128)
     hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, block, 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
                        o_part, lse_part, Hq, Hkv, 0, num_splits, scale, sl2, block_table,
-                       seqlens, page_shift, max_pages, num_pages, chunk);
+                       seqlens, page_shift, max_pages, num_pages, chunk, Nq, causal ? 1 : 0);
   else
     hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, block, 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
                        o_part, lse_part, Hq, Hkv, 0, num_splits, scale, sl2, block_table,
-                       seqlens, page_shift, max_pages, num_pages, chunk);
+                       seqlens, page_shift, max_pages, num_pages, chunk, Nq, causal ? 1 : 0);
   return hipGetLastError();
 }
 

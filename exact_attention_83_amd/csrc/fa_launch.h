@@ -70,7 +70,8 @@ hipError_t launch_decode_split_paged(const void* q, const void* k_cache, const v
                                      const int* block_table, const int* seqlens, float* o_part,
                                      float* lse_part, int B, int Hq, int Hkv, int page_shift,
                                      int max_pages, int num_pages, int chunk, int d, float scale,
-                                     int num_splits, hipStream_t stream);
+                                     int num_splits, hipStream_t stream, int Nq = 1,
+                                     bool causal = false);
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o,
                                  float* lse, int B, int Hq, int d, int num_splits,
                                  hipStream_t stream);

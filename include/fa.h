@@ -338,6 +338,23 @@ fa_status fa_decode_splitkv_paged(const void* q, const void* k_cache, const void
                                   float scale, int num_splits, hipStream_t stream);
 
 /*
+ * fa_decode_splitkv_paged with a few query tokens per head: q [B][Hq][Nq][d]
+ * are the newest Nq positions of each entry, with the end-aligned causal mask
+ * of fa_decode_splitkv_q (token t sees logical keys 0 .. seqlens[b]-Nq+t)
+ * when causal is set.  Partials and the combine as for fa_decode_splitkv_q
+ * (rows per (b, hq, token)).  Requires 1 <= Nq <= max_seqlen and
+ * (Hq/Hkv) * Nq <= 32; an entry with seqlens[b] < Nq leaves its first tokens
+ * without keys when causal (O = 0, LSE = -inf).  Nq == 1 is exactly
+ * fa_decode_splitkv_paged.
+ */
+fa_status fa_decode_splitkv_paged_q(const void* q, const void* k_cache, const void* v_cache,
+                                    const int* block_table, const int* seqlens,
+                                    float* o_part, float* lse_part,
+                                    int B, int Hq, int Hkv, int Nq, int num_pages, int page_size,
+                                    int max_pages, int max_seqlen, int d,
+                                    float scale, int causal, int num_splits, hipStream_t stream);
+
+/*
  * Merge of the split partials ([CH18] §18.8.2 (2), reduction step):
  *   lse = M + ln sum_c exp(lse_c - M) with M = max_c lse_c,
  *   O   = sum_c exp(lse_c - lse) * O_c.

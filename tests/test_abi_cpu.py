@@ -295,3 +295,16 @@ def test_decode_tokens_validation(lib):
     assert call(Nq=9) == fa.FA_ERR_UNSUPPORTED          # 4 heads x 9 tokens > 32
     assert call(d=96) == fa.FA_ERR_UNSUPPORTED
 
+
+def test_decode_paged_tokens_validation(lib):
+    """fa_decode_splitkv_paged_q: the paged checks plus the token count
+    (1 .. max_seqlen) and the 32 columns of a tile."""
+    def call(Nq=4, Hq=8, Hkv=2, maxs=100, page=16, maxp=8):
+        return lib.fa_decode_splitkv_paged_q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, Hq, Hkv,
+                                             Nq, 64, page, maxp, maxs, 128, 0.1, 1, 4, None)
+    assert call(Nq=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Nq=101) == fa.FA_ERR_INVALID_ARG
+    assert call(Nq=9) == fa.FA_ERR_UNSUPPORTED           # 4 heads x 9 tokens > 32
+    assert call(page=24) == fa.FA_ERR_UNSUPPORTED
+    assert call(maxs=129) == fa.FA_ERR_INVALID_ARG
+

@@ -839,6 +839,45 @@ def test_decode_paged_small(fa_gpu, cfg):
                 assert np.all(np.isfinite(lpn[b, :, c]))
 
 
+@pytest.mark.parametrize("cfg", [
+    # B, Hq, Hkv, seqlens, page, d, splits, Nq
+    (2, 8, 2, (1000, 77), 16, 128, 8, 4),    # ragged lengths, 4 heads x 4 tokens
+    (3, 4, 4, (5, 33, 512), 32, 128, 4, 5),  # a sequence barely longer than the tokens
+    (1, 32, 8, (4096,), 64, 64, 16, 8),      # 4 heads x 8 tokens = 32 columns, d = 64
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_paged_tokens(fa_gpu, cfg, causal):
+    """A few query tokens over a paged cache, with and without the end-aligned
+    causal mask, against the oracle (gather through the table, then the
+    few-token decode)."""
+    B, Hq, Hkv, seqlens, page, d, splits, Nq = cfg
+    w, x = paged_case(B, Hq, Hkv, seqlens, page, d, splits, seed=62)
+    g = torch.Generator("cpu").manual_seed(63)
+    q = torch.randn(B, Hq, Nq, d, generator=g).to(torch.bfloat16).cuda()
+    say(f"decode paged tokens B={B} Hq={Hq} Hkv={Hkv} seqlens={seqlens} page={page} d={d} "
+        f"splits={splits} Nq={Nq} causal={causal}")
+    o, lse = fa_gpu.decode_paged_tokens(q, x["k_cache"], x["v_cache"], x["block_table"],
+                                        x["seqlens"], splits, causal=causal,
+                                        max_seqlen=max(seqlens))
+    torch.cuda.synchronize()
+    ro, rl = A.decode_paged_multi(to_f64(q), to_f64(x["k_cache"]), to_f64(x["v_cache"]),
+                                  x["block_table"].cpu().numpy(), seqlens, w.scale, causal)
+    assert maxabs(to_f64(o), ro) <= BF16_O
+    assert maxabs(to_f64(lse), rl) <= BF16_LSE
+
+
+def test_decode_paged_tokens_one_token_is_paged_decode(fa_gpu):
+    """Nq = 1 runs the paged single-token decode's arithmetic: bit-identical."""
+    w, x = paged_case(2, 8, 2, (1000, 77), 16, 128, 8, seed=64)
+    say("decode paged tokens Nq=1 vs paged decode")
+    a = fa_gpu.decode_paged_tokens(x["q"], x["k_cache"], x["v_cache"], x["block_table"],
+                                   x["seqlens"], 8, causal=True, max_seqlen=1000)
+    b = fa_gpu.decode_paged(x["q"], x["k_cache"], x["v_cache"], x["block_table"], x["seqlens"],
+                            8, max_seqlen=1000)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
 def test_decode_paged_equals_dense(fa_gpu):
     """The same K/V rows laid out densely and scattered over 16-key pages,
     with the same 512-key chunks: the two kernels run the same arithmetic, so
