@@ -136,6 +136,23 @@ def test_bf16_backward_small(fa_gpu, d, causal, shape):
         assert e <= BF16_GRAD, (name, e)
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 1, 300, 700, 128), (2, 4, 2, 777, 129, 64),
+                                   (1, 2, 2, 64, 4000, 128), (1, 1, 1, 1000, 33, 128)])
+def test_bf16_backward_unequal_lengths(fa_gpu, shape):
+    """Non-causal backward with Nq != Nk (more keys than queries and the
+    reverse, ragged on both sides, GQA), against the oracle."""
+    B, Hq, Hkv, Nq, Nk, d = shape
+    x = gen(B, Hq, Hkv, Nq, Nk, d, "bf16", 32, grad=True)
+    o, lse = check_forward(fa_gpu, x, False, BF16_O, BF16_LSE, f"bwd-prep Nq={Nq} Nk={Nk}")
+    say(f"backward bf16 unequal lengths shape={shape}")
+    grads = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=False)
+    torch.cuda.synchronize()
+    ref = A.backward(*(to_f64(x[n]) for n in ("q", "k", "v", "do")), 1 / math.sqrt(d), False)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        e = rel_l2(to_f64(got), want)
+        assert e <= BF16_GRAD, (name, e)
+
+
 def test_causal_config_sampled(fa_gpu):
     """bf16 B=2 H=16 N=8192 d=128 causal at full size, in the launch
     configuration the benchmark times.  Forward: 24 rows of every head
