@@ -14,7 +14,8 @@
  *
  * Conventions shared by every entry point
  *   - Tensors are device pointers to contiguous row-major [B][H][N][d] arrays
- *     ("BHSD"): element (b,h,n,c) sits at ((b*H + h)*N + n)*d + c.
+ *     ("BHSD"): element (b,h,n,c) sits at ((b*H + h)*N + n)*d + c, unless an
+ *     entry point states another layout (packed batches, paged caches).
  *   - bf16 tensors are IEEE bfloat16 stored as 16-bit words; fp32 tensors are
  *     float.  Every tensor pointer must be 16-byte aligned.
  *   - Grouped-query attention: Hq must be a multiple of Hkv and query head hq
@@ -22,7 +23,8 @@
  *   - scale multiplies Q K^T; it must be finite and > 0 (the usual value is
  *     1/sqrt(d)).
  *   - causal: key j is visible to query i iff j <= i ([CH18] §18.2.2 item 3);
- *     it requires Nq == Nk.
+ *     it requires Nq == Nk.  The few-token decode entry points align their
+ *     causal mask to the end of the keys instead (stated there).
  *   - lse is fp32 [B][Hq][Nq]: lse_i = ln sum_j exp(scale * q_i . k_j) over the
  *     visible keys (natural log).
  *   - Ownership: the caller allocates and owns every buffer, workspaces
