@@ -190,6 +190,11 @@ def main(argv=None):
     ms_step = t_start.elapsed_time(t_end) / a.steps
     avg = lambda i, j: sum(m[i].elapsed_time(m[j]) for m in marks) / a.steps
     fwd_ms, dkdv_ms, dq_ms = avg(0, 1), avg(2, 3), avg(4, 5)
+    # per-step spread: median and minimum of each step (forward start to dQ
+    # end) and of each dK/dV launch
+    per_step = sorted(m[0].elapsed_time(m[5]) for m in marks)
+    per_dkdv = sorted(m[2].elapsed_time(m[3]) for m in marks)
+    median = lambda xs: xs[len(xs) // 2] if len(xs) % 2 else 0.5 * (xs[len(xs) // 2 - 1] + xs[len(xs) // 2])
     step_flops = w.fwd_flops() + w.bwd_flops()
     value = step_flops / (ms_step * 1e-3) / 1e12
     rate = lambda flops, ms: flops / (ms * 1e-3) / 1e12
@@ -208,7 +213,12 @@ def main(argv=None):
                            "tflops": round(rate(w.bwd_flops(), bwd_ms), 1),
                            "frac_peak": round(rate(w.bwd_flops(), bwd_ms) / PEAK_BF16_TFLOPS, 4),
                            "dkdv_executed_tflops": round(rate(4 * unit, dkdv_ms), 1),
-                           "dq_executed_tflops": round(rate(3 * unit, dq_ms), 1)}
+                           "dq_executed_tflops": round(rate(3 * unit, dq_ms), 1),
+                           "dkdv_ms_median": round(median(per_dkdv), 4),
+                           "dkdv_ms_min": round(per_dkdv[0], 4)}
+    parts["step_spread"] = {"ms_median": round(median(per_step), 4),
+                            "ms_min": round(per_step[0], 4),
+                            "ms_max": round(per_step[-1], 4)}
     log(f"step {ms_step:.3f} ms: fwd {fwd_ms:.3f} ms ({rate(w.fwd_flops(), fwd_ms):.0f} TF), "
         f"dkdv {dkdv_ms:.3f} ms, dq {dq_ms:.3f} ms, bwd {rate(w.bwd_flops(), bwd_ms):.0f} TF")
 
