@@ -1051,6 +1051,24 @@ def test_fp8_forward_edge_cases(fa_gpu, case, causal):
     assert maxabs(to_f64(lse), rl) <= 5e-2
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_forward_bf16_backward(fa_gpu, causal):
+    """The mixed mode the pages name as the fp8 fallback: fp8 forward (rotated,
+    per-block e4m3) for O and LSE, then the bf16 backward on the unquantised
+    inputs with those O and LSE.  On N(0,1) inputs the gradients stay within
+    the fp8 tolerance of the exact ones."""
+    x = gen(1, 2, 2, 1024, 1024, 128, "bf16", 65, grad=True)
+    signs = (torch.randint(0, 2, (128,), generator=torch.Generator().manual_seed(8)) * 2 - 1).to(torch.int8).cuda()
+    say(f"fp8 forward + bf16 backward causal={causal}")
+    o8, l8, _ = fp8_pipeline(fa_gpu, x, signs, causal)
+    grads = fa_gpu.backward(x["q"], x["k"], x["v"], o8, l8, x["do"], causal=causal)
+    torch.cuda.synchronize()
+    ref = A.backward(*(to_f64(x[n]) for n in ("q", "k", "v", "do")), 1 / math.sqrt(128), causal)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        e = rel_l2(to_f64(got), want)
+        assert e <= FP8_REL, (name, e)
+
+
 def test_fp8_config_sampled(fa_gpu):
     """B=2 H=16 N=8192 d=128 with 0.1% outliers of magnitude 50 in Q and K,
     rotated: sampled rows of every head against the oracle on the dequantised
