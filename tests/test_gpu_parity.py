@@ -153,6 +153,34 @@ def test_bf16_backward_unequal_lengths(fa_gpu, shape):
         assert e <= BF16_GRAD, (name, e)
 
 
+def _random_shapes(n, seed):
+    rs = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rs.choice([1, 2, 3]))
+        g = int(rs.choice([1, 2, 4]))
+        causal = bool(rs.integers(0, 2))
+        nq = int(rs.integers(1, 700))
+        nk = nq if causal else int(rs.integers(1, 700))
+        out.append((int(rs.integers(1, 3)), hkv * g, hkv, nq, nk, int(rs.choice([64, 128])), causal))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(12, 2026))
+def test_random_shapes_forward_backward(fa_gpu, shape):
+    """Seeded random shapes (batch, group size, lengths from 1 to 699, both
+    head dims, causal or not): forward and backward against the oracle."""
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    x = gen(B, Hq, Hkv, Nq, Nk, d, "bf16", 96, grad=True)
+    o, lse = check_forward(fa_gpu, x, causal, BF16_O, BF16_LSE, f"random {shape}")
+    grads = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal)
+    torch.cuda.synchronize()
+    ref = A.backward(*(to_f64(x[n]) for n in ("q", "k", "v", "do")), 1 / math.sqrt(d), causal)
+    for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+        e = rel_l2(to_f64(got), want)
+        assert e <= BF16_GRAD, (name, e)
+
+
 def test_causal_config_sampled(fa_gpu):
     """bf16 B=2 H=16 N=8192 d=128 causal at full size, in the launch
     configuration the benchmark times.  Forward: 24 rows of every head
