@@ -673,10 +673,11 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   constexpr int ROWB = D * 2;
   constexpr int TILE = BC * ROWB;
   constexpr int LPW = TILE / 1024 / NW;
-  // Two slots of (K, V), one LDS variable each (see bwd_dkdv_kernel).
-  __shared__ __attribute__((aligned(1024))) char k0s[TILE], v0s[TILE], k1s[TILE], v1s[TILE];
-  auto kslot = [&](int sl) -> char* { return sl == 0 ? k0s : k1s; };
-  auto vslot = [&](int sl) -> char* { return sl == 0 ? v0s : v1s; };
+  // Three slots of (K, V), one LDS variable each (see bwd_dkdv_kernel).
+  __shared__ __attribute__((aligned(1024))) char k0s[TILE], v0s[TILE], k1s[TILE], v1s[TILE],
+      k2s[TILE], v2s[TILE];
+  auto kslot = [&](int sl) -> char* { return sl == 0 ? k0s : sl == 1 ? k1s : k2s; };
+  auto vslot = [&](int sl) -> char* { return sl == 0 ? v0s : sl == 1 ? v1s : v2s; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -792,11 +793,19 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   }
   settle(lse2);
   settle(dlt);
-  if (ntiles > 0) issue(0, 0);
+  // Two K/V tiles in flight while one is computed.  Past the last tile the
+  // last one is loaded again into the free slot, so that every step issues
+  // the same loads: the wait below is then exact, and the compiler's view of
+  // which slot is in flight stays precise enough not to add waits of its own.
+  if (ntiles > 0) {
+    issue(0, 0);
+    issue(min(1, ntiles - 1), 1);
+  }
   // One iteration per KV tile; S = slot (a compile-time constant).
   auto body = [&](int j, auto S) {
     constexpr int slot = decltype(S)::value;
-    wait_vmem();
+    // tile j has landed once at most the next step's loads (2*LPW) remain
+    wait_vmem_le<2 * LPW>();
     lds_barrier();
     const char* ks_ = kslot(slot);
     const char* vs_ = vslot(slot);
@@ -817,17 +826,31 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
       s[kb] = f32x16{0};
       dp[kb] = f32x16{0};
     }
+    // LDS operands are read PF products ahead of their use (the latency of
+    // a read is several products long, and only one other wave shares the
+    // SIMD to hide it).  Operand m of phases A and B: key block m % 2, k-step
+    // m / 2.
+    constexpr int PFA = 4, PFB = 3;
+    auto ka_of = [&](int m) { return lds_read<u32x4>(ks_, (m & 1) * 32 * ROWB + ard[m >> 1]); };
+    auto va_of = [&](int m) { return lds_read<u32x4>(vs_, (m & 1) * 32 * ROWB + ard[m >> 1]); };
     // (A)
+    u32x4 va[PFB];
+    {
+      u32x4 ka[PFA];
 #pragma unroll
-    for (int m = 0; m < NAB; ++m) {
-      const int kk = m >> 1, kb = m & 1;
-      const u32x4 ka = lds_read<u32x4>(ks_, kb * 32 * ROWB + ard[kk]);
-      if (m == 0) {
-        // next tile's loads after this tile's first LDS reads
-        asm volatile("" ::: "memory");
-        if (j + 1 < ntiles) issue(j + 1, slot ^ 1);
+      for (int p = 0; p < PFA; ++p) ka[p] = ka_of(p);
+      // next tile's loads after this tile's first LDS reads
+      asm volatile("" ::: "memory");
+      issue(min(j + 2, ntiles - 1), (slot + 2) % 3);
+#pragma unroll
+      for (int m = 0; m < NAB; ++m) {
+        const int kk = m >> 1, kb = m & 1;
+        const u32x4 a = ka[m % PFA];
+        if (m + PFA < NAB) ka[m % PFA] = ka_of(m + PFA);
+        else if (m + PFA - NAB < PFB) va[m + PFA - NAB] = va_of(m + PFA - NAB);
+        s[kb] = mfma_32x32x16_bf16(a, qf[kk], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      s[kb] = mfma_32x32x16_bf16(ka, qf[kk], s[kb]);
     }
     const int rw0 = q0 + wave * 32;  // this wave's first row
     bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > rw0);
@@ -851,12 +874,12 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     __builtin_amdgcn_sched_barrier(0);
     // (B)
     {
-      u32x4 va = lds_read<u32x4>(vs_, ard[0]);
 #pragma unroll
       for (int m = 0; m < NAB; ++m) {
         const int kk = m >> 1, kb = m & 1;
-        dp[kb] = mfma_32x32x16_bf16(va, gf[kk], dp[kb]);
-        if (m + 1 < NAB) va = lds_read<u32x4>(vs_, ((m + 1) & 1) * 32 * ROWB + ard[(m + 1) >> 1]);
+        const u32x4 a = va[m % PFB];
+        if (m + PFB < NAB) va[m % PFB] = va_of(m + PFB);
+        dp[kb] = mfma_32x32x16_bf16(a, gf[kk], dp[kb]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < EPB; ++t) {
@@ -875,8 +898,6 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
         dsb[kb][st][w] = pack_bf16(dp[kb][r - 1], dp[kb][r]);
       }
     };
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ds_elem(0, r);
     auto kfragT = [&](int kb, int st, int db) {
       const char* kp = ks_ + (kb * 32 + st * 16) * ROWB;
       const u32x2 a0 = lds_read_tr16(kp + trd0[db]);
@@ -884,13 +905,17 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
       return u32x4{a0[0], a0[1], a1[0], a1[1]};
     };
     {
-      u32x4 kt = kfragT(0, 0, 0);
+      // operand m: key block m / NCB, k-step (m / DBLK) % 2, head-dim block m % DBLK
+      auto kt_of = [&](int m) { return kfragT(m / NCB, (m / DBLK) & 1, m % DBLK); };
+      u32x4 kt[2] = {kt_of(0), kt_of(1)};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds_elem(0, r);
 #pragma unroll
       for (int m = 0; m < 2 * NCB; ++m) {
         const int kb = m / NCB, st = (m / DBLK) & 1, db = m % DBLK;
-        dq[db] = mfma_32x32x16_bf16(kt, dsb[kb][st], dq[db]);
-        if (m + 1 < 2 * NCB)
-          kt = kfragT((m + 1) / NCB, ((m + 1) / DBLK) & 1, (m + 1) % DBLK);
+        const u32x4 a = kt[m & 1];
+        if (m + 2 < 2 * NCB) kt[m & 1] = kt_of(m + 2);
+        dq[db] = mfma_32x32x16_bf16(a, dsb[kb][st], dq[db]);
         __builtin_amdgcn_sched_barrier(0);
         if (m < NCB) {
 #pragma unroll
@@ -900,10 +925,12 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
       }
     }
   };
-  for (int j = 0; j < ntiles; j += 2) {
+  for (int j = 0; j < ntiles; j += 3) {
     body(j, IntConst<0>{});
     if (j + 1 < ntiles) body(j + 1, IntConst<1>{});
+    if (j + 2 < ntiles) body(j + 2, IntConst<2>{});
   }
+  wait_vmem();  // the reloads of the last tile
 
   // dQ = scale * dQ^T, written as bf16 rows.
   if (qrow < Nq) {
