@@ -477,17 +477,45 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       sb[kb] = f32x16{0};
       dpb[kb] = f32x16{0};
     }
-    // (1) S: pair ks shares the Q fragment.
+    // Transposed B operand (dO^T or Q^T rows) of pair j of phases 3/4:
+    // st = j / DBLK, db = j % DBLK.
+    auto trB = [&](const char* base, int j) {
+      const int ro = (j / DBLK) * 16 * ROWB;
+      const u32x2 v0 = lds_read_tr16(base + ro + trd0[j % DBLK]);
+      const u32x2 v1 = lds_read_tr16(base + ro + trd1[j % DBLK]);
+      return u32x4{v0[0], v0[1], v1[0], v1[1]};
+    };
+    // The first LDS operands of each phase are read during the last products
+    // of the phase before it, so that no phase starts by waiting for LDS.
+    u32x4 ga[2], va[2][KB];  // phase 2: dO and V fragments, two pairs ahead
+    f32x4 lvn;               // phase 2: lse of the current row group
+    u32x4 gb[2], qb[2];      // phases 3 / 4: first two transposed B operands
+    f32x4 dln;               // phase 3: delta of the current row group
+    // (1) S: pair ks shares the Q fragment, read PF1 pairs ahead.
     {
-      u32x4 qa[2];
-      qa[0] = lds_read<u32x4>(qs, ard[0]);
-      qa[1] = lds_read<u32x4>(qs, ard[1]);
+      constexpr int PF1 = 3;
+      static_assert(KSTEPS >= PF1, "phase 1 prefetch depth");
+      u32x4 qa[PF1];
+#pragma unroll
+      for (int p = 0; p < PF1; ++p) qa[p] = lds_read<u32x4>(qs, ard[p]);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const u32x4 a = qa[ks & 1];
-        if (ks + 2 < KSTEPS) qa[ks & 1] = lds_read<u32x4>(qs, ard[ks + 2]);
+        const u32x4 a = qa[ks % PF1];
+        if (ks + PF1 < KSTEPS) {
+          qa[ks % PF1] = lds_read<u32x4>(qs, ard[ks + PF1]);
+        } else {
+          const int pp = ks + PF1 - KSTEPS;
+          if (pp < 2) {
+            ga[pp] = lds_read<u32x4>(gs, ard[pp]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) va[pp][kb] = lds_read<u32x4>(vw, kb * 32 * ROWB + ard[pp]);
+          } else {
+            lvn = lds_read<f32x4>(ls, (hf * 4) * 4);
+          }
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) sb[kb] = mfma_32x32x16_bf16(a, kf[kb][ks], sb[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // Mask keys past Nk, rows past Nq and (causal) keys after the query.
@@ -517,15 +545,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     // (2) dP, with P (in place of S) and its bf16 A operands.  Pair ks uses
     // the dO fragment ga and the V fragments of both key blocks.
     {
-      u32x4 ga[2], va[2][KB];
       f32x4 nl;  // -lse * log2(e) of the current row group
-      f32x4 lvn = lds_read<f32x4>(ls, (hf * 4) * 4);
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        ga[pp] = lds_read<u32x4>(gs, ard[pp]);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) va[pp][kb] = lds_read<u32x4>(vw, kb * 32 * ROWB + ard[pp]);
-      }
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const u32x4 g = ga[ks & 1];
@@ -537,6 +557,10 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
             va[ks & 1][kb] = lds_read<u32x4>(vw, kb * 32 * ROWB + ard[ks + 2]);
+        } else {
+          // phase 3's first operands
+          gb[ks + 2 - KSTEPS] = trB(gs, ks + 2 - KSTEPS);
+          if (ks + 1 == KSTEPS) dln = lds_read<f32x4>(ls, BQ * 4 + (hf * 4) * 4);
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -564,22 +588,14 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
         }
       }
     }
-    // Transposed B operand (dO^T or Q^T rows) of pair j of phases 3/4:
-    // st = j / DBLK, db = j % DBLK.
-    auto trB = [&](const char* base, int j) {
-      const int ro = (j / DBLK) * 16 * ROWB;
-      const u32x2 v0 = lds_read_tr16(base + ro + trd0[j % DBLK]);
-      const u32x2 v1 = lds_read_tr16(base + ro + trd1[j % DBLK]);
-      return u32x4{v0[0], v0[1], v1[0], v1[1]};
-    };
     // (3) dV += P^T dO, with dS = P (dP - delta) and its bf16 A operands.
     {
-      f32x4 dl, dln = lds_read<f32x4>(ls, BQ * 4 + (hf * 4) * 4);
-      u32x4 gb[2] = {trB(gs, 0), trB(gs, 1)};
+      f32x4 dl;
 #pragma unroll
       for (int j = 0; j < NPR; ++j) {
         const u32x4 b = gb[j & 1];
         if (j + 2 < NPR) gb[j & 1] = trB(gs, j + 2);
+        else qb[j + 2 - NPR] = trB(qs, j + 2 - NPR);  // phase 4's first operands
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const int m = 2 * j + kb;
@@ -602,7 +618,6 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     }
     // (4) dK += dS^T Q.
     {
-      u32x4 qb[2] = {trB(qs, 0), trB(qs, 1)};
 #pragma unroll
       for (int j = 0; j < NPR; ++j) {
         const u32x4 b = qb[j & 1];
