@@ -354,6 +354,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     return lds_read<u32x4>(ks, (h & 1) * 32 * ROWB + krd[h >> 1]);
   };
 
+  // The first AHEAD K and V fragments of a step are read at the end of the
+  // step before it (or in the prologue), after that step's barrier: a step
+  // starts with its first operands in flight rather than waiting for them.
+  constexpr int AHEAD = 2;
+  u32x4 kfr[AHEAD], vfr[AHEAD];
+#pragma unroll
+  for (int h = 0; h < AHEAD; ++h) {
+    kfr[h] = kfrag(kslot(1), h);  // K_1
+    vfr[h] = vfrag(vslot(1), h);  // zeros ("V_{-1}")
+  }
   // One pipeline step; U = i % 2 makes slots and buffers compile-time
   // constants, so the LDS fragment addresses are a per-lane register plus an
   // immediate.
@@ -364,22 +374,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     u32x4 (*pb_cur)[2] = pbuf[u];
     u32x4 (*pb_prev)[2] = pbuf[u ^ 1];
     const bool more_k = i + 2 < ntiles;
-    constexpr int AHEAD = 2;
     float lt = 0.f;  // this lane's sum of p over tile i
     {
       const char* ks = kslot(u ^ 1);   // K_{i+1}
       const char* vs = vslot(u ^ 1);   // V_{i-1}
       s_nxt[0] = f32x16{0};
       s_nxt[1] = f32x16{0};
-      u32x4 kfr[AHEAD], vfr[AHEAD];
-#pragma unroll
-      for (int h = 0; h < AHEAD; ++h) {
-        kfr[h] = kfrag(ks, h);
-        vfr[h] = vfrag(vs, h);
-      }
-      // This step's loads go out after its first LDS reads: where the
-      // compiler cannot tell the slots apart (at the loop head) its wait then
-      // covers only the previous step's loads.
+      // This step's loads go out after its first LDS reads (issued at the
+      // end of the previous step).
       asm volatile("" ::: "memory");
       if (more_k) issue_k(i + 2, u);
       issue_v(i, u);
@@ -414,9 +416,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
         }
       };
       F(0);
+      // After group GB every LDS read of this step has been issued (the last
+      // K and V fragments are read AHEAD products before their use): wait for
+      // this step's loads (K_{i+2}, V_i) and the other waves there, then read
+      // the next step's first fragments while the last products run.
+      constexpr int GB = NG - 2 * AHEAD;
+      u32x4 kn[AHEAD], vn[AHEAD];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const int h = g >> 1;
+        if (g == GB) {
+          wait_vmem();
+          lds_barrier();
+#pragma unroll
+          for (int hh = 0; hh < AHEAD; ++hh) {
+            kn[hh] = kfrag(kslot(u), hh);
+            vn[hh] = vfrag(vslot(u), hh);
+          }
+        }
         if ((g & 1) == 0) {
           s_nxt[h & 1] = mfma_32x32x16_bf16(kfr[h % AHEAD], qf[h >> 1], s_nxt[h & 1]);
           if (h + AHEAD < NQK) kfr[h % AHEAD] = kfrag(ks, h + AHEAD);
@@ -432,6 +449,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
       A(NG - 1);
+#pragma unroll
+      for (int hh = 0; hh < AHEAD; ++hh) {
+        kfr[hh] = kn[hh];
+        vfr[hh] = vn[hh];
+      }
     }
     // Rare: the reference is too low for tile i.  Move it to the tile's max,
     // rescale O (which now holds tiles up to i-1) and l, and redo tile i's p.
@@ -454,9 +476,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(
     }
     l_run += lt;
     if (i + 1 < ntiles) mask(i + 1, s_nxt);
-    // K_{i+2} and V_i, issued above, are read in the next iteration.
-    wait_vmem();
-    lds_barrier();
   };
   for (int i0 = 0; i0 < ntiles; i0 += 2) {
     step(i0, IntConst<0>{});
