@@ -463,8 +463,10 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     // Four phases of NPH products each: (1) S = Q K^T; (2) dP = dO V^T with
     // P = exp(S*scale - lse) of the finished S computed between its products;
     // (3) dV += P^T dO with dS = P (dP - delta) computed between its products;
-    // (4) dK += dS^T Q.  Every LDS operand is read two product pairs ahead
-    // (this kernel has one wave per SIMD, so nothing else hides LDS latency).
+    // (4) dK += dS^T Q.  LDS operands are read two product pairs ahead (Q in
+    // phase 1 three), and each phase's first ones during the last products of
+    // the phase before it (this kernel has one wave per SIMD, so nothing else
+    // hides LDS latency).
     // Element x of phases 2/3 (EPP per product) is register r = 4*(x/8) + x%4
     // of block kb = (x/4)%2; register r holds query row 8*(r/4) + 4*hf + r%4.
     constexpr int NPH = KB * KSTEPS;  // products per phase
