@@ -36,13 +36,17 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c)
 // the backward).  Left to itself the compiler assigns MFMA results to one
 // register file for the whole kernel and, when the short-lived products
 // (whose results feed VALU work) compete for it, shuffles the long-lived
-// accumulators between files around every product.  The leading s_nop gives
-// the two wait states the hardware requires between a VALU write of an
-// operand and its read by a matrix instruction, which the compiler cannot see
-// through inline assembly; LDS and memory results are waited for by the
-// compiler as for any other use.
+// accumulators between files around every product.  The hardware needs two
+// wait states between a VALU write of an operand (or of the accumulator) and
+// its read by a matrix instruction, and the compiler does not look inside
+// inline assembly for that hazard: callers pass only operands produced well
+// before the product (fragments from LDS reads, whose waits the compiler
+// inserts as for any other use, and bf16 values packed in an earlier phase).
+// A CPU test compiles the kernels to assembly and checks that no VALU
+// instruction writes a register of a pinned product in the two instructions
+// before it.
 __device__ __forceinline__ void mfma_acc_pinned(f32x16& c, u32x4 a, u32x4 b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 // Wait states between the last pinned product into c and any read of c by a
 // non-matrix instruction (more than the 19 the longest product needs).
