@@ -547,6 +547,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     // (2) dP, with P (in place of S) and its bf16 A operands.  Pair ks uses
     // the dO fragment ga and the V fragments of both key blocks.
     {
+      // bf16 A operand of the element pair (x - 1, x), x odd
+      auto pack_p = [&](int x) {
+        const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
+        pa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(sb[kbe][r - 1], sb[kbe][r]);
+      };
       f32x4 nl;  // -lse * log2(e) of the current row group
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -583,12 +588,18 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
               if (gr < 3) lvn = lds_read<f32x4>(ls, ((gr + 1) * 8 + hf * 4) * 4);
             }
             sb[kbe][r] = fast_exp2(fmaf(sb[kbe][r], scale_log2, nl[e]));
-            if (e & 1)
-              pa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(sb[kbe][r - 1], sb[kbe][r]);
+          }
+          // The previous product's pairs are packed here, one product after
+          // their exp: packing right behind the exp costs a wait state each.
+          if (m > 0) {
+#pragma unroll
+            for (int t = 1; t < EPP; t += 2) pack_p(EPP * (m - 1) + t);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+#pragma unroll
+      for (int t = 1; t < EPP; t += 2) pack_p(EPP * (NPH - 1) + t);
     }
     // (3) dV += P^T dO, with dS = P (dP - delta) and its bf16 A operands.
     {
