@@ -21,12 +21,17 @@ size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
-// Shape checks shared by the attention entry points.
-fa_status check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+// Shape checks shared by the attention entry points.  elem_bytes is the size
+// of one Q/K/V element on the path (2 bf16, 4 fp32, 1 fp8).
+fa_status check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int elem_bytes = 2) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   // element offsets are formed in 64-bit, per-(b,h) row counts in 32-bit
   if ((int64_t)B * Hq > (1 << 24) || (int64_t)B * Hkv > (1 << 24)) return FA_ERR_UNSUPPORTED;
+  // One (b, head) slab of Q, K or V is addressed through a buffer descriptor
+  // with a 32-bit size and signed 32-bit offsets: it must stay below 2 GiB.
+  const int64_t n_max = Nq > Nk ? Nq : Nk;
+  if (n_max * d * elem_bytes >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -122,7 +127,7 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
                      hipStream_t stream) {
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
-  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d, 4)) return s;
   if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
   if (d != 64) return FA_ERR_UNSUPPORTED;
   if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
@@ -138,11 +143,12 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d) {
 static fa_status bwd_common(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, const void* dq, const void* dk,
                             const void* dv, void* ws, size_t ws_bytes, int B, int Hq, int Hkv,
-                            int Nq, int Nk, int d, float scale, int causal) {
+                            int Nq, int Nk, int d, float scale, int causal,
+                            int elem_bytes = 2) {
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_INVALID_ARG;
-  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d, elem_bytes)) return s;
   if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
   if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;
   if (ws == nullptr || !aligned16(ws)) return FA_ERR_WORKSPACE;
@@ -311,7 +317,7 @@ fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float
                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
                      int Nk, int d, float scale, int causal, hipStream_t stream) {
   if (fa_status s = bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
-                               Hq, Hkv, Nq, Nk, d, scale, causal))
+                               Hq, Hkv, Nq, Nk, d, scale, causal, 4))
     return s;
   if (d != 64) return FA_ERR_UNSUPPORTED;
   float* delta = static_cast<float*>(workspace);
@@ -439,7 +445,7 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(q_scale) ||
       !aligned16(k_scale) || !aligned16(v_scale) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
-  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d)) return s;
+  if (fa_status s = check_shape(B, Hq, Hkv, Nq, Nk, d, 1)) return s;
   if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
   if (d != 128) return FA_ERR_UNSUPPORTED;
   if (causal && Nq != Nk) return FA_ERR_UNSUPPORTED;

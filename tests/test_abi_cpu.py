@@ -124,6 +124,43 @@ def test_fp8_validation(lib):
                           0.1, 0, None) == fa.FA_ERR_INVALID_ARG
 
 
+def test_dense_paths_reject_slabs_past_2gib(lib):
+    """One (b, head) slab of Q, K or V is addressed through a buffer descriptor
+    with a 32-bit size and signed offsets: a slab of 2 GiB or more must be
+    refused (FA_ERR_UNSUPPORTED), never launched with a wrapped size."""
+    big = (1 << 31) // (128 * 2)                     # N * d * 2 == 2^31 at d = 128
+    assert call_fwd(lib, Nq=64, Nk=big) == fa.FA_ERR_UNSUPPORTED
+    assert call_fwd(lib, Nq=big, Nk=64) == fa.FA_ERR_UNSUPPORTED
+    assert call_fwd(lib, causal=1, Nq=big, Nk=big) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_window(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, big, big, 128, 0.1, 1,
+                             16, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_block_sparse(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, big, 128, 0.1, 0,
+                                   FAKE, FAKE, 4, None) == fa.FA_ERR_UNSUPPORTED
+    big32 = (1 << 31) // (64 * 4)                    # fp32 elements at d = 64
+    assert call_fwd(lib, "fa_fwd_f32", d=64, Nq=64, Nk=big32) == fa.FA_ERR_UNSUPPORTED
+    big8 = (1 << 31) // 128                          # fp8 codes at d = 128
+    assert lib.fa_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, big8, 128,
+                          0.1, 0, None) == fa.FA_ERR_UNSUPPORTED
+    ws = 1 << 40                                     # large enough never to be the reason
+    for name in ("fa_bwd", "fa_bwd_f32"):
+        d = 128 if name == "fa_bwd" else 64
+        n = big if name == "fa_bwd" else big32
+        assert getattr(lib, name)(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                  1, 1, 1, n, n, d, 0.1, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_window(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                             1, 1, 1, big, big, 128, 0.1, 1, 64, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 1, 1, 64, big,
+                           128, 0.1, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 1, 1, big, 64, 128,
+                         0.1, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_block_sparse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                   1, 1, 1, 64, big, 128, 0.1, 0, FAKE, FAKE, 4,
+                                   None) == fa.FA_ERR_UNSUPPORTED
+    # one row below the bound passes the shape check: the call then fails on
+    # the scale, which is checked after it, so nothing is launched
+    assert call_fwd(lib, Nq=64, Nk=big - 1, scale=0.0) == fa.FA_ERR_INVALID_ARG
+
+
 def test_binding_raises_value_error_on_bad_args(lib):
     with pytest.raises(ValueError):
         fa.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, 64, 128, 0.1, False, stream=0)
