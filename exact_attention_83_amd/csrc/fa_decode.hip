@@ -314,7 +314,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     const float* op = o_part + (size_t)row * S * d + j * VW;
 #pragma unroll 4
     for (int c = g; c < S; c += G) {
-      const float w = __expf(lp[c] - lse);
+      // a row no split saw (every lse_c = -inf, so lse = -inf) gets O = 0
+      const float w = lse == -INFINITY ? 0.f : __expf(lp[c] - lse);
       if constexpr (VW == 4) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(op + (size_t)c * d);
 #pragma unroll

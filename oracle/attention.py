@@ -142,6 +142,23 @@ def head_backward(q, k, v, do, scale, causal, window=None):
     return dq, dk, dv, delta
 
 
+def head_forward_backward(q, k, v, do, scale, causal, window=None):
+    """head_forward and head_backward of one head from one evaluation of P
+    (the same operations in the same order as those two functions, so the
+    results are identical to calling them separately).
+    Returns (o, lse, dq, dk, dv)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    p, m, l = softmax_rows(scores(q, k, scale, causal, window=window))
+    o = p @ v
+    lse = m + np.log(l)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = softmax_backward(p, dp)
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return o, lse, dq, dk, dv
+
+
 def head_dq_rows(q, k, v, do, scale, causal, rows):
     """dQ of the listed query rows of one head, row by row ([CH18] §18.2.4
     (2) restricted to row i: P_i = softmax of row i's visible scores,
@@ -217,28 +234,38 @@ def decode_multi(q, k, v, scale, causal=False):
     v = _f64(v)
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
-    assert Nq <= Nk
-    o = np.empty((B, Hq, Nq, v.shape[-1]))
-    lse = np.empty((B, Hq, Nq))
+    o = np.zeros((B, Hq, Nq, v.shape[-1]))
+    lse = np.full((B, Hq, Nq), -np.inf)
     vis = np.ones((Nq, Nk), dtype=bool)
     if causal:
         vis = np.arange(Nk)[None, :] <= (Nk - Nq + np.arange(Nq))[:, None]
+    # With more tokens than keys the earliest tokens see no key at all: their
+    # output is 0 and their LSE -inf (the sum over an empty set).
+    live = vis.any(axis=1)
     for b in range(B):
         for h in range(Hq):
             hk = kv_head(h, Hq, Hkv)
-            s = np.where(vis, scale * (q[b, h] @ k[b, hk].T), -np.inf)
+            s = np.where(vis[live], scale * (q[b, h][live] @ k[b, hk].T), -np.inf)
             p, m, l = softmax_rows(s)
-            o[b, h] = p @ v[b, hk]
-            lse[b, h] = m + np.log(l)
+            o[b, h][live] = p @ v[b, hk]
+            lse[b, h][live] = m + np.log(l)
     return o, lse
 
 
 def combine(o_parts, lse_parts):
     """Merge split partials with their log-sum-exp weights ([CH18] §18.8.2 (2),
-    the reduction step).  o_parts [..][S][d], lse_parts [..][S]."""
+    the reduction step).  o_parts [..][S][d], lse_parts [..][S].  A chunk
+    with no visible key has lse_c = -inf and weight 0; a row whose chunks are
+    all empty saw no key at all and gets O = 0, lse = -inf."""
+    o_parts = _f64(o_parts)
+    lse_parts = _f64(lse_parts)
     M = lse_parts.max(axis=-1, keepdims=True)
-    lse = M[..., 0] + np.log(np.exp(lse_parts - M).sum(axis=-1))
-    w = np.exp(lse_parts - lse[..., None])
+    dead = np.isneginf(M)
+    Mr = np.where(dead, 0.0, M)
+    z = np.exp(lse_parts - Mr).sum(axis=-1)
+    with np.errstate(divide="ignore"):
+        lse = Mr[..., 0] + np.log(z)
+    w = np.where(dead, 0.0, np.exp(lse_parts - np.where(dead, 0.0, lse[..., None])))
     o = (w[..., None] * o_parts).sum(axis=-2)
     return o, lse
 
@@ -341,7 +368,9 @@ def decode_paged(q, k_cache, v_cache, block_table, seqlens, scale):
 def decode_paged_multi(q, k_cache, v_cache, block_table, seqlens, scale, causal=False):
     """decode_multi over a paged KV cache: entry b's keys are the logical rows
     0 .. seqlens[b]-1 gathered through block_table[b] (as in decode_paged),
-    and its Nq query tokens are the newest positions (each seqlens[b] >= Nq).
+    and its Nq query tokens are the newest positions.  With seqlens[b] < Nq
+    and ``causal`` the entry's first Nq - seqlens[b] tokens see no key
+    (O = 0, LSE = -inf).
     q [B][Hq][Nq][d] -> O [B][Hq][Nq][d], LSE [B][Hq][Nq] (fp64)."""
     q = _f64(q)
     B, Hq, Nq, d = q.shape
@@ -350,7 +379,7 @@ def decode_paged_multi(q, k_cache, v_cache, block_table, seqlens, scale, causal=
     lse = np.empty((B, Hq, Nq))
     for b in range(B):
         n = int(seqlens[b])
-        assert n >= Nq
+        assert n >= 1
         kb = np.stack([gather_pages(k_cache, block_table[b], n, hk) for hk in range(Hkv)])[None]
         vb = np.stack([gather_pages(v_cache, block_table[b], n, hk) for hk in range(Hkv)])[None]
         o[b:b + 1], lse[b:b + 1] = decode_multi(q[b:b + 1], kb, vb, scale, causal)

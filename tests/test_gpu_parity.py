@@ -6,7 +6,11 @@ Tolerances (from the benchmark spec of the problem):
                            dQ/dK/dV relative L2 <= 1e-2
   fp32 tiny configuration: all of the above <= 1e-5
   fp8 forward:             relative L2 of O <= 5e-2 against the oracle fed the
-                           dequantised operands the kernel receives
+                           dequantised operands the kernel receives (the
+                           full-size fp8 check runs the oracle's own pipeline
+                           from the bf16 inputs)
+The full-size checks of every head of the benchmark's workloads are in
+test_gpu_full_size.py.
 """
 import math
 
@@ -181,36 +185,6 @@ def test_random_shapes_forward_backward(fa_gpu, shape):
         assert e <= BF16_GRAD, (name, e)
 
 
-def test_causal_config_sampled(fa_gpu):
-    """bf16 B=2 H=16 N=8192 d=128 causal at full size, in the launch
-    configuration the benchmark times.  Forward: 24 rows of every head
-    (tile edges, the diagonal, first and last rows).  Backward: dQ rows of
-    every head plus complete dK/dV of two heads, from the oracle's per-head
-    materialising backward."""
-    w = WORKLOADS["causal_bf16"]
-    x = {n: t.cuda() for n, t in make_inputs(w).items()}
-    say("forward causal_bf16 full size")
-    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=True)
-    torch.cuda.synchronize()
-    rows = np.array([0, 1, 63, 64, 127, 128, 129, 255, 256, 1000, 2047, 2048, 4095, 4096,
-                     5000, 6143, 6144, 7000, 8000, 8127, 8128, 8190, 8191, 3333])
-    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
-    o_ref, lse_ref = A.forward(q, k, v, w.scale, True, rows=rows)
-    assert maxabs(to_f64(o)[:, :, rows], o_ref) <= BF16_O
-    assert maxabs(to_f64(lse)[:, :, rows], lse_ref) <= BF16_LSE
-
-    say("backward causal_bf16 full size")
-    dq, dk, dv = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=True)
-    torch.cuda.synchronize()
-    do = to_f64(x["do"])
-    dq, dk, dv = to_f64(dq), to_f64(dk), to_f64(dv)
-    for (b, h) in ((0, 0), (1, 15)):
-        rq, rk, rv, _ = A.head_backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, True)
-        for name, got, want in (("dq", dq[b, h], rq), ("dk", dk[b, h], rk), ("dv", dv[b, h], rv)):
-            e = rel_l2(got, want)
-            assert e <= BF16_GRAD, (b, h, name, e)
-
-
 def test_long_sequence_causal(fa_gpu):
     """N = 65536 (eight times the benchmark length; GQA 2:1, d = 128, causal):
     sampled forward rows and dQ rows against the oracle row by row, and two
@@ -354,36 +328,6 @@ def test_window_covering_everything_equals_dense(fa_gpu, causal):
         assert torch.equal(a, b)
 
 
-def test_window_config_sampled(fa_gpu):
-    """B=2 H=16 N=8192 d=128, causal with a 4096-key left window (the page's
-    Mistral example), in the benchmark's launch configuration: sampled
-    forward rows of every head, dQ/dK/dV of two heads from the oracle."""
-    from workloads import WINDOWED
-    w = WINDOWED["window_bf16"]
-    x = {n: t.cuda() for n, t in make_inputs(w).items()}
-    win = (w.window_left, w.window_right)
-    say("forward window_bf16 full size")
-    o, lse = fa_gpu.forward(x["q"], x["k"], x["v"], causal=w.causal, window=win)
-    torch.cuda.synchronize()
-    rows = np.array([0, 1, 255, 256, 4095, 4096, 4097, 4352, 5000, 6143, 8000, 8191])
-    q, k, v = (to_f64(x[n]) for n in ("q", "k", "v"))
-    o_ref, lse_ref = A.forward(q, k, v, w.scale, w.causal, rows=rows, window=win)
-    assert maxabs(to_f64(o)[:, :, rows], o_ref) <= BF16_O
-    assert maxabs(to_f64(lse)[:, :, rows], lse_ref) <= BF16_LSE
-    say("backward window_bf16 full size")
-    dq, dk, dv = fa_gpu.backward(x["q"], x["k"], x["v"], o, lse, x["do"], causal=w.causal,
-                                 window=win)
-    torch.cuda.synchronize()
-    do = to_f64(x["do"])
-    dq, dk, dv = to_f64(dq), to_f64(dk), to_f64(dv)
-    for (b, h) in ((0, 3), (1, 12)):
-        rq, rk, rv, _ = A.head_backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal,
-                                        window=win)
-        for name, got, want in (("dq", dq[b, h], rq), ("dk", dk[b, h], rk), ("dv", dv[b, h], rv)):
-            e = rel_l2(got, want)
-            assert e <= BF16_GRAD, (b, h, name, e)
-
-
 # ------------------------------------------------------------- block-sparse
 
 def random_pattern(nq, nk, seed, p=0.4):
@@ -442,26 +386,6 @@ def test_block_sparse_all_blocks_equals_dense(fa_gpu, causal):
     od, ld = fa_gpu.forward(x["q"], x["k"], x["v"], causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o, od) and torch.equal(lse, ld)
-
-
-def test_block_sparse_config_sampled(fa_gpu):
-    """B=2 H=16 N=8192 d=128 with the local (+-1024 keys) + global (first 256
-    keys) pattern, in the benchmark's launch configuration: sampled rows of
-    every head against the oracle."""
-    from workloads import SPARSE
-    w = SPARSE["sparse_bf16"]
-    x = {n: t.cuda() for n, t in make_inputs(w).items()}
-    ptr, idx = w.pattern()
-    say("block-sparse full size")
-    o, lse = fa_gpu.forward_block_sparse(x["q"], x["k"], x["v"],
-                                         torch.tensor(ptr, dtype=torch.int32, device="cuda"),
-                                         torch.tensor(idx, dtype=torch.int32, device="cuda"))
-    torch.cuda.synchronize()
-    rows = np.array([0, 255, 256, 1500, 4095, 4096, 6000, 8191])
-    ro, rl = A.forward_block_sparse(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), w.scale, ptr,
-                                    idx, w.block_q, w.block_k, False, rows=rows)
-    assert maxabs(to_f64(o)[:, :, rows], ro) <= BF16_O
-    assert maxabs(to_f64(lse)[:, :, rows], rl) <= BF16_LSE
 
 
 @pytest.mark.parametrize("shape,causal", [((1, 4, 2, 700, 700, 128), False),
@@ -539,30 +463,6 @@ def test_block_sparse_backward_all_blocks_equals_dense(fa_gpu, causal):
     torch.cuda.synchronize()
     for a, b in zip(gs, gd):
         assert torch.equal(a, b)
-
-
-def test_block_sparse_backward_config_sampled(fa_gpu):
-    """The local + global pattern at B=2 H=16 N=8192 d=128, in the
-    benchmark's launch configuration: complete gradients of two heads
-    against the oracle (its backward restricted to one head)."""
-    from workloads import SPARSE
-    w = SPARSE["sparse_bf16"]
-    x = {n: t.cuda() for n, t in make_inputs(w).items()}
-    ptr, idx = w.pattern()
-    pd = torch.tensor(ptr, dtype=torch.int32, device="cuda")
-    idd = torch.tensor(idx, dtype=torch.int32, device="cuda")
-    say("block-sparse backward full size")
-    o, lse = fa_gpu.forward_block_sparse(x["q"], x["k"], x["v"], pd, idd)
-    dq, dk, dv = fa_gpu.backward_block_sparse(x["q"], x["k"], x["v"], o, lse, x["do"], pd, idd)
-    torch.cuda.synchronize()
-    dq, dk, dv = to_f64(dq), to_f64(dk), to_f64(dv)
-    for b, h in ((0, 0), (1, 15)):
-        one = [to_f64(x[n][b:b + 1, h:h + 1]) for n in ("q", "k", "v", "do")]
-        rq, rk, rv = A.backward_block_sparse(*one, w.scale, ptr, idx, w.block_q, w.block_k)
-        for name, got, want in (("dq", dq[b, h], rq[0, 0]), ("dk", dk[b, h], rk[0, 0]),
-                                ("dv", dv[b, h], rv[0, 0])):
-            e = rel_l2(got, want)
-            assert e <= BF16_GRAD, (b, h, name, e)
 
 
 # ------------------------------------------------------------------- decode
@@ -679,6 +579,31 @@ def test_decode_combine_direct(fa_gpu, B, Hq, S, d):
     assert maxabs(to_f64(lse)[:, :, 0], rl) <= 1e-5
 
 
+def test_decode_combine_rows_without_keys(fa_gpu):
+    """A row whose splits all have lse = -inf saw no key: the merge writes
+    O = 0 and LSE = -inf (never NaN); the other rows are merged as usual."""
+    B, Hq, S, d = 2, 3, 9, 128
+    say(f"decode combine rows without keys B={B} Hq={Hq} S={S} d={d}")
+    g = torch.Generator("cpu").manual_seed(1234)
+    op = torch.randn(B, Hq, S, d, generator=g, dtype=torch.float32)
+    lp = 3 * torch.randn(B, Hq, S, generator=g, dtype=torch.float32)
+    lp[0, 1, :] = -math.inf
+    lp[1, 2, :] = -math.inf
+    lp[1, 0, ::2] = -math.inf
+    o = torch.empty(B, Hq, 1, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, Hq, 1, dtype=torch.float32, device="cuda")
+    fa_gpu.fa_decode_combine(op.cuda(), lp.cuda(), o, lse, B, Hq, d, S)
+    torch.cuda.synchronize()
+    ro, rl = A.combine(op.double().numpy(), lp.double().numpy())
+    on, ln = to_f64(o)[:, :, 0], to_f64(lse)[:, :, 0]
+    assert not np.isnan(on).any() and not np.isnan(ln).any()
+    dead = np.isneginf(rl)
+    assert dead.sum() == 2 and np.array_equal(np.isneginf(ln), dead)
+    assert not on[dead].any()
+    assert maxabs(on[~dead], ro[~dead]) <= BF16_O
+    assert maxabs(ln[~dead], rl[~dead]) <= 1e-5
+
+
 def test_decode_config_full(fa_gpu):
     """B=8 Hq=32 Hkv=8 Nk=131072 d=128, 64 splits: every output and partial,
     the oracle widening one (b, KV head) slab at a time."""
@@ -770,33 +695,6 @@ def test_varlen_equals_dense(fa_gpu, causal):
     assert torch.equal(lse.view(Hq, B, N).permute(1, 0, 2), lsed)
 
 
-def test_varlen_config_sampled(fa_gpu):
-    """The packed workload (10 sequences, 31706 tokens, H=16, d=128, causal):
-    sampled query rows of every sequence and head against the oracle."""
-    from workloads import VARLEN, make_varlen_inputs
-    w = VARLEN["varlen_bf16"]
-    x = make_varlen_inputs(w, device="cuda")
-    say("varlen_bf16 full size")
-    mx = max(w.seqlens)
-    o, lse = fa_gpu.forward_varlen(x["q"], x["k"], x["v"], x["cu"], x["cu"], mx, mx,
-                                   causal=w.causal)
-    torch.cuda.synchronize()
-    o, lse = to_f64(o), to_f64(lse)
-    cu = x["cu"].tolist()
-    rs = np.random.default_rng(5)
-    for b, n in enumerate(w.seqlens):
-        rows = sorted(set([0, n - 1] + rs.integers(0, n, 6).tolist()))
-        sl = slice(cu[b], cu[b + 1])
-        qq = to_f64(x["q"][sl]).transpose(1, 0, 2)[None]
-        kk = to_f64(x["k"][sl]).transpose(1, 0, 2)[None]
-        vv = to_f64(x["v"][sl]).transpose(1, 0, 2)[None]
-        ro, rl = A.forward(qq, kk, vv, w.scale, w.causal, rows=rows)
-        got_o = o[cu[b] + np.array(rows)].transpose(1, 0, 2)
-        got_l = lse[:, cu[b] + np.array(rows)]
-        assert maxabs(got_o, ro[0]) <= BF16_O, b
-        assert maxabs(got_l, rl[0]) <= BF16_LSE, b
-
-
 # --------------------------------------------------------- varlen backward
 
 def varlen_grad_case(lens_q, Hq, Hkv, d, seed, lens_k=None):
@@ -868,33 +766,6 @@ def test_varlen_backward_equals_dense(fa_gpu, causal):
         assert torch.equal(dense(got, H), want)
 
 
-def test_varlen_backward_config_sampled(fa_gpu):
-    """The packed workload (10 sequences, 31706 tokens, H=16, d=128, causal)
-    backward in the benchmark's launch configuration: complete dQ/dK/dV of
-    one head of the longest sequence and of two heads of two short ones,
-    against the oracle's per-head backward."""
-    from workloads import VARLEN, make_varlen_inputs
-    w = VARLEN["varlen_bf16"]
-    x = make_varlen_inputs(w, device="cuda")
-    say("varlen_bf16 backward full size")
-    mx = max(w.seqlens)
-    o, lse = fa_gpu.forward_varlen(x["q"], x["k"], x["v"], x["cu"], x["cu"], mx, mx,
-                                   causal=w.causal)
-    dq, dk, dv = fa_gpu.backward_varlen(x["q"], x["k"], x["v"], o, lse, x["do"], x["cu"],
-                                        x["cu"], mx, mx, causal=w.causal)
-    torch.cuda.synchronize()
-    dq, dk, dv = to_f64(dq), to_f64(dk), to_f64(dv)
-    cu = x["cu"].tolist()
-    for b, h in ((0, 3), (1, 0), (1, 15), (5, 0), (5, 15)):
-        sl = slice(cu[b], cu[b + 1])
-        qq, kk, vv, gg = (to_f64(x[n][sl, h]) for n in ("q", "k", "v", "do"))
-        rq, rk, rv, _ = A.head_backward(qq, kk, vv, gg, w.scale, w.causal)
-        for name, got, want in (("dq", dq[sl, h], rq), ("dk", dk[sl, h], rk),
-                                ("dv", dv[sl, h], rv)):
-            e = rel_l2(got, want)
-            assert e <= BF16_GRAD, (b, h, name, e)
-
-
 # ------------------------------------------------------------- paged decode
 
 def paged_case(B, Hq, Hkv, seqlens, page, d, splits, seed, spare=3):
@@ -961,6 +832,32 @@ def test_decode_paged_tokens(fa_gpu, cfg, causal):
                                   x["block_table"].cpu().numpy(), seqlens, w.scale, causal)
     assert maxabs(to_f64(o), ro) <= BF16_O
     assert maxabs(to_f64(lse), rl) <= BF16_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_paged_tokens_fewer_keys_than_tokens(fa_gpu, causal):
+    """An entry with fewer keys than query tokens: under the end-aligned causal
+    mask its first tokens see no key, so every split is empty and the merge
+    must write O = 0 and LSE = -inf for them (not NaN); the other tokens and
+    entries match the oracle."""
+    B, Hq, Hkv, seqlens, page, d, splits, Nq = 3, 4, 2, (2, 300, 4), 16, 128, 4, 5
+    w, x = paged_case(B, Hq, Hkv, seqlens, page, d, splits, seed=65)
+    g = torch.Generator("cpu").manual_seed(66)
+    q = torch.randn(B, Hq, Nq, d, generator=g).to(torch.bfloat16).cuda()
+    say(f"decode paged tokens seqlens={seqlens} Nq={Nq} causal={causal}")
+    o, lse = fa_gpu.decode_paged_tokens(q, x["k_cache"], x["v_cache"], x["block_table"],
+                                        x["seqlens"], splits, causal=causal,
+                                        max_seqlen=max(seqlens))
+    torch.cuda.synchronize()
+    ro, rl = A.decode_paged_multi(to_f64(q), to_f64(x["k_cache"]), to_f64(x["v_cache"]),
+                                  x["block_table"].cpu().numpy(), seqlens, w.scale, causal)
+    on, ln = to_f64(o), to_f64(lse)
+    assert not np.isnan(on).any() and not np.isnan(ln).any()
+    dead = np.isneginf(rl)
+    assert dead.sum() == (Hq * (3 + 1) if causal else 0)   # 3 tokens of entry 0, 1 of entry 2
+    assert np.array_equal(np.isneginf(ln), dead) and not on[dead].any()
+    assert maxabs(on[~dead], ro[~dead]) <= BF16_O
+    assert maxabs(ln[~dead], rl[~dead]) <= BF16_LSE
 
 
 def test_decode_paged_tokens_one_token_is_paged_decode(fa_gpu):
@@ -1148,23 +1045,3 @@ def test_fp8_forward_bf16_backward(fa_gpu, causal):
         e = rel_l2(to_f64(got), want)
         assert e <= FP8_REL, (name, e)
 
-
-def test_fp8_config_sampled(fa_gpu):
-    """B=2 H=16 N=8192 d=128 with 0.1% outliers of magnitude 50 in Q and K,
-    rotated: sampled rows of every head against the oracle on the dequantised
-    operands; the error against exact attention on the unquantised inputs is
-    printed (it is dominated by e4m3 rounding of Q and K, not by the kernel)."""
-    w = WORKLOADS["fp8_fwd"]
-    x = {n: t.cuda() for n, t in make_inputs(w).items()}
-    say("fp8 forward full size")
-    o, lse, parts = fp8_pipeline(fa_gpu, x, x["signs"])
-    torch.cuda.synchronize()
-    rows = np.array([0, 1, 127, 128, 4095, 4096, 8191, 777])
-    dq, dk, dv = dequant_inputs(parts)
-    # dequantised Q/K are rotated; the oracle forward on them is the kernel's problem
-    ro, rl = A.forward(dq, dk, dv, w.scale, False, rows=rows)
-    og = to_f64(o)[:, :, rows]
-    assert rel_l2(og, ro) <= FP8_REL
-    exact, _ = A.forward(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), w.scale, False, rows=rows)
-    print(f"fp8 config: rel-L2 vs dequantised oracle {rel_l2(og, ro):.4f}, "
-          f"vs exact unquantised {rel_l2(og, exact):.4f}")

@@ -228,6 +228,20 @@ def test_backward_matches_torch_autograd_fp64(causal):
         assert np.abs(a - b.numpy()).max() < 1e-12
 
 
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, (5, 0)),
+                                           (False, (3, 2))])
+def test_head_forward_backward_equals_separate_calls(causal, window):
+    """The one-pass helper used by the full-size parity checks returns exactly
+    what head_forward and head_backward return (bit for bit)."""
+    N, d = 23, 8
+    q, k, v, do = rnd(N, d), rnd(N, d), rnd(N, d), rnd(N, d)
+    o, lse, dq, dk, dv = A.head_forward_backward(q, k, v, do, 0.4, causal, window)
+    ro, rl = A.head_forward(q, k, v, 0.4, causal, window=window)
+    rq, rk, rv, _ = A.head_backward(q, k, v, do, 0.4, causal, window)
+    for a, b in ((o, ro), (lse, rl), (dq, rq), (dk, rk), (dv, rv)):
+        assert np.array_equal(a, b)
+
+
 def test_delta_equals_rowwise_do_dot_o():
     """delta_i = sum_j P_ij dP_ij equals dO_i . O_i (the identity that lets a
     pre-pass compute it from O and dO)."""
@@ -292,6 +306,23 @@ def test_combine_matches_page_formula_with_unnormalised_partials():
     assert abs(lse - (mg + math.log((l_t * np.exp(m_t - mg)).sum()))) < 1e-14
 
 
+def test_combine_weighs_empty_chunks_zero_and_empty_rows_give_zero():
+    """A chunk with no visible key has lse_c = -inf: it must weigh nothing,
+    so merging with it equals merging the other chunks alone.  A row whose
+    chunks are all empty saw no key at all: O = 0 and lse = -inf (the
+    log-sum over an empty set), never NaN."""
+    S, d = 6, 4
+    op, lp = rnd(2, S, d), rnd(2, S) * 2
+    lp[0, [1, 4]] = -np.inf
+    lp[1, :] = -np.inf
+    o, lse = A.combine(op, lp)
+    keep = [0, 2, 3, 5]
+    o_ref, lse_ref = A.combine(op[0, keep], lp[0, keep])
+    assert np.abs(o[0] - o_ref).max() < 1e-14 and abs(lse[0] - lse_ref) < 1e-14
+    assert np.array_equal(o[1], np.zeros(d)) and lse[1] == -np.inf
+    assert not np.isnan(o).any()
+
+
 # -------------------------------------------------------------------- fp8 pins
 
 def test_e4m3_decode_matches_torch_all_codes():
@@ -348,6 +379,49 @@ def test_quantize_block_roundtrip_error_bound():
     assert zs == 1.0 and not zc.any()
 
 
+@pytest.mark.parametrize("block_rows", [128, 32])
+def test_quantize_multi_block_scales_and_partial_tail(block_rows):
+    """Per-block quantisation over several (b, h, row-block) slabs whose
+    maxima differ by four orders of magnitude, with a partial last block
+    ([CH18] §18.6.2 (1)(2): one scale s = amax / 448 per block).  For every
+    block: its stored scale is its own amax / 448, its largest element maps
+    to code +-448, and dequantising with that scale returns every element
+    within half an e4m3 step of the input.  A scale index shifted by one
+    block, a block sliced at the wrong rows, or a tail taken from the wrong
+    slab breaks these bounds by orders of magnitude."""
+    B, H, d = 2, 3, 16
+    nb_full = 3
+    N = nb_full * block_rows + block_rows // 4 + 3           # partial last block
+    nb = (N + block_rows - 1) // block_rows
+    x = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    mags = np.array([0.01, 1.0, 300.0, 7.0])
+    amax_ref = np.empty((B, H, nb))
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                r0, r1 = i * block_rows, min(N, (i + 1) * block_rows)
+                m = mags[(i + b + 2 * h) % len(mags)]
+                blk = x[b, h, r0:r1]
+                blk *= np.float32(m / np.abs(blk).max())   # amax of the block is exactly m
+                amax_ref[b, h, i] = np.abs(blk).max()
+    codes, scales = F8.quantize(x, block_rows)
+    assert scales.shape == (B, H, nb) and codes.shape == x.shape
+    deq = F8.dequantize(codes, scales, block_rows)
+    mag = F8.e4m3_decode(codes)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                r0, r1 = i * block_rows, min(N, (i + 1) * block_rows)
+                a = amax_ref[b, h, i]
+                assert scales[b, h, i] == np.float32(np.float32(a) / np.float32(448.0))
+                assert np.abs(mag[b, h, r0:r1]).max() == 448.0
+                xb = x[b, h, r0:r1].astype(np.float64)
+                err = np.abs(deq[b, h, r0:r1] - xb)
+                # half a step: 2^-4 relative for normals, 2^-10 * s for subnormals
+                bound = np.maximum(np.abs(xb) * 2.0 ** -4, a / 448 * 2.0 ** -10) * 1.0001
+                assert np.all(err <= bound), (b, h, i)
+
+
 def test_hadamard_rotation_properties():
     import scipy.linalg
     n = 128
@@ -388,6 +462,49 @@ def test_incoherent_processing_error_is_reported():
     print(f"quantised QK^T rel-L2: plain {plain:.4f}, rotated {rot:.4f}, ratio {plain / rot:.3f}")
     # two operands each rounded with relative error <= 2^-4
     assert plain < 2 * 2.0 ** -4 and rot < 2 * 2.0 ** -4
+
+
+def _outlier_inputs(n, d, seed, outliers=True):
+    r = np.random.default_rng(seed)
+    q, k, v = (r.standard_normal((1, 1, n, d)).astype(np.float32) for _ in range(3))
+    if outliers:
+        for t in (q, k):
+            flat = t.reshape(-1)
+            pos = r.choice(flat.size, int(round(1e-3 * flat.size)), replace=False)
+            flat[pos] = r.choice([-50.0, 50.0], pos.size)
+    return q, k, v, r.choice([-1.0, 1.0], d)
+
+
+def test_fp8_error_floor_against_exact_attention():
+    """The fp8 workload's 5e-2 bar measured against exact attention on the
+    unquantised inputs is out of reach of e4m3 operands on outlier data, at
+    any scale granularity: e4m3 keeps 3 mantissa bits, so every operand
+    carries a relative rounding error of up to 2^-4 whatever its block scale,
+    and a key with a magnitude-50 outlier gives scores of spread 50 * scale
+    ~ 4.4 whose rounding error (~0.1) moves the softmax weights by ~10%.
+    Pinned here with the oracle alone: per-block (128 rows) and per-row
+    scales, with and without the rotation, all stay above 5e-2; the same
+    pipeline on N(0,1) inputs without outliers stays below it."""
+    n, d = 1024, 128
+    sc = 1 / math.sqrt(d)
+
+    def e2e(q, k, v, signs, rot, rows):
+        qq = F8.rotate(q, signs).astype(np.float32) if rot else q
+        kk = F8.rotate(k, signs).astype(np.float32) if rot else k
+        deq = [F8.dequantize(*F8.quantize(t, rows), rows) for t in (qq, kk, v)]
+        o, _ = A.forward(*deq, sc, False)
+        ex, _ = A.forward(q, k, v, sc, False)
+        return np.linalg.norm(o - ex) / np.linalg.norm(ex)
+
+    q, k, v, signs = _outlier_inputs(n, d, 8305)
+    errs = {(rot, rows): e2e(q, k, v, signs, rot, rows) for rot in (False, True)
+            for rows in (128, 1)}
+    print("fp8 end-to-end rel-L2 vs exact on outlier data:", errs)
+    assert min(errs.values()) > 5e-2
+    q0, k0, v0, s0 = _outlier_inputs(n, d, 8305, outliers=False)
+    clean = e2e(q0, k0, v0, s0, False, 128)
+    print("without outliers:", clean)
+    assert clean < 5e-2
 
 
 # -------------------------------------------------------------- schedule pins
@@ -491,6 +608,30 @@ def test_decode_paged_multi_uniform_scores(causal):
                 cnt = n - Nq + t + 1 if causal else n
                 assert np.allclose(o[b, h, t], rows[:cnt].mean(axis=0), atol=1e-13)
                 assert abs(lse[b, h, t] - math.log(cnt)) < 1e-13
+
+
+def test_decode_paged_multi_fewer_keys_than_tokens():
+    """An entry shorter than the Nq tokens: with the end-aligned causal mask
+    token t sees logical keys 0 .. n-Nq+t, which is empty for the first
+    Nq-n tokens (O = 0, LSE = -inf); the others are the mean of the rows they
+    see under uniform scores.  Without the mask every token sees all n keys."""
+    page, Hkv, Hq, d, Nq = 16, 1, 2, 3, 5
+    lens = [2, 7]
+    cache_k, cache_v = rnd(3, page, Hkv, d), rnd(3, page, Hkv, d)
+    table = np.array([[2], [0]])
+    q = np.zeros((2, Hq, Nq, d))
+    for causal in (True, False):
+        o, lse = A.decode_paged_multi(q, cache_k, cache_v, table, lens, 0.7, causal)
+        for b, n in enumerate(lens):
+            rows = cache_v[table[b][0], :n, 0]
+            for h in range(Hq):
+                for t in range(Nq):
+                    cnt = min(n, n - Nq + t + 1) if causal else n
+                    if cnt <= 0:
+                        assert np.array_equal(o[b, h, t], np.zeros(d)) and lse[b, h, t] == -np.inf
+                    else:
+                        assert np.allclose(o[b, h, t], rows[:cnt].mean(axis=0), atol=1e-13)
+                        assert abs(lse[b, h, t] - math.log(cnt)) < 1e-13
 
 
 # ---------------------------------------------------------------- varlen pins
