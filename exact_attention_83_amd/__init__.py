@@ -61,6 +61,7 @@ _SIGS = {
                                  _P]),
     "fa_decode_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
+    "fa_decode_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P,
                         _I, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -182,6 +183,12 @@ def fa_decode_workspace_size(B, Hq, d, num_splits):
 def fa_decode_splitkv(q, k, v, o_part, lse_part, B, Hq, Hkv, Nk, d, scale, num_splits,
                       stream=None):
     _call("fa_decode_splitkv", _ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, Hq,
+          Hkv, Nk, d, scale, num_splits, _stream(stream))
+
+
+def fa_decode_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nk, d, scale, num_splits,
+                              stream=None):
+    _call("fa_decode_splitkv_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
           Hkv, Nk, d, scale, num_splits, _stream(stream))
 
 
@@ -348,6 +355,20 @@ def decode(q, k, v, num_splits, scale=None, stream=None, return_partials=False):
     if return_partials:
         return o, lse, o_part, lse_part
     return o, lse
+
+
+def decode_noalloc(q, k, v, num_splits, scale=None, stream=None, out=None, lse=None):
+    """decode() through fa_decode_splitkv_noalloc: the library keeps the split
+    partials in its own fixed device scratch.  Outputs are allocated here
+    unless ``out`` / ``lse`` are given (then nothing is allocated)."""
+    import torch
+    B, Hq, _, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    s = _default_scale(d, scale)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if lse is None else lse
+    fa_decode_splitkv_noalloc(q, k, v, o, l, B, Hq, Hkv, Nk, d, s, num_splits, stream)
+    return o, l
 
 
 def decode_tokens(q, k, v, num_splits, causal=False, scale=None, stream=None,

@@ -429,6 +429,24 @@ fa_status fa_decode_combine(const float* o_part, const float* lse_part, void* o,
       fa::launch_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream));
 }
 
+fa_status fa_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int Nk, int d, float scale,
+                                   int num_splits, hipStream_t stream) {
+  static_assert(fa::kNoAllocScratchBytes == FA_NOALLOC_SCRATCH_BYTES, "scratch size");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (fa_status s = check_shape(B, Hq, Hkv, 1, Nk, d)) return s;
+  if (!good_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (num_splits <= 0 || num_splits > Nk || Nk % num_splits != 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 32) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv * num_splits > (int64_t)1 << 30) return FA_ERR_UNSUPPORTED;
+  if (fa_decode_workspace_size(B, Hq, d, num_splits) > FA_NOALLOC_SCRATCH_BYTES)
+    return FA_ERR_WORKSPACE;
+  return hip_status(fa::launch_decode_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nk, d, scale,
+                                              num_splits, stream));
+}
+
 fa_status fa_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float* scales, int B,
                           int H, int N, int d, hipStream_t stream) {
   if (!aligned16(x) || !aligned16(x8) || !aligned16(scales)) return FA_ERR_INVALID_ARG;

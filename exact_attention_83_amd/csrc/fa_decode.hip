@@ -21,8 +21,19 @@
 // The work is bound by HBM reads of K and V (about 4 FLOP per byte); MFMA
 // waste on the padded n axis costs nothing that matters.
 
+#include <atomic>
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_launch.h"
+
+// Scratch for the no-allocation decode (fa_decode_splitkv_noalloc): the split
+// partials of one call, o_part then lse_part at the next 256-byte boundary.
+// Each GPU the library runs on holds its own copy until the process ends.  In
+// host code the name is only a stand-in for the symbol: its device address is
+// looked up once per device (fa::noalloc_scratch) and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[fa::kNoAllocScratchBytes];
 
 namespace fa {
 
@@ -373,6 +384,50 @@ hipError_t launch_decode_split_paged(const void* q, const void* k_cache, const v
                        o_part, lse_part, Hq, Hkv, 0, num_splits, scale, sl2, block_table,
                        seqlens, page_shift, max_pages, num_pages, chunk, Nq, causal ? 1 : 0);
   return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_lock;
+}  // namespace
+
+hipError_t noalloc_scratch(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> guard(g_scratch_lock);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      // with this device current: the address of its own copy of the array
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return hipSuccess;
+}
+
+hipError_t launch_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int B, int Hq, int Hkv, int Nk, int d, float scale,
+                                 int num_splits, hipStream_t stream) {
+  void* base = nullptr;
+  hipError_t e = noalloc_scratch(&base);
+  if (e != hipSuccess) return e;
+  // same layout as a caller's workspace of fa_decode_workspace_size bytes
+  const size_t rows = (size_t)B * Hq * num_splits;
+  const size_t o_bytes = (rows * d * sizeof(float) + 255) & ~size_t(255);
+  float* o_part = static_cast<float*>(base);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(base) + o_bytes);
+  e = launch_decode_split(q, k, v, o_part, lse_part, B, Hq, Hkv, Nk, d, scale, num_splits,
+                          stream);
+  if (e != hipSuccess) return e;
+  return launch_decode_combine(o_part, lse_part, o, lse, B, Hq, d, num_splits, stream);
 }
 
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o,

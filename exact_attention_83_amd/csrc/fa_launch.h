@@ -75,6 +75,17 @@ hipError_t launch_decode_split_paged(const void* q, const void* k_cache, const v
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o,
                                  float* lse, int B, int Hq, int d, int num_splits,
                                  hipStream_t stream);
+// Bytes of the fixed device scratch of the no-allocation decode (one copy per
+// GPU); equal to FA_NOALLOC_SCRATCH_BYTES of the C ABI.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+// Device address of this GPU's scratch (looked up once per device, with that
+// device current; no allocation).
+hipError_t noalloc_scratch(void** addr);
+// Split + combine with the partials in the scratch (the caller has checked
+// that fa_decode_workspace_size(B, Hq, d, num_splits) fits in it).
+hipError_t launch_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int B, int Hq, int Hkv, int Nk, int d, float scale,
+                                 int num_splits, hipStream_t stream);
 
 hipError_t launch_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float* scales,
                                int B, int H, int N, int d, hipStream_t stream);

@@ -29,7 +29,9 @@
  *     visible keys (natural log).
  *   - Ownership: the caller allocates and owns every buffer, workspaces
  *     included.  The library allocates no device memory and keeps no mutable
- *     global state, so concurrent calls on different streams are safe.
+ *     global state, so concurrent calls on different streams are safe.  The
+ *     one exception is fa_decode_splitkv_noalloc, which keeps its partials in
+ *     a fixed per-GPU scratch array (see there).
  *   - Calls are asynchronous on `stream`.  Argument errors are detected before
  *     anything is enqueued and return FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or
  *     FA_ERR_WORKSPACE; a failed kernel launch returns FA_ERR_HIP.  Faults in a
@@ -369,6 +371,28 @@ fa_status fa_decode_combine(const float* o_part, const float* lse_part,
 /* Bytes the caller must provide for o_part and lse_part together (one
  * allocation: o_part first, lse_part at the next 256-byte boundary). */
 size_t fa_decode_workspace_size(int B, int Hq, int d, int num_splits);
+
+/*
+ * Split-KV decode and its merge in one call that allocates nothing, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid it).  Same inputs, outputs and
+ * requirements as fa_decode_splitkv followed by fa_decode_combine:
+ *   q [B][Hq][1][d], k,v [B][Hkv][Nk][d] bf16 in; o [B][Hq][1][d] bf16 and
+ *   lse [B][Hq][1] fp32 out.
+ * The split partials go to a fixed scratch array in device memory that the
+ * library holds for each GPU it runs on, until the process ends, instead of a
+ * caller's workspace.  fa_decode_workspace_size(B, Hq, d, num_splits) must not
+ * exceed FA_NOALLOC_SCRATCH_BYTES (16 MiB; e.g. B=8, Hq=32, d=128, 64 splits
+ * needs 8.4 MB): a larger call returns FA_ERR_WORKSPACE and enqueues nothing.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap on
+ * one GPU (on different streams, or from different threads without ordering)
+ * race and give undefined output; calls ordered on one stream are safe.  The
+ * first call on a device looks up the scratch's address (no allocation).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+fa_status fa_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int Hq, int Hkv, int Nk, int d,
+                                    float scale, int num_splits, hipStream_t stream);
 
 /*
  * FP8 quantisation pre-pass ([CH18] §18.6.2 (1)(2); [L21] slide 24).

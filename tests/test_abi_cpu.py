@@ -161,6 +161,23 @@ def test_dense_paths_reject_slabs_past_2gib(lib):
     assert call_fwd(lib, Nq=64, Nk=big - 1, scale=0.0) == fa.FA_ERR_INVALID_ARG
 
 
+def test_noalloc_decode_validation(lib):
+    """The no-allocation decode refuses partials beyond its fixed scratch
+    (FA_ERR_WORKSPACE) and bad arguments before any HIP call."""
+    def call(**kw):
+        a = dict(B=8, Hq=32, Hkv=8, Nk=131072, d=128, scale=0.1, S=64)
+        a.update(kw)
+        return lib.fa_decode_splitkv_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"],
+                                             a["Hkv"], a["Nk"], a["d"], a["scale"], a["S"], None)
+    assert lib.fa_decode_workspace_size(8, 32, 128, 64) <= 16 << 20
+    assert call(Hq=64, S=128) == fa.FA_ERR_WORKSPACE          # 33.8 MB of partials
+    assert call(S=7) == fa.FA_ERR_INVALID_ARG
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_decode_splitkv_noalloc(FAKE, FAKE, FAKE, MIS, FAKE, 1, 1, 1, 64, 128, 0.1, 1,
+                                         None) == fa.FA_ERR_INVALID_ARG
+
+
 def test_binding_raises_value_error_on_bad_args(lib):
     with pytest.raises(ValueError):
         fa.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, 64, 128, 0.1, False, stream=0)
