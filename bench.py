@@ -2,8 +2,9 @@
 """Benchmark of the MI355X exact-attention library.
 
 One step = the headline workload's whole training pass: bf16 causal forward
-plus backward at B=2, H=16, N=8192, d=128 (fa_fwd, then fa_bwd's three
-stages: delta pre-pass, dK/dV kernel, dQ kernel), inputs resident in HBM.  The value is its aggregate throughput in
+plus backward at B=2, H=16, N=8192, d=128 (fa_fwd, then fa_bwd's two
+stages: the dQ kernel, which also forms delta = dO . O, and the dK/dV
+kernel), inputs resident in HBM.  The value is its aggregate throughput in
 TFLOP/s, counting 4*B*H*N*N*d/2 for the causal forward and 2.5x that for the
 backward.  The remaining rows of the path are timed after the steps, each on
 its own workload, and reported under "parts": the non-causal forward at the
@@ -72,36 +73,153 @@ def measured_traffic(path=TRAFFIC_PROFILE):
     return int(float(vals["traffic_bytes_per_launch"]))
 
 
-def cpu_baseline(w, min_seconds=10.0, max_heads=8):
-    """The fp64 oracle on the host cores: forward + backward of whole (b, h)
-    heads of the headline workload at full sequence length, head after head
-    until about `min_seconds` of CPU work (at most `max_heads` heads)."""
+def _host_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(fp8_sample=None, c3_seconds=8.0, max_heads=8):
+    """The fp64 oracle on the host cores, timed on a bounded sample of every
+    workload (whole heads at full length; decode: whole (b, KV head) slabs),
+    so the default run stays within minutes.  The headline value is the
+    causal workload's forward + backward rate.  With `fp8_sample` (two heads
+    of the fp8 workload's bf16 inputs and the GPU's fp8 output for them) the
+    fp8 output's relative L2 error against exact attention on the
+    unquantised inputs is measured here too, beside the oracle's own fp8
+    pipeline's error (the e4m3 floor)."""
     import numpy as np
     import torch
     from oracle import attention as A
-    from workloads import to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    g = torch.Generator("cpu").manual_seed(w.seed)
-    mk = lambda: to_f64(torch.randn(w.Nq, w.d, generator=g).to(torch.bfloat16))
-    heads, dt = 0, 0.0
-    while heads < max_heads and (heads == 0 or dt < min_seconds):
-        q, k, v, do = mk(), mk(), mk(), mk()
+    from oracle import fp8 as F8
+    from workloads import WORKLOADS, to_f64
+
+    per = {}
+    mk = lambda g, n, d: to_f64(torch.randn(n, d, generator=g).to(torch.bfloat16))
+
+    def run(name, w, heads_max, seconds, fn, flops_per_unit, unit_name):
+        g = torch.Generator("cpu").manual_seed(w.seed)
+        n, dt = 0, 0.0
+        while n < heads_max and (n == 0 or dt < seconds):
+            dt += fn(g)
+            n += 1
+        per[name] = {"seconds": round(dt, 3), "units": n, "unit": unit_name,
+                     "tflops": round(n * flops_per_unit / dt / 1e12, 6)}
+        return n, dt
+
+    # tiny fp32 B1 H1 N256 d64: forward + backward, best of 3
+    wt = WORKLOADS["tiny_f32"]
+
+    def tiny(g):
+        q, k, v, do = (torch.randn(wt.Nq, wt.d, generator=g).double().numpy() for _ in range(4))
+        best = 1e9
+        for _ in range(3):
+            t0 = time.perf_counter()
+            A.head_forward(q, k, v, wt.scale, wt.causal)
+            A.head_backward(q, k, v, do, wt.scale, wt.causal)
+            best = min(best, time.perf_counter() - t0)
+        return best
+    run("tiny_f32 fwd+bwd", wt, 1, 0, tiny, wt.fwd_flops() + wt.bwd_flops(), "whole problem")
+
+    # prefill d=64: forward of whole heads
+    wp = WORKLOADS["prefill_bf16"]
+
+    def prefill(g):
+        q, k, v = (mk(g, wp.Nq, wp.d) for _ in range(3))
+        t0 = time.perf_counter()
+        A.head_forward(q, k, v, wp.scale, False)
+        return time.perf_counter() - t0
+    one_p = wp.scaled(B=1, Hq=1, Hkv=1)
+    run("prefill_bf16 fwd", wp, 8, 1.0, prefill, one_p.fwd_flops(), "head")
+
+    # headline causal B2 H16 N8192 d128: forward + backward of whole heads
+    w = WORKLOADS["causal_bf16"]
+
+    def causal(g):
+        q, k, v, do = (mk(g, w.Nq, w.d) for _ in range(4))
         t0 = time.perf_counter()
         A.head_forward(q, k, v, w.scale, w.causal)
         A.head_backward(q, k, v, do, w.scale, w.causal)
-        dt += time.perf_counter() - t0
-        heads += 1
+        return time.perf_counter() - t0
     one = w.scaled(B=1, Hq=1, Hkv=1)
+    heads, dt = run("causal_bf16 fwd+bwd", w, max_heads, c3_seconds, causal,
+                    one.fwd_flops() + one.bwd_flops(), "head")
+
+    # split-KV decode: one (b, KV head) slab (its 4 query heads, 131072 keys)
+    wd = WORKLOADS["decode_gqa"]
+    G = wd.Hq // wd.Hkv
+
+    def decode(g):
+        q = to_f64(torch.randn(1, G, 1, wd.d, generator=g).to(torch.bfloat16))
+        kk = to_f64(torch.randn(1, 1, wd.Nk, wd.d, generator=g).to(torch.bfloat16))
+        vv = to_f64(torch.randn(1, 1, wd.Nk, wd.d, generator=g).to(torch.bfloat16))
+        t0 = time.perf_counter()
+        A.decode_split(q, kk, vv, wd.scale, wd.num_splits)
+        return time.perf_counter() - t0
+    run("decode_gqa split+combine", wd, 2, 1.0, decode, 4.0 * G * wd.Nk * wd.d, "(b, KV head)")
+
+    # fp8 forward: the oracle's fp8 pipeline (rotate, quantise, dequantise,
+    # forward) on whole heads
+    wf = WORKLOADS["fp8_fwd"]
+
+    def fp8(g):
+        q, k, v = (torch.randn(1, 1, wf.Nq, wf.d, generator=g).to(torch.bfloat16).float().numpy()
+                   for _ in range(3))
+        signs = np.where(np.arange(wf.d) % 3 == 0, -1.0, 1.0)
+        t0 = time.perf_counter()
+        deq = [F8.dequantize(*F8.quantize(F8.rotate(q, signs).astype(np.float32))),
+               F8.dequantize(*F8.quantize(F8.rotate(k, signs).astype(np.float32))),
+               F8.dequantize(*F8.quantize(v))]
+        A.forward(*deq, wf.scale, False)
+        return time.perf_counter() - t0
+    one_f = wf.scaled(B=1, Hq=1, Hkv=1)
+    run("fp8_fwd (emulated)", wf, 1, 0, fp8, one_f.fwd_flops(), "head")
+
+    fp8_err = None
+    if fp8_sample is not None:
+        rel = lambda a, b: float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        signs = fp8_sample["signs"].double().numpy()
+        e_gpu, e_floor = [], []
+        for h in range(fp8_sample["q"].shape[0]):
+            q, k, v = (fp8_sample[n][h].float().numpy()[None, None] for n in ("q", "k", "v"))
+            exact, _ = A.forward(q, k, v, wf.scale, False)
+            deq = [F8.dequantize(*F8.quantize(F8.rotate(q, signs).astype(np.float32))),
+                   F8.dequantize(*F8.quantize(F8.rotate(k, signs).astype(np.float32))),
+                   F8.dequantize(*F8.quantize(v))]
+            emul, _ = A.forward(*deq, wf.scale, False)
+            e_gpu.append(rel(fp8_sample["o"][h].double().numpy(), exact[0, 0]))
+            e_floor.append(rel(emul[0, 0], exact[0, 0]))
+        fp8_err = {"rel_l2_vs_exact": round(max(e_gpu), 4),
+                   "oracle_fp8_rel_l2_vs_exact": round(max(e_floor), 4),
+                   "heads": fp8_sample["heads"]}
+
     flops = heads * (one.fwd_flops() + one.bwd_flops())
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"forward+backward of {heads} of the {w.B * w.Hq} heads "
-                      f"(N={w.Nq}, d={w.d}, causal), numpy fp64"}
+    out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(_blas_threads()),
+           "kind": "oracle", "seconds": round(dt, 3),
+           "sample": f"forward+backward of {heads} of the {w.B * w.Hq} heads "
+                     f"(N={w.Nq}, d={w.d}, causal), numpy fp64; per_config: a bounded sample "
+                     "of every workload",
+           "per_config": per, "host": _host_info()}
+    return out, fp8_err
 
 
 def main(argv=None):
@@ -125,6 +243,7 @@ def main(argv=None):
     from workloads import WORKLOADS, make_inputs
 
     fa.load()
+    fp8_sample = None
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     parts = {}
@@ -153,19 +272,17 @@ def main(argv=None):
     def fwd(causal=True):
         fa.fa_fwd(q, k, v, o, lse, *args, w.scale, causal, sh)
 
-    def bwd_pre():
-        fa.fa_bwd_pre(o, do, ws, ws_bytes, w.B, w.Hq, w.Nq, w.d, sh)
+    # fa_bwd's two stages: dQ (which also writes delta = dO . O), then dK/dV
+    def bwd_dq():
+        fa.fa_bwd_dq_delta(q, k, v, o, do, lse, dq, ws, ws_bytes, *args, w.scale, True, sh)
 
     def bwd_dkdv():
         fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, ws_bytes, *args, w.scale, True, sh)
 
-    def bwd_dq():
-        fa.fa_bwd_dq(q, k, v, do, lse, dq, ws, ws_bytes, *args, w.scale, True, sh)
-
     ev = lambda: torch.cuda.Event(enable_timing=True)
     log("warmup")
     for _ in range(a.warmup):
-        fwd(); bwd_pre(); bwd_dkdv(); bwd_dq()
+        fwd(); bwd_dq(); bwd_dkdv()
     torch.cuda.synchronize()
     marks = [tuple(ev() for _ in range(6)) for _ in range(a.steps)]
     t_start, t_end = ev(), ev()
@@ -173,27 +290,26 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for f0, f1, k0, k1, q0_, q1_ in marks:
+    for f0, f1, q0_, q1_, k0, k1 in marks:
         f0.record(stream)
         fwd()
         f1.record(stream)
-        bwd_pre()
-        k0.record(stream)
-        bwd_dkdv()
-        k1.record(stream)
         q0_.record(stream)
         bwd_dq()
         q1_.record(stream)
+        k0.record(stream)
+        bwd_dkdv()
+        k1.record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / a.steps
     avg = lambda i, j: sum(m[i].elapsed_time(m[j]) for m in marks) / a.steps
-    fwd_ms, dkdv_ms, dq_ms = avg(0, 1), avg(2, 3), avg(4, 5)
-    # per-step spread: median and minimum of each step (forward start to dQ
-    # end) and of each dK/dV launch
+    fwd_ms, dq_ms, dkdv_ms = avg(0, 1), avg(2, 3), avg(4, 5)
+    # per-step spread: median and minimum of each step (forward start to
+    # dK/dV end) and of each dK/dV launch
     per_step = sorted(m[0].elapsed_time(m[5]) for m in marks)
-    per_dkdv = sorted(m[2].elapsed_time(m[3]) for m in marks)
+    per_dkdv = sorted(m[4].elapsed_time(m[5]) for m in marks)
     median = lambda xs: xs[len(xs) // 2] if len(xs) % 2 else 0.5 * (xs[len(xs) // 2 - 1] + xs[len(xs) // 2])
     step_flops = w.fwd_flops() + w.bwd_flops()
     value = step_flops / (ms_step * 1e-3) / 1e12
@@ -203,7 +319,7 @@ def main(argv=None):
     unit = w.fwd_flops() / 2
     kern = {"fwd_bf16_kernel<128,causal> (fa_fwd)": (w.fwd_flops(), fwd_ms),
             "bwd_dkdv_kernel<128,causal> (fa_bwd_dkdv)": (4 * unit, dkdv_ms),
-            "bwd_dq_kernel<128,causal> (fa_bwd_dq)": (3 * unit, dq_ms)}
+            "bwd_dq_kernel<128,causal,delta> (fa_bwd_dq_delta)": (3 * unit, dq_ms)}
     dom = max(kern, key=lambda n: kern[n][1])
     bwd_ms = ms_step - fwd_ms
     parts["fwd_causal"] = {"ms": round(fwd_ms, 4), "tflops": round(rate(w.fwd_flops(), fwd_ms), 1),
@@ -472,6 +588,11 @@ def main(argv=None):
                             "quant_GB/s": round(qbytes / (tq * 1e-3) / 1e9, 1),
                             "tflops_incl_quant": round(wf.fwd_flops() / ((t + tq) * 1e-3) / 1e12, 1)}
         log(f"fp8 fwd {t:.3f} ms {tf:.0f} TF, quant {tq:.3f} ms")
+        # two heads of inputs and output, for the error against exact
+        # attention measured in the CPU leg
+        fp8_sample = {"q": xf["q"][0, :2].cpu(), "k": xf["k"][0, :2].cpu(),
+                      "v": xf["v"][0, :2].cpu(), "o": of[0, :2].cpu(),
+                      "signs": xf["signs"].cpu(), "heads": [[0, 0], [0, 1]]}
         del xf
 
     result = {
@@ -501,7 +622,9 @@ def main(argv=None):
     }
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"], fp8_err = cpu_baseline(fp8_sample)
+        if fp8_err is not None:
+            parts["fp8_fwd"].update(fp8_err)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -39,6 +39,8 @@ _SIGS = {
                          _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _Z,
                        _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_bwd_dq_delta": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                             _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_bwd_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                         _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -165,6 +167,13 @@ def fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, workspace_bytes, B, Hq, H
 def fa_bwd_dq(q, k, v, dout, lse, dq, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale,
               causal, stream=None):
     _call("fa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq),
+          _ptr(workspace), workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
+          _stream(stream))
+
+
+def fa_bwd_dq_delta(q, k, v, o, dout, lse, dq, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk,
+                    d, scale, causal, stream=None):
+    _call("fa_bwd_dq_delta", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
           _ptr(workspace), workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
           _stream(stream))
 

@@ -164,14 +164,14 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                                Hq, Hkv, Nq, Nk, d, scale, causal))
     return s;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // dQ first: it also forms delta = dO . O for its rows (no pre-pass), which
+  // the dK/dV kernel then reads
   float* delta = static_cast<float*>(workspace);
-  hipError_t e = fa::launch_bwd_pre(o, dout, delta, B, Hq, Nq, d, stream);
+  hipError_t e = fa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Nq, Nk, d, scale,
+                                   causal != 0, stream, -1, -1, o);
   if (e == hipSuccess)
     e = fa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
                             causal != 0, stream);
-  if (e == hipSuccess)
-    e = fa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Nq, Nk, d, scale,
-                          causal != 0, stream);
   return hip_status(e);
 }
 
@@ -187,13 +187,11 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (Nq != Nk) return FA_ERR_UNSUPPORTED;
   float* delta = static_cast<float*>(workspace);
-  hipError_t e = fa::launch_bwd_pre(o, dout, delta, B, Hq, Nq, d, stream);
+  hipError_t e = fa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Nq, Nk, d, scale,
+                                   causal != 0, stream, window_left, window_right, o);
   if (e == hipSuccess)
     e = fa::launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
                             causal != 0, stream, window_left, window_right);
-  if (e == hipSuccess)
-    e = fa::launch_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Nq, Nk, d, scale,
-                          causal != 0, stream, window_left, window_right);
   return hip_status(e);
 }
 
@@ -225,15 +223,13 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   if (workspace == nullptr || !aligned16(workspace)) return FA_ERR_WORKSPACE;
   if (workspace_bytes < fa_bwd_workspace_size(1, Hq, total_q, d)) return FA_ERR_WORKSPACE;
   float* delta = static_cast<float*>(workspace);
-  hipError_t e = fa::launch_bwd_pre(o, dout, delta, 1, 1, total_q * Hq, d, stream, Hq);
+  hipError_t e = fa::launch_bwd_dq_varlen(q, k, v, dout, lse, delta, dq, cu_seqlens_q,
+                                          cu_seqlens_k, batch, Hq, Hkv, total_q, max_seqlen_q, d,
+                                          scale, causal != 0, stream, o);
   if (e == hipSuccess)
     e = fa::launch_bwd_dkdv_varlen(q, k, v, dout, lse, delta, dk, dv, cu_seqlens_q,
                                    cu_seqlens_k, batch, Hq, Hkv, total_q, max_seqlen_k, d,
                                    scale, causal != 0, stream);
-  if (e == hipSuccess)
-    e = fa::launch_bwd_dq_varlen(q, k, v, dout, lse, delta, dq, cu_seqlens_q, cu_seqlens_k,
-                                 batch, Hq, Hkv, total_q, max_seqlen_q, d, scale, causal != 0,
-                                 stream);
   return hip_status(e);
 }
 
@@ -266,12 +262,9 @@ fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const
     return FA_ERR_WORKSPACE;
   float* delta = static_cast<float*>(workspace);
   uint8_t* map = static_cast<uint8_t*>(workspace) + fa_bwd_workspace_size(B, Hq, Nq, d);
-  hipError_t e = fa::launch_bwd_pre(o, dout, delta, B, Hq, Nq, d, stream);
-  if (e == hipSuccess)
-    e = fa::launch_bwd_bf16_sparse(q, k, v, dout, lse, delta, map, dq, dk, dv, q_tile_ptr,
-                                   kv_block_idx, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0,
-                                   stream);
-  return hip_status(e);
+  return hip_status(fa::launch_bwd_bf16_sparse(q, k, v, dout, lse, delta, map, dq, dk, dv,
+                                               q_tile_ptr, kv_block_idx, B, Hq, Hkv, Nq, Nk, d,
+                                               scale, causal != 0, stream, o));
 }
 
 fa_status fa_bwd_pre(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
@@ -308,8 +301,23 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
                                workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, causal))
     return s;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  return hip_status(fa::launch_bwd_dq(q, k, v, dout, lse, static_cast<const float*>(workspace),
-                                      dq, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream));
+  // (reads the delta fa_bwd_pre wrote; nothing is written to the workspace)
+  return hip_status(fa::launch_bwd_dq(q, k, v, dout, lse,
+                                      static_cast<float*>(const_cast<void*>(workspace)), dq, B,
+                                      Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream));
+}
+
+fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* workspace,
+                          size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                          float scale, int causal, hipStream_t stream) {
+  // dk and dv are not touched by this stage; q stands in for them
+  if (fa_status s = bwd_common(q, k, v, o, dout, lse, dq, q, q, workspace, workspace_bytes, B,
+                               Hq, Hkv, Nq, Nk, d, scale, causal))
+    return s;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_bwd_dq(q, k, v, dout, lse, static_cast<float*>(workspace), dq, B,
+                                      Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream, -1, -1, o));
 }
 
 fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,

@@ -683,16 +683,20 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 // row-major K tile.  K/V tiles of 64 keys are double-buffered in LDS.
 // WIN: sliding window as for bwd_dkdv_kernel; only the key tiles that some
 // row's window reaches are visited.
-template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false>
+// DELTA: the kernel forms its rows' delta = dO . O itself (from O, beside the
+// dO rows it holds) and writes it to Delta for the dK/dV kernel that runs after
+// it; otherwise it reads Delta from the pre-pass.
+template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false,
+          bool DELTA = false>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta,
+    const float* __restrict__ LSE, float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale,
     float scale_log2, int BH, int nqt, int win_l = -1, int win_r = -1,
     const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
     int total_q = 0, const int* __restrict__ sp_ptr = nullptr,
-    const int* __restrict__ sp_idx = nullptr) {
+    const int* __restrict__ sp_idx = nullptr, const uint16_t* __restrict__ O = nullptr) {
   constexpr int NW = kDqWaves;
   constexpr int BR = kDqBr;
   constexpr int BC = kDqBc;
@@ -741,6 +745,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   const int qrow = q0 + wave * 32 + l32;
   const int qrow_c = qrow < Nq ? qrow : Nq - 1;
   u32x4 qf[KSTEPS], gf[KSTEPS];
+  u32x4 of[DELTA ? KSTEPS : 1];
   {
     const uint16_t* qr = Q + q_off + (size_t)qrow_c * SQ;
     const uint16_t* gr = dO + q_off + (size_t)qrow_c * SQ;
@@ -749,12 +754,33 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
       qf[ks] = ldg<u32x4>(qr + ks * 16 + hf * 8);
       gf[ks] = ldg<u32x4>(gr + ks * 16 + hf * 8);
     }
+    if constexpr (DELTA) {
+      // this lane's half of its row of O, in the layout of its dO elements
+      const uint16_t* orow = O + q_off + (size_t)qrow_c * SQ;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) of[ks] = ldg<u32x4>(orow + ks * 16 + hf * 8);
+    }
   }
   float lse2 = LSE[l_off + qrow_c] * kLog2e;
   // a row that sees no key (lse = -inf, possible only with a sparse pattern)
   // gets P = 0: every score of it is masked, and -inf - (+inf) = -inf
   if constexpr (SPARSE) lse2 = lse2 == -INFINITY ? INFINITY : lse2;
-  const float dlt = Delta[l_off + qrow_c];
+  float dlt;
+  if constexpr (DELTA) {
+    // delta_i = dO_i . O_i ([CH18] §18.4.4: rowsum(P * dP) = dO_i . O_i);
+    // the two lane halves hold the two halves of the row
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(bf16_lo(of[ks][w]), bf16_lo(gf[ks][w]), acc);
+        acc = fmaf(bf16_hi(of[ks][w]), bf16_hi(gf[ks][w]), acc);
+      }
+    dlt = sum_halves(acc);
+  } else {
+    dlt = Delta[l_off + qrow_c];
+  }
 
   int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
   int jf = 0;  // first key tile visited
@@ -960,6 +986,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   }
   wait_vmem();  // the reloads of the last tile
 
+  // (written last: a store among the loop's loads would upset its exact
+  // load-count waits)
+  if constexpr (DELTA)
+    if (hf == 0 && qrow < Nq) Delta[l_off + qrow] = dlt;
   // dQ = scale * dQ^T, written as bf16 rows.
   if (qrow < Nq) {
     uint16_t* op = dQ + q_off + (size_t)qrow * SQ;
@@ -1045,9 +1075,9 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                         const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                         const float* lse, float* delta, void* dq, int B, int Hq, int Hkv,
                          int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream,
-                         int win_l, int win_r) {
+                         int win_l, int win_r, const void* o) {
   const int BH = B * Hq;
   const int nqt = (Nq + kDqBr - 1) / kDqBr;
   dim3 grid(BH * nqt), block(kDqWaves * 64);
@@ -1056,10 +1086,18 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   auto V = (const uint16_t*)v;
   auto G = (const uint16_t*)dout;
   auto dQ = (uint16_t*)dq;
+  auto Op = (const uint16_t*)o;
   const float sl2 = scale * kLog2e;
-#define FA_LAUNCH_DQ(DD, CC, WW)                                                              \
-  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW>), grid, block, 0, stream, Q, K, V, G, lse,     \
-                     delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, win_l, win_r)
+#define FA_LAUNCH_DQ(DD, CC, WW)                                                                 \
+  do {                                                                                           \
+    if (Op)                                                                                      \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW, false, false, true>), grid, block, 0, stream, \
+                         Q, K, V, G, lse, delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, win_l,  \
+                         win_r, nullptr, nullptr, 0, nullptr, nullptr, Op);                        \
+    else                                                                                         \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW>), grid, block, 0, stream, Q, K, V, G, lse,     \
+                         delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, win_l, win_r);           \
+  } while (0)
   const bool win = win_l >= 0 || win_r >= 0;
   if (d == 128) {
     if (win) {
@@ -1112,10 +1150,10 @@ hipError_t launch_bwd_dkdv_varlen(const void* q, const void* k, const void* v, c
 }
 
 hipError_t launch_bwd_dq_varlen(const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* delta, void* dq, const int* cu_q,
+                                const float* lse, float* delta, void* dq, const int* cu_q,
                                 const int* cu_k, int batch, int Hq, int Hkv, int total_q,
                                 int max_seqlen_q, int d, float scale, bool causal,
-                                hipStream_t stream) {
+                                hipStream_t stream, const void* o) {
   const int BH = batch * Hq;
   const int nqt = (max_seqlen_q + kDqBr - 1) / kDqBr;
   dim3 grid(BH * nqt), block(kDqWaves * 64);
@@ -1124,10 +1162,19 @@ hipError_t launch_bwd_dq_varlen(const void* q, const void* k, const void* v, con
   auto V = (const uint16_t*)v;
   auto G = (const uint16_t*)dout;
   auto dQ = (uint16_t*)dq;
+  auto Op = (const uint16_t*)o;
   const float sl2 = scale * kLog2e;
 #define FA_LAUNCH_DQ_VL(DD, CC)                                                                  \
-  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, false, true>), grid, block, 0, stream, Q, K, V, G, lse, \
-                     delta, dQ, Hq, Hkv, 0, 0, scale, sl2, BH, nqt, -1, -1, cu_q, cu_k, total_q)
+  do {                                                                                           \
+    if (Op)                                                                                      \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, false, true, false, true>), grid, block, 0,      \
+                         stream, Q, K, V, G, lse, delta, dQ, Hq, Hkv, 0, 0, scale, sl2, BH, nqt, \
+                         -1, -1, cu_q, cu_k, total_q, nullptr, nullptr, Op);                     \
+    else                                                                                         \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, false, true>), grid, block, 0, stream, Q, K, V,  \
+                         G, lse, delta, dQ, Hq, Hkv, 0, 0, scale, sl2, BH, nqt, -1, -1, cu_q,     \
+                         cu_k, total_q);                                                         \
+  } while (0)
   if (d == 128) {
     if (causal) FA_LAUNCH_DQ_VL(128, true);
     else FA_LAUNCH_DQ_VL(128, false);
@@ -1162,10 +1209,10 @@ __global__ __launch_bounds__(256) void sparse_block_map_kernel(const int* __rest
 }
 
 hipError_t launch_bwd_bf16_sparse(const void* q, const void* k, const void* v, const void* dout,
-                                  const float* lse, const float* delta, uint8_t* map, void* dq,
+                                  const float* lse, float* delta, uint8_t* map, void* dq,
                                   void* dk, void* dv, const int* sp_ptr, const int* sp_idx, int B,
                                   int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                                  bool causal, hipStream_t stream) {
+                                  bool causal, hipStream_t stream, const void* o) {
   const int nqb = (Nq + kSpBq - 1) / kSpBq;
   const int nkb = (Nk + kSpBk - 1) / kSpBk;
   hipLaunchKernelGGL(sparse_block_map_kernel, dim3(nqb), dim3(256), 0, stream, sp_ptr, sp_idx,
@@ -1174,7 +1221,32 @@ hipError_t launch_bwd_bf16_sparse(const void* q, const void* k, const void* v, c
   auto K = (const uint16_t*)k;
   auto V = (const uint16_t*)v;
   auto G = (const uint16_t*)dout;
+  auto Op = (const uint16_t*)o;
   const float sl2 = scale * kLog2e;
+  // dQ first: with o given it also writes delta, which dK/dV then reads
+  const int BH = B * Hq;
+  const int nqt = (Nq + kDqBr - 1) / kDqBr;
+  dim3 grid_q(BH * nqt), block_q(kDqWaves * 64);
+  auto dQ = (uint16_t*)dq;
+#define FA_LAUNCH_DQ_SP(DD, CC)                                                                  \
+  do {                                                                                           \
+    if (Op)                                                                                      \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, false, false, true, true>), grid_q, block_q, 0,  \
+                         stream, Q, K, V, G, lse, delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH,    \
+                         nqt, -1, -1, nullptr, nullptr, 0, sp_ptr, sp_idx, Op);                  \
+    else                                                                                         \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, false, false, true>), grid_q, block_q, 0, stream, \
+                         Q, K, V, G, lse, delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, -1,    \
+                         -1, nullptr, nullptr, 0, sp_ptr, sp_idx);                               \
+  } while (0)
+  if (d == 128) {
+    if (causal) FA_LAUNCH_DQ_SP(128, true);
+    else FA_LAUNCH_DQ_SP(128, false);
+  } else {
+    if (causal) FA_LAUNCH_DQ_SP(64, true);
+    else FA_LAUNCH_DQ_SP(64, false);
+  }
+#undef FA_LAUNCH_DQ_SP
   const int BHkv = B * Hkv;
   dim3 grid_kv(BHkv * ((Nk + kKvBkv - 1) / kKvBkv)), block_kv(kKvWaves * 64);
   auto dK = (uint16_t*)dk;
@@ -1191,22 +1263,6 @@ hipError_t launch_bwd_bf16_sparse(const void* q, const void* k, const void* v, c
     else FA_LAUNCH_DKDV_SP(64, false);
   }
 #undef FA_LAUNCH_DKDV_SP
-  const int BH = B * Hq;
-  const int nqt = (Nq + kDqBr - 1) / kDqBr;
-  dim3 grid_q(BH * nqt), block_q(kDqWaves * 64);
-  auto dQ = (uint16_t*)dq;
-#define FA_LAUNCH_DQ_SP(DD, CC)                                                                 \
-  hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, false, false, true>), grid_q, block_q, 0, stream, Q, \
-                     K, V, G, lse, delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, -1, -1,      \
-                     nullptr, nullptr, 0, sp_ptr, sp_idx)
-  if (d == 128) {
-    if (causal) FA_LAUNCH_DQ_SP(128, true);
-    else FA_LAUNCH_DQ_SP(128, false);
-  } else {
-    if (causal) FA_LAUNCH_DQ_SP(64, true);
-    else FA_LAUNCH_DQ_SP(64, false);
-  }
-#undef FA_LAUNCH_DQ_SP
   return hipGetLastError();
 }
 

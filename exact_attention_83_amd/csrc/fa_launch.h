@@ -39,26 +39,29 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            const float* lse, const float* delta, void* dk, void* dv, int B,
                            int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal,
                            hipStream_t stream, int win_l = -1, int win_r = -1);
+// o given: the dQ kernel forms delta = dO . O itself and writes it to `delta`
+// (launch it before dK/dV, which reads it); o null: it reads `delta`.
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                         const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                         const float* lse, float* delta, void* dq, int B, int Hq, int Hkv,
                          int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream,
-                         int win_l = -1, int win_r = -1);
+                         int win_l = -1, int win_r = -1, const void* o = nullptr);
 hipError_t launch_bwd_dkdv_varlen(const void* q, const void* k, const void* v, const void* dout,
                                   const float* lse, const float* delta, void* dk, void* dv,
                                   const int* cu_q, const int* cu_k, int batch, int Hq, int Hkv,
                                   int total_q, int max_seqlen_k, int d, float scale, bool causal,
                                   hipStream_t stream);
 hipError_t launch_bwd_dq_varlen(const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* delta, void* dq, const int* cu_q,
+                                const float* lse, float* delta, void* dq, const int* cu_q,
                                 const int* cu_k, int batch, int Hq, int Hkv, int total_q,
                                 int max_seqlen_q, int d, float scale, bool causal,
-                                hipStream_t stream);
+                                hipStream_t stream, const void* o = nullptr);
 // map: nqb * nkb bytes of scratch (query tiles of 256 rows x key blocks of 64).
+// o given: the dQ kernel (launched first) writes delta; else delta is read.
 hipError_t launch_bwd_bf16_sparse(const void* q, const void* k, const void* v, const void* dout,
-                                  const float* lse, const float* delta, uint8_t* map, void* dq,
+                                  const float* lse, float* delta, uint8_t* map, void* dq,
                                   void* dk, void* dv, const int* sp_ptr, const int* sp_idx, int B,
                                   int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                                  bool causal, hipStream_t stream);
+                                  bool causal, hipStream_t stream, const void* o = nullptr);
 
 // Nq query tokens per (b, head) ([B][Hq][Nq][d]; G*Nq <= 32), partials
 // [B][Hq][Nq][S][d] / [B][Hq][Nq][S]; causal: token t sees keys <= Nk-Nq+t.

@@ -248,6 +248,11 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  *                dO_i . O_i).
  *   fa_bwd_dkdv: dk and dv written.
  *   fa_bwd_dq:   dq written.
+ * fa_bwd itself runs the two-stage order fa_bwd_dq_delta + fa_bwd_dkdv: the
+ * dQ kernel, which holds each row's dO, reads the row's O beside it and
+ * writes delta itself, so no pre-pass is launched.
+ *   fa_bwd_dq_delta: dq written, and delta into the workspace; fa_bwd_dkdv
+ *                must follow it on the stream (or be ordered after it).
  */
 fa_status fa_bwd_pre(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Nq, int d, hipStream_t stream);
@@ -259,6 +264,10 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
                     const float* lse, void* dq, const void* workspace, size_t workspace_bytes,
                     int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                     hipStream_t stream);
+fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* workspace,
+                          size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                          float scale, int causal, hipStream_t stream);
 
 /* Backward, fp32 tensors, d == 64.  Same meaning as fa_bwd; deterministic. */
 fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
