@@ -68,6 +68,7 @@ _SIGS = {
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P,
                         _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_schedule": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _I]),
+    "fa_persistent_schedule": (_I, [_I, _I, _P, _I]),
 }
 
 _lib = None
@@ -299,6 +300,17 @@ def fa_fwd_schedule(B, Hq, Nq, Nk, d, causal):
     n2 = lib.fa_fwd_schedule(B, Hq, Nq, Nk, d, int(causal), *[ctypes.addressof(a) for a in arr], n)
     assert n2 == n
     return [list(a) for a in arr]
+
+
+def fa_persistent_schedule(n_units, grid):
+    """Workgroup of a persistent grid that takes each position of the
+    longest-first unit list (a list of n_units ints)."""
+    lib = load()
+    arr = (ctypes.c_int * max(n_units, 1))()
+    n = lib.fa_persistent_schedule(n_units, grid, ctypes.addressof(arr), n_units)
+    if n < 0:
+        raise ValueError("fa_persistent_schedule: invalid arguments")
+    return list(arr)[:n_units]
 
 
 # ---------------------------------------------------------- torch conveniences

@@ -479,6 +479,10 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                                        Nq, Nk, d, scale, causal != 0, stream));
 }
 
+int fa_persistent_schedule(int n_units, int grid, int* worker_out, int capacity) {
+  return fa::persistent_schedule(n_units, grid, worker_out, capacity);
+}
+
 int fa_fwd_schedule(int B, int Hq, int Nq, int Nk, int d, int causal, int* bh_out,
                     int* qtile_out, int* cost_out, int capacity) {
   if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return -1;

@@ -243,15 +243,15 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk, int stride = RO
 // WIN: sliding window (key j visible to query i iff i - win_l <= j <= i +
 // win_r; negative = unbounded): only the query tiles whose windows reach this
 // work unit's keys are visited.
-template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false>
-__global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
+template <int D, bool CAUSAL, bool WIN, bool VARLEN, bool SPARSE>
+__device__ __forceinline__ void bwd_dkdv_unit(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq_arg,
-    int Nk_arg, float scale, float scale_log2, int BHkv, int win_l = -1, int win_r = -1,
-    const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
-    int total_q = 0, const uint8_t* __restrict__ sp_map = nullptr, int sp_nkb = 0) {
+    int Nk_arg, float scale, float scale_log2, int BHkv, int win_l, int win_r,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q,
+    const uint8_t* __restrict__ sp_map, int sp_nkb, int unit) {
   constexpr int NW = kKvWaves;
   constexpr int KB = kKvKb;
   constexpr int BQ = kKvBq;
@@ -268,13 +268,17 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char s0[SLOT], s1[SLOT];
   auto sslot = [&](int sl) -> char* { return sl == 0 ? s0 : s1; };
 
-  const int tid = threadIdx.x;
+  // (opaque to the optimiser: per-lane offsets derived from it are then
+  // recomputed for each unit of a persistent loop instead of being kept
+  // live, and spilled, across it)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int t = blockIdx.x;
+  const int t = unit;
   const int bhk = t % BHkv;
   const int jt = t / BHkv;  // ascending KV tiles = longest first under causal
   const int b = bhk / Hkv;
@@ -675,6 +679,22 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
       }
 }
 
+// The dK/dV kernel: one workgroup per key tile, launched in longest-first
+// order (a persistent grid over the same list measured no faster here).
+template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false>
+__global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq_arg,
+    int Nk_arg, float scale, float scale_log2, int BHkv, int win_l = -1, int win_r = -1,
+    const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
+    int total_q = 0, const uint8_t* __restrict__ sp_map = nullptr, int sp_nkb = 0) {
+  bwd_dkdv_unit<D, CAUSAL, WIN, VARLEN, SPARSE>(Q, K, V, dO, LSE, Delta, dK, dV, Hq, Hkv, Nq_arg,
+                                                Nk_arg, scale, scale_log2, BHkv, win_l, win_r,
+                                                cu_q, cu_k, total_q, sp_map, sp_nkb, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // dQ.  The forward's structure with keys on the MFMA m axis: S^T = K Q^T and
 // dP^T = V dO^T with this wave's 32 queries on n (Q and dO rows in registers),
@@ -686,17 +706,15 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 // DELTA: the kernel forms its rows' delta = dO . O itself (from O, beside the
 // dO rows it holds) and writes it to Delta for the dK/dV kernel that runs after
 // it; otherwise it reads Delta from the pre-pass.
-template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false,
-          bool DELTA = false>
-__global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
+template <int D, bool CAUSAL, bool WIN, bool VARLEN, bool SPARSE, bool DELTA>
+__device__ __forceinline__ void bwd_dq_unit(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, float* __restrict__ Delta,
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale,
-    float scale_log2, int BH, int nqt, int win_l = -1, int win_r = -1,
-    const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
-    int total_q = 0, const int* __restrict__ sp_ptr = nullptr,
-    const int* __restrict__ sp_idx = nullptr, const uint16_t* __restrict__ O = nullptr) {
+    float scale_log2, int BH, int nqt, int win_l, int win_r, const int* __restrict__ cu_q,
+    const int* __restrict__ cu_k, int total_q, const int* __restrict__ sp_ptr,
+    const int* __restrict__ sp_idx, const uint16_t* __restrict__ O, int unit) {
   constexpr int NW = kDqWaves;
   constexpr int BR = kDqBr;
   constexpr int BC = kDqBc;
@@ -711,14 +729,18 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   auto kslot = [&](int sl) -> char* { return sl == 0 ? k0s : sl == 1 ? k1s : k2s; };
   auto vslot = [&](int sl) -> char* { return sl == 0 ? v0s : sl == 1 ? v1s : v2s; };
 
-  const int tid = threadIdx.x;
+  // (opaque to the optimiser: per-lane offsets derived from it are then
+  // recomputed for each unit of a persistent loop instead of being kept
+  // live, and spilled, across it)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
   int bh, qt;
-  query_tile_of(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
+  query_tile_of(unit, BH, nqt, CAUSAL, &bh, &qt);
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int hk = h / (Hq / Hkv);
@@ -1004,6 +1026,39 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
   }
 }
 
+// The dQ kernel: one workgroup per query tile in longest-first order, or
+// (PERSIST) a persistent grid walking that list in snake order, as for the
+// forward.
+template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false,
+          bool DELTA = false, bool PERSIST = false>
+__global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, float* __restrict__ Delta,
+    uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale,
+    float scale_log2, int BH, int nqt, int win_l = -1, int win_r = -1,
+    const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
+    int total_q = 0, const int* __restrict__ sp_ptr = nullptr,
+    const int* __restrict__ sp_idx = nullptr, const uint16_t* __restrict__ O = nullptr) {
+  if constexpr (PERSIST) {
+    const int n = BH * nqt;
+    for (int i = 0;; ++i) {
+      const int p = persistent_position(i, blockIdx.x, gridDim.x);
+      if (p >= n) break;
+      bwd_dq_unit<D, CAUSAL, WIN, VARLEN, SPARSE, DELTA>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv,
+                                                         Nq_arg, Nk_arg, scale, scale_log2, BH,
+                                                         nqt, win_l, win_r, cu_q, cu_k, total_q,
+                                                         sp_ptr, sp_idx, O, p);
+      __syncthreads();  // every wave is done with the LDS slots before the next unit
+    }
+  } else {
+    bwd_dq_unit<D, CAUSAL, WIN, VARLEN, SPARSE, DELTA>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv,
+                                                       Nq_arg, Nk_arg, scale, scale_log2, BH, nqt,
+                                                       win_l, win_r, cu_q, cu_k, total_q, sp_ptr,
+                                                       sp_idx, O, blockIdx.x);
+  }
+}
+
 // ---------------------------------------------------------------------------
 
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
@@ -1098,13 +1153,26 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
       hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW>), grid, block, 0, stream, Q, K, V, G, lse,     \
                          delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, win_l, win_r);           \
   } while (0)
+  // causal: a persistent grid over the longest-first list (as for the forward)
+#define FA_LAUNCH_DQ_PERSIST(DD)                                                                 \
+  do {                                                                                           \
+    const dim3 pg(persistent_grid(BH * nqt));                                                    \
+    if (Op)                                                                                      \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, true, false, false, false, true, true>), pg, block, 0, \
+                         stream, Q, K, V, G, lse, delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, \
+                         -1, -1, nullptr, nullptr, 0, nullptr, nullptr, Op);                      \
+    else                                                                                         \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, true, false, false, false, false, true>), pg, block,  \
+                         0, stream, Q, K, V, G, lse, delta, dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH,  \
+                         nqt);                                                                   \
+  } while (0)
   const bool win = win_l >= 0 || win_r >= 0;
   if (d == 128) {
     if (win) {
       if (causal) FA_LAUNCH_DQ(128, true, true);
       else FA_LAUNCH_DQ(128, false, true);
     } else {
-      if (causal) FA_LAUNCH_DQ(128, true, false);
+      if (causal) FA_LAUNCH_DQ_PERSIST(128);
       else FA_LAUNCH_DQ(128, false, false);
     }
   } else {
@@ -1112,11 +1180,12 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
       if (causal) FA_LAUNCH_DQ(64, true, true);
       else FA_LAUNCH_DQ(64, false, true);
     } else {
-      if (causal) FA_LAUNCH_DQ(64, true, false);
+      if (causal) FA_LAUNCH_DQ_PERSIST(64);
       else FA_LAUNCH_DQ(64, false, false);
     }
   }
 #undef FA_LAUNCH_DQ
+#undef FA_LAUNCH_DQ_PERSIST
   return hipGetLastError();
 }
 

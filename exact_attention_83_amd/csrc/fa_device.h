@@ -114,6 +114,17 @@ __host__ __device__ inline void query_tile_of(int t, int BH, int nqt, bool causa
   *qt = causal ? (nqt - 1 - t / BH) : (t / BH);
 }
 
+// Persistent grids: workgroup w of G takes the positions of the longest-first
+// unit list in snake order, w, 2G-1-w, 2G+w, 4G-1-w, ... (round i).  On a
+// list sorted by non-increasing cost this pairs the longest remaining units
+// of one round with the shortest of the next ([L21] slides 26-46: a
+// persistent grid whose work is handed out longest first).  Positions grow
+// with i, so a workgroup stops at its first position past the list.
+__host__ __device__ inline int persistent_position(int i, int w, int G) {
+  const int r = i >> 1;
+  return (i & 1) ? (2 * r + 2) * G - 1 - w : 2 * r * G + w;
+}
+
 template <int N>
 struct IntConst {
   static constexpr int value = N;

@@ -9,6 +9,18 @@
 
 namespace fa {
 
+// Workgroups of a persistent grid over `units` work units: one per compute
+// unit of the current device (the forward and dQ kernels each hold a whole
+// compute unit), never more than there are units.
+inline int persistent_grid(int units) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return units < cus ? units : cus;
+}
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                            bool causal, hipStream_t stream, int win_l = -1, int win_r = -1);
@@ -25,6 +37,9 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           hipStream_t stream);
 int fwd_schedule(int B, int Hq, int Nq, int Nk, bool causal, int* bh_out, int* qt_out,
                  int* cost_out, int capacity);
+// Workgroup of a persistent grid of `grid` workgroups that takes each list
+// position (persistent_position); returns n_units, or -1 on bad arguments.
+int persistent_schedule(int n_units, int grid, int* worker_out, int capacity);
 
 hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                           const float* dout, const float* lse, float* dq, float* dk, float* dv,

@@ -70,9 +70,10 @@ int fa_version(void);
  *   lse [B][Hq][Nq]: fp32.
  *   d in {64, 128}.  Softmax and accumulation are fp32; O is rounded to
  *   bf16 (nearest-even).
- * Query tiles are launched longest-first (causal) so the hardware dispatcher
- * hands the largest remaining work to the next free compute unit ([L21]
- * slides 27-46).
+ * Work units (query tiles) are ordered longest first ([L21] slides 27-46);
+ * causal, a persistent grid of one workgroup per compute unit walks that list
+ * (fa_persistent_schedule; [L21] slide 26), otherwise one workgroup per unit
+ * is launched in that order.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -444,6 +445,19 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  */
 int fa_fwd_schedule(int B, int Hq, int Nq, int Nk, int d, int causal,
                     int* bh_out, int* qtile_out, int* cost_out, int capacity);
+
+/*
+ * Host-side view of the persistent grids ([L21] slide 26: a grid of as many
+ * workgroups as compute units, each taking work units in turn; slides 27-46:
+ * longest first).  The causal dense forward and dQ kernels launch
+ * min(n_units, compute units) workgroups; workgroup w of G takes the
+ * positions w, 2G-1-w, 2G+w, 4G-1-w, ... of the longest-first list (snake
+ * order), so each round's longest units pair with the next round's shortest.
+ * Writes, for each of the n_units list positions, the workgroup that takes
+ * it.  Returns n_units, or -1 on bad arguments (n_units < 0, grid <= 0,
+ * capacity < n_units with a non-NULL output).  No GPU is needed.
+ */
+int fa_persistent_schedule(int n_units, int grid, int* worker_out, int capacity);
 
 #ifdef __cplusplus
 }

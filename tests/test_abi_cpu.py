@@ -216,6 +216,41 @@ def test_forward_schedule_matches_greedy_lpt(lib, workers):
     assert max(loads) <= max(worst)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(2, 16, 8192, 128), (1, 3, 1000, 128), (4, 16, 2048, 64),
+                                     (1, 2, 65536, 128), (3, 5, 3000, 64)])
+def test_persistent_schedule_balances_like_greedy_lpt(lib, B, H, N, d):
+    """The persistent grid's snake placement of the longest-first list
+    ([L21] slides 26-46): every position goes to exactly one of the G
+    workgroups, each workgroup's positions ascend (so it can stop at the
+    first one past the list), and the busiest workgroup's load is within 5%
+    of greedy longest-first list scheduling (the oracle's) on the same unit
+    costs, and never worse than in-order greedy dispatch."""
+    bh, qt, cost = fa.fa_fwd_schedule(B, H, N, N, d, True)
+    n = len(cost)
+    G = min(256, n)
+    owner = fa.fa_persistent_schedule(n, G)
+    assert sorted(set(owner)) == list(range(G))
+    for w in range(G):
+        pos = [p for p in range(n) if owner[p] == w]
+        assert pos == sorted(pos)
+    loads = [0] * G
+    for p in range(n):
+        loads[owner[p]] += cost[p]
+    greedy, _ = SCH.list_schedule([cost[i] for i in SCH.lpt_order(cost)], G)
+    assert max(loads) <= 1.05 * max(greedy), (max(loads), max(greedy))
+    inorder = sorted(range(n), key=lambda i: (bh[i], qt[i]))
+    worst, _ = SCH.list_schedule([cost[i] for i in inorder], G)
+    assert max(loads) <= max(worst)
+
+
+def test_persistent_schedule_arguments(lib):
+    assert lib.fa_persistent_schedule(10, 0, None, 0) == -1
+    assert lib.fa_persistent_schedule(-1, 4, None, 0) == -1
+    assert lib.fa_persistent_schedule(7, 3, None, 0) == 7
+    assert fa.fa_persistent_schedule(7, 3) == [0, 1, 2, 2, 1, 0, 0]
+    assert fa.fa_persistent_schedule(0, 3) == []
+
+
 def test_window_validation(lib):
     """fa_fwd_window / fa_bwd_window: window sides below -1, Nq != Nk, head
     dims, workspace."""
