@@ -365,11 +365,52 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
 
   constexpr int NG = 8;            // product groups per step: 4 QK^T, 4 PV
   constexpr int EPG = 32 / NG;     // elements of S_i per group (per lane)
+  // Lazy check of a finished tile (its p' codes, sum lt and coefficients):
+  // if some lane's sum exceeds the bound, move the reference to the tile's
+  // max, rescale O (which holds the tiles before it) and l, and redo its p'.
+  // It runs at the start of the next step, before that step's products, as
+  // does the masking of a tile: a branch after the products would let the
+  // compiler sink the products it does not feed below it, out of the exp
+  // interleave (measured: half the products ran with no VALU work beside
+  // them).
+  float lt_prev = 0.f, ci_prev = 0.f, ei_prev = 0.f, ri_prev = 0.f;
+  auto settle_tile = [&](const f32x16* s_prev, i32x8& p_prev) {
+    if (__builtin_amdgcn_ballot_w64(lt_prev > kLazyLimit)) {
+      const float Mn = fmaxf(M, tile_max(s_prev) * ci_prev);
+      const float alpha = fast_exp2(M - Mn);
+      M = Mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int d4 = 0; d4 < DBLK; ++d4) o[d4] *= alpha;
+      float lt = 0.f;
+      const float bias2 = ei_prev - M + kP8Shift;
+      int pw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float q4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          q4[e] = fast_exp2(fmaf(s_prev[(4 * k + e) >> 4][(4 * k + e) & 15], ci_prev, bias2));
+          lt += q4[e];
+        }
+        pw[k] = cvt_fp8x4(q4[0], q4[1], q4[2], q4[3]);
+      }
+      p_prev = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+      lt_prev = lt;
+    }
+    l_run += lt_prev * ri_prev;
+  };
   auto step = [&](int i, auto U) {
     constexpr int u = decltype(U)::value;
     f32x16* s_cur = sbuf[u];
     f32x16* s_nxt = sbuf[u ^ 1];
-    const bool more_k = i + 2 < ntiles;
+    // tile i-1 (S in s_nxt until it is overwritten below, P' in pbuf[u ^ 1]);
+    // then tile i's mask (tile 0's was applied in the prologue).  Both
+    // branches come before the products.
+    if (i > 0) {
+      settle_tile(s_nxt, pbuf[u ^ 1]);
+      mask(i, s_cur);
+    }
     float ci, ei, ri;
     tile_coef(i, &ci, &ei, &ri);
     const float bias = ei - M + kP8Shift;
@@ -382,7 +423,9 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
       i32x8 kfr = kfrag(ks, 0, 0);
       i32x8 vfr = vfrag(vs, 0);
       asm volatile("" ::: "memory");
-      if (more_k) issue_k(i + 2, u);
+      // K_{i+2} into the slot K_i left; past the end the last tile is loaded
+      // again (nothing reads it), so that no branch splits the step
+      issue_k(min(i + 2, ntiles - 1), u);
       issue_v(i, u);
       float p[32];
       int pw[8];
@@ -424,32 +467,10 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
       A(NG - 1);
       pbuf[u] = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     }
-    // Rare: the reference is too low for tile i.  Move it to the tile's max,
-    // rescale O (which holds tiles up to i-1) and l, and redo tile i's p'.
-    if (__builtin_amdgcn_ballot_w64(lt > kLazyLimit)) {
-      const float Mn = fmaxf(M, tile_max(s_cur) * ci);
-      const float alpha = fast_exp2(M - Mn);
-      M = Mn;
-      l_run *= alpha;
-#pragma unroll
-      for (int d4 = 0; d4 < DBLK; ++d4) o[d4] *= alpha;
-      lt = 0.f;
-      const float bias2 = ei - M + kP8Shift;
-      int pw[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float q4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          q4[e] = fast_exp2(fmaf(s_cur[(4 * k + e) >> 4][(4 * k + e) & 15], ci, bias2));
-          lt += q4[e];
-        }
-        pw[k] = cvt_fp8x4(q4[0], q4[1], q4[2], q4[3]);
-      }
-      pbuf[u] = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-    }
-    l_run += lt * ri;
-    if (i + 1 < ntiles) mask(i + 1, s_nxt);
+    lt_prev = lt;
+    ci_prev = ci;
+    ei_prev = ei;
+    ri_prev = ri;
     wait_vmem();
     lds_barrier();
   };
@@ -457,6 +478,9 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
     step(i0, IntConst<0>{});
     if (i0 + 1 < ntiles) step(i0 + 1, IntConst<1>{});
   }
+  // the last tile's check
+  if ((ntiles - 1) & 1) settle_tile(sbuf[1], pbuf[1]);
+  else settle_tile(sbuf[0], pbuf[0]);
   // The last tile's O^T += V^T P'^T.
   auto pv_last = [&](auto U) {
     constexpr int u = decltype(U)::value;
