@@ -1,0 +1,101 @@
+"""The C ABI's host layer (argument validation and dispatch, csrc/fa_api.cpp)
+built with AddressSanitizer and UndefinedBehaviorSanitizer on the CPU, linked
+with the library's kernel objects, and driven by the ABI tests in a separate
+process with the ASan runtime preloaded.  Host code only: the kernel objects
+are the normal build, and nothing here needs or touches a GPU."""
+import os
+import shutil
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "exact_attention_83_amd", "csrc")
+OBJ = os.path.join(ROOT, "exact_attention_83_amd", "_build")
+KERNEL_OBJS = ["fa_fwd.o", "fa_bwd.o", "fa_decode.o", "fa_fp8.o"]
+
+
+def _runtime(name):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        return None
+    p = subprocess.run([gxx, f"-print-file-name={name}"], capture_output=True, text=True).stdout.strip()
+    return p if os.path.isabs(p) and os.path.exists(p) else None
+
+
+@pytest.fixture(scope="module")
+def sanitized_lib(tmp_path_factory, lib):
+    # (`lib` makes sure the normal build, whose kernel objects are reused, exists)
+    asan = _runtime("libasan.so")
+    if asan is None or _runtime("libubsan.so") is None:
+        pytest.skip("g++ with the ASan/UBSan runtimes is not available")
+    objs = [os.path.join(OBJ, o) for o in KERNEL_OBJS]
+    if not all(os.path.exists(o) for o in objs):
+        pytest.skip("kernel objects not built")
+    d = tmp_path_factory.mktemp("asan")
+    api_o = str(d / "fa_api_asan.o")
+    so = str(d / "libfa_asan.so")
+    flags = ["-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    subprocess.run(["g++", *flags, "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-c",
+                    os.path.join(CSRC, "fa_api.cpp"), "-o", api_o], check=True)
+    subprocess.run(["g++", "-shared", "-fsanitize=address,undefined", api_o, *objs,
+                    "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lamdhip64", "-o", so],
+                   check=True)
+    return so, asan
+
+
+def _run(code, so, asan):
+    env = dict(os.environ, LD_PRELOAD=asan, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1", FA_TEST_LIB=so,
+               HIP_VISIBLE_DEVICES="")
+    return subprocess.run([sys.executable, "-c", textwrap.dedent(code)], cwd=ROOT, env=env,
+                          capture_output=True, text=True, timeout=600)
+
+
+def test_abi_tests_pass_under_asan_and_ubsan(sanitized_lib):
+    so, asan = sanitized_lib
+    r = _run("""
+        import ctypes, os, sys
+        assert hasattr(ctypes.CDLL(None), "__asan_init"), "ASan runtime not active"
+        import exact_attention_83_amd as fa
+        fa.LIB_PATH = os.environ["FA_TEST_LIB"]
+        import pytest
+        sys.exit(pytest.main(["tests/test_abi_cpu.py", "-q", "-p", "no:cacheprovider",
+                              "-m", "not gpu"]))
+        """, so, asan)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+
+
+def test_valid_calls_reach_the_launch_under_asan(sanitized_lib):
+    """Valid arguments pass every check and reach the launch, which reports
+    FA_ERR_HIP on a host without a GPU; the schedule views fill their
+    outputs.  Nothing is dereferenced on the host."""
+    so, asan = sanitized_lib
+    r = _run("""
+        import os, sys
+        import exact_attention_83_amd as fa
+        fa.LIB_PATH = os.environ["FA_TEST_LIB"]
+        lib = fa.load()
+        A = 0x100000
+        ws = lib.fa_bwd_workspace_size(2, 4, 300, 128)
+        codes = [
+            lib.fa_fwd(A, A, A, A, A, 2, 4, 2, 300, 300, 128, 0.1, 1, None),
+            lib.fa_fwd(A, A, A, A, A, 1, 2, 2, 100, 700, 64, 0.1, 0, None),
+            lib.fa_bwd(A, A, A, A, A, A, A, A, A, A, ws, 2, 4, 2, 300, 300, 128, 0.1, 1, None),
+            lib.fa_decode_splitkv(A, A, A, A, A, 2, 8, 2, 4096, 128, 0.1, 16, None),
+            lib.fa_decode_combine(A, A, A, A, 2, 8, 128, 16, None),
+            lib.fa_decode_splitkv_noalloc(A, A, A, A, A, 2, 8, 2, 4096, 128, 0.1, 16, None),
+            lib.fa_quantize_fp8(A, None, A, A, 1, 2, 300, 128, None),
+        ]
+        assert all(c == fa.FA_ERR_HIP for c in codes), codes
+        bh, qt, cost = fa.fa_fwd_schedule(2, 16, 8192, 8192, 128, True)
+        assert len(cost) == 1024
+        owner = fa.fa_persistent_schedule(1024, 256)
+        assert sorted(set(owner)) == list(range(256))
+        print("ok")
+        """, so, asan)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout[-3000:] + r.stderr[-3000:]
