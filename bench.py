@@ -339,6 +339,31 @@ def main(argv=None):
         f"dkdv {dkdv_ms:.3f} ms, dq {dq_ms:.3f} ms, bwd {rate(w.bwd_flops(), bwd_ms):.0f} TF")
 
     iters = max(5, a.steps)
+    if not only or "fp8_bwd" in only:
+        # the same causal step's backward with the fp8 dS products (K and Q
+        # quantisers, fp8-dQ kernel, fp8-dK dK/dV kernel)
+        ws8_bytes = fa.fa_bwd_fp8_workspace_size(*args)
+        ws8 = torch.empty(ws8_bytes, dtype=torch.uint8, device="cuda")
+        k8 = torch.empty(k.shape, dtype=torch.uint8, device="cuda")
+        ke = torch.empty((w.B, w.Hkv, (w.Nk + 31) // 32), dtype=torch.uint8, device="cuda")
+
+        def b8():
+            fa.fa_bwd_fp8(q, k, v, o, do, lse, dq, dk, dv, ws8, ws8_bytes, *args, w.scale, True,
+                          sh)
+
+        def kq():
+            # (the quantiser of K; Q's has the same shape here)
+            fa.fa_quantize_pow2_e4m3(k, k8, ke, w.B, w.Hkv, w.Nk, w.d, sh)
+
+        b8()
+        t8 = timed(b8, iters, stream)
+        tq = timed(kq, iters, stream)
+        parts["fp8_bwd_causal"] = {
+            "ms": round(t8, 4), "tflops": round(rate(w.bwd_flops(), t8), 1),
+            "vs_bf16_bwd": round(bwd_ms / t8, 4), "quant_ms_each": round(tq, 4),
+            "kernels_ms_est": round(t8 - 2 * tq, 4)}
+        log(f"fp8 bwd {t8:.3f} ms (bf16 {bwd_ms:.3f}), quantiser {tq:.3f} ms each (K, Q)")
+        del ws8, k8, ke
     if not only or "fwd" in only:
         t = timed(lambda: fwd(False), iters, stream)
         tf = 2 * w.fwd_flops() / (t * 1e-3) / 1e12

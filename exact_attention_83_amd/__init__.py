@@ -67,6 +67,10 @@ _SIGS = {
     "fa_quantize_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P,
                         _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_quantize_pow2_e4m3": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "fa_bwd_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "fa_bwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                        _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_schedule": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _I]),
     "fa_persistent_schedule": (_I, [_I, _I, _P, _I]),
 }
@@ -288,6 +292,21 @@ def fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, Nq, Nk
     _call("fa_fwd_fp8", _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale),
           _ptr(v_scale), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, scale, int(causal),
           _stream(stream))
+
+
+def fa_quantize_pow2_e4m3(x, x8, x_scale, B, H, N, d, stream=None):
+    _call("fa_quantize_pow2_e4m3", _ptr(x), _ptr(x8), _ptr(x_scale), B, H, N, d, _stream(stream))
+
+
+def fa_bwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nk, d):
+    return load().fa_bwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+
+
+def fa_bwd_fp8(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+               B, Hq, Hkv, Nq, Nk, d, scale, causal, stream=None):
+    _call("fa_bwd_fp8", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+          _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale,
+          int(causal), _stream(stream))
 
 
 def fa_fwd_schedule(B, Hq, Nq, Nk, d, causal):
@@ -542,6 +561,32 @@ def quantize_fp8(x, signs=None, stream=None):
     sc = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
     fa_quantize_fp8(x, signs, x8, sc, B, H, N, d, stream)
     return x8, sc
+
+
+def quantize_pow2_e4m3(x, stream=None):
+    """e4m3 codes (uint8, same shape) and per-32-row e8m0 scale bytes."""
+    import torch
+    B, H, N, d = x.shape
+    x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    xe = torch.empty((B, H, (N + 31) // 32), dtype=torch.uint8, device=x.device)
+    fa_quantize_pow2_e4m3(x, x8, xe, B, H, N, d, stream)
+    return x8, xe
+
+
+def backward_fp8(q, k, v, o, lse, dout, causal=False, scale=None, workspace=None, stream=None):
+    """dQ, dK, dV (bf16) with the fp8 dS product for dQ (fa_bwd_fp8)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    s = _default_scale(d, scale)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws_bytes = fa_bwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    fa_bwd_fp8(q, k, v, o, dout, lse, dq, dk, dv, ws, ws.numel() * ws.element_size(), B, Hq, Hkv,
+               Nq, Nk, d, s, causal, stream)
+    return dq, dk, dv
 
 
 def forward_fp8(q8, k8, v8, qs, ks, vs, causal=False, scale=None, stream=None):

@@ -320,6 +320,53 @@ fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const voi
                                       Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream, -1, -1, o));
 }
 
+size_t fa_bwd_fp8_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+  // delta, e4m3 K and its 32-row scale words, e4m3 Q and its scale words
+  return round256((size_t)B * Hq * Nq * sizeof(float)) + round256((size_t)B * Hkv * Nk * d) +
+         round256((size_t)B * Hkv * ((Nk + 31) / 32) * 4) + round256((size_t)B * Hq * Nq * d) +
+         round256((size_t)B * Hq * ((Nq + 31) / 32) * 4);
+}
+
+fa_status fa_bwd_fp8(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                     int Nk, int d, float scale, int causal, hipStream_t stream) {
+  if (fa_status s = bwd_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
+                               Hq, Hkv, Nq, Nk, d, scale, causal))
+    return s;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa_bwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nk, d)) return FA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws);
+  ws += round256((size_t)B * Hq * Nq * sizeof(float));
+  uint8_t* k8 = reinterpret_cast<uint8_t*>(ws);
+  ws += round256((size_t)B * Hkv * Nk * d);
+  int32_t* ke = reinterpret_cast<int32_t*>(ws);
+  ws += round256((size_t)B * Hkv * ((Nk + 31) / 32) * 4);
+  uint8_t* q8 = reinterpret_cast<uint8_t*>(ws);
+  ws += round256((size_t)B * Hq * Nq * d);
+  int32_t* qe = reinterpret_cast<int32_t*>(ws);
+  hipError_t e = fa::launch_quantize_pow2_e4m3_words(k, k8, ke, B * Hkv, Nk, stream);
+  if (e == hipSuccess) e = fa::launch_quantize_pow2_e4m3_words(q, q8, qe, B * Hq, Nq, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dq_fp8(q, k, v, dout, lse, delta, dq, k8, ke, o, B, Hq, Hkv, Nq, Nk, scale,
+                              causal != 0, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dkdv_fp8(q, k, v, dout, lse, delta, dk, dv, q8, qe, B, Hq, Hkv, Nq, Nk,
+                                scale, causal != 0, stream);
+  return hip_status(e);
+}
+
+fa_status fa_quantize_pow2_e4m3(const void* x, uint8_t* x8, uint8_t* x_scale, int B, int H,
+                                int N, int d, hipStream_t stream) {
+  if (!aligned16(x) || !aligned16(x8) || x_scale == nullptr) return FA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * ((N + 31) / 32) >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_quantize_pow2_e4m3(x, x8, x_scale, B * H, N, stream));
+}
+
 fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                      const float* dout, const float* lse, float* dq, float* dk, float* dv,
                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,

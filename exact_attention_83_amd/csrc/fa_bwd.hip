@@ -243,7 +243,15 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk, int stride = RO
 // WIN: sliding window (key j visible to query i iff i - win_l <= j <= i +
 // win_r; negative = unbounded): only the query tiles whose windows reach this
 // work unit's keys are visited.
-template <int D, bool CAUSAL, bool WIN, bool VARLEN, bool SPARSE>
+// FP8DS: dK += dS^T Q runs on the 32x32x64 scaled fp8 MFMA ([CH18] §18.6.2
+// (3)), two query tiles per product: the first tile of each pair keeps its
+// dS (e5m2, one power-of-two scale per (key, 32-query tile)) and its half of
+// the Q fragments in registers, and the second tile's products take the two
+// tiles as their two 32-query k-blocks; Q comes in e4m3 from the quantiser's
+// per-32-row blocks (Q8, e8m0 scale words QE), staged in each slot beside the
+// bf16 Q and read with transposing byte reads.  A last tile without a partner
+// pairs with zeros.
+template <int D, bool CAUSAL, bool WIN, bool VARLEN, bool SPARSE, bool FP8DS>
 __device__ __forceinline__ void bwd_dkdv_unit(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -251,7 +259,9 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq_arg,
     int Nk_arg, float scale, float scale_log2, int BHkv, int win_l, int win_r,
     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q,
-    const uint8_t* __restrict__ sp_map, int sp_nkb, int unit) {
+    const uint8_t* __restrict__ sp_map, int sp_nkb, const uint8_t* __restrict__ Q8,
+    const int32_t* __restrict__ QE, int unit) {
+  static_assert(!FP8DS || (D == 128 && !WIN && !VARLEN && !SPARSE), "fp8 dS: dense, d = 128");
   constexpr int NW = kKvWaves;
   constexpr int KB = kKvKb;
   constexpr int BQ = kKvBq;
@@ -261,7 +271,12 @@ __device__ __forceinline__ void bwd_dkdv_unit(
   constexpr int ROWB = D * 2;
   constexpr int QTILE = BQ * ROWB;
   constexpr int LPW = QTILE / 1024 / NW;  // direct loads per wave per Q (or dO) tile
-  constexpr int SLOT = 2 * QTILE + 2 * BQ * 4;  // Q, dO, lse, delta
+  // Q, dO, lse, delta; FP8DS: the e4m3 Q tile (1 KB-aligned) and each wave's
+  // copy of its scale word
+  constexpr int Q8OFF = 2 * QTILE + 1024;
+  constexpr int QEOFF = Q8OFF + BQ * D;
+  constexpr int SLOT = FP8DS ? QEOFF + NW * 256 : 2 * QTILE + 2 * BQ * 4;
+  static_assert(2 * SLOT <= 64 * 1024, "slot bases within a read's immediate offset");
   // One variable per slot: with the slot a compile-time constant in the loop
   // body, the compiler sees that the direct loads into one slot cannot alias
   // the reads of the other and does not wait for them.
@@ -399,6 +414,9 @@ __device__ __forceinline__ void bwd_dkdv_unit(
   int qoff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) qoff[i] = swz_src_offset<ROWB>(lane, wave * LPW + i, SQ * 2);
+  static_assert(!FP8DS || BQ * D == NW * 1024, "one 1 KB e4m3 load per wave per tile");
+  const int q8row = wave * 8 + (lane >> 3);
+  const int q8off = q8row * D + (((lane & 7) ^ f8_swz_t(q8row)) << 4);
   auto issue = [&](int it, int slot) {
     int bh, q0;
     tile_head(it, &bh, &q0);
@@ -422,6 +440,16 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     if (wave == 1 && lane < BQ)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (lds_void_t*)(ld + BQ * 4), 4, lane * 4, q0 * 4,
                                                0, 0);
+    if constexpr (FP8DS) {
+      // wave w: e4m3 rows 8w .. 8w+7 (lane -> row 8w + lane/8, LDS chunk
+      // position lane%8 holding source chunk (lane%8) ^ swz), and the tile's
+      // scale word into its own 256-byte copy
+      const __amdgpu_buffer_rsrc_t rQ8 = make_rsrc(Q8 + q_off(bh), (uint32_t)Nq * D);
+      buffer_load_lds16(rQ8, sslot(slot) + Q8OFF + wave * 1024, q8off, q0 * D);
+      const int nqb8 = (Nq + 31) / 32;
+      const __amdgpu_buffer_rsrc_t rQE = make_rsrc(QE + (size_t)bh * nqb8, (uint32_t)nqb8 * 4);
+      buffer_load_lds4(rQE, sslot(slot) + QEOFF + wave * 256, 0, (q0 / 32) * 4);
+    }
   };
 
   // A-operand rows of S / dP (b128): query l32, chunk 2*ks + hf.
@@ -437,6 +465,27 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     trd0[db] = tr_offset<ROWB>(lane, 0, 32 * db);
     trd1[db] = tr_offset<ROWB>(lane, 8, 32 * db);
   }
+
+  // FP8DS: B operand of dK (k = query, n = head dim 32*db + l32), one tile's
+  // half: bytes 16*th .. 16*th+15 of the 32 come from tile th of the pair,
+  // byte i of lane half hf being query 8*(i/4) + 4*hf + i%4 of that tile
+  // (the S accumulator's row order).  Source lane 2r + half of 16-lane group
+  // g16 addresses row 8*(r/4) + 4*hf + r%4 (+16 for the second read), head
+  // dims 32*db + 16*(g16%2) + 8*half.
+  int q8rd[FP8DS ? DBLK : 1];
+  if constexpr (FP8DS) {
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int vr = j16 >> 1;
+    const int row = 8 * (vr >> 2) + 4 * hf + (vr & 3);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+      q8rd[db] = row * D + (((2 * db + (g16 & 1)) ^ f8_swz_t(row)) << 4) + 8 * (j16 & 1);
+  }
+  // the first tile of a pair: dS codes, dS scale codes, Q fragment halves and
+  // Q scale word
+  constexpr int F8N = FP8DS ? 1 : 0;
+  int dsc_prev[KB][4 * F8N + 1 - F8N], esc_prev[KB], q8h_prev[DBLK][4 * F8N + 1 - F8N];
+  int qe_prev = 0;
 
   f32x16 dk[KB][DBLK], dv[KB][DBLK];
 #pragma unroll
@@ -460,6 +509,9 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     wait_vmem();
     lds_barrier();
     if (it + 1 < total) issue(it + 1, slot ^ 1);
+    // FP8DS: first (slot 0) or second (slot 1) tile of a pair; a first tile
+    // with no second one runs the products itself, against zeros
+    const bool lone = FP8DS && slot == 0 && it + 1 >= total;
     const char* qs = sslot(slot);
     const char* gs = qs + QTILE;
     const char* ls = qs + 2 * QTILE;
@@ -605,14 +657,18 @@ __device__ __forceinline__ void bwd_dkdv_unit(
 #pragma unroll
       for (int t = 1; t < EPP; t += 2) pack_p(EPP * (NPH - 1) + t);
     }
-    // (3) dV += P^T dO, with dS = P (dP - delta) and its bf16 A operands.
+    // (3) dV += P^T dO, with dS = P (dP - delta) and its bf16 A operands
+    // (FP8DS: the largest |dS| of each key block, over this lane's rows).
+    float am[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) am[kb] = 0.f;
     {
       f32x4 dl;
 #pragma unroll
       for (int j = 0; j < NPR; ++j) {
         const u32x4 b = gb[j & 1];
         if (j + 2 < NPR) gb[j & 1] = trB(gs, j + 2);
-        else qb[j + 2 - NPR] = trB(qs, j + 2 - NPR);  // phase 4's first operands
+        else if (!FP8DS) qb[j + 2 - NPR] = trB(qs, j + 2 - NPR);  // phase 4's first operands
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const int m = 2 * j + kb;
@@ -626,15 +682,79 @@ __device__ __forceinline__ void bwd_dkdv_unit(
               if (gr < 3) dln = lds_read<f32x4>(ls, BQ * 4 + ((gr + 1) * 8 + hf * 4) * 4);
             }
             dpb[kbe][r] = sb[kbe][r] * (dpb[kbe][r] - dl[e]);
-            if (e & 1)
-              dsa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(dpb[kbe][r - 1], dpb[kbe][r]);
+            if constexpr (FP8DS) {
+              am[kbe] = fmaxf(am[kbe], fabsf(dpb[kbe][r]));
+            } else {
+              if (e & 1)
+                dsa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] =
+                    pack_bf16(dpb[kbe][r - 1], dpb[kbe][r]);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
     // (4) dK += dS^T Q.
-    {
+    if constexpr (FP8DS) {
+      // this tile's dS in e5m2 with one power-of-two scale per (key, tile)
+      // (the maximum over both lane halves), its Q fragment halves and scale
+      int dsc[KB][4], esc[KB], q8h[DBLK][4];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int e = pow2_block_exp<16>(max_halves(am[kb]));
+        const float sc = exp2_pos(e);
+        esc[kb] = e + 127;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dsc[kb][i] = cvt_bf8x4_div(dpb[kb][4 * i], dpb[kb][4 * i + 1], dpb[kb][4 * i + 2],
+                                     dpb[kb][4 * i + 3], sc);
+      }
+      const char* q8s = qs + Q8OFF;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const i32x2_t x0 = lds_read_tr8(q8s + q8rd[db]);
+        const i32x2_t x1 = lds_read_tr8(q8s + 16 * D + q8rd[db]);
+        q8h[db][0] = x0[0];
+        q8h[db][1] = x0[1];
+        q8h[db][2] = x1[0];
+        q8h[db][3] = x1[1];
+      }
+      const int qe = lds_read<int>(qs + QEOFF + wave * 256, 0);
+      if (slot == 0 && !lone) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          esc_prev[kb] = esc[kb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dsc_prev[kb][i] = dsc[kb][i];
+        }
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q8h_prev[db][i] = q8h[db][i];
+        qe_prev = qe;
+      } else {
+        // k-block 0 = the pair's first tile (or this lone tile), k-block 1 =
+        // the second tile (or zeros with unit scales); lane half hf supplies
+        // k-block hf's scales
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const i32x8 a = lone ? i32x8{dsc[kb][0], dsc[kb][1], dsc[kb][2], dsc[kb][3], 0, 0, 0, 0}
+                               : i32x8{dsc_prev[kb][0], dsc_prev[kb][1], dsc_prev[kb][2],
+                                       dsc_prev[kb][3], dsc[kb][0], dsc[kb][1], dsc[kb][2],
+                                       dsc[kb][3]};
+          const int sa = lone ? (hf ? 127 : esc[kb]) : (hf ? esc[kb] : esc_prev[kb]);
+          const int sb = lone ? (hf ? 127 : qe) : (hf ? qe : qe_prev);
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) {
+            const i32x8 b =
+                lone ? i32x8{q8h[db][0], q8h[db][1], q8h[db][2], q8h[db][3], 0, 0, 0, 0}
+                     : i32x8{q8h_prev[db][0], q8h_prev[db][1], q8h_prev[db][2], q8h_prev[db][3],
+                             q8h[db][0], q8h[db][1], q8h[db][2], q8h[db][3]};
+            mfma_scale_bf8_fp8_pinned(dk[kb][db], a, b, sa, sb);
+          }
+        }
+      }
+    } else {
 #pragma unroll
       for (int j = 0; j < NPR; ++j) {
         const u32x4 b = qb[j & 1];
@@ -681,7 +801,8 @@ __device__ __forceinline__ void bwd_dkdv_unit(
 
 // The dK/dV kernel: one workgroup per key tile, launched in longest-first
 // order (a persistent grid over the same list measured no faster here).
-template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false>
+template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false,
+          bool FP8DS = false>
 __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -689,10 +810,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq_arg,
     int Nk_arg, float scale, float scale_log2, int BHkv, int win_l = -1, int win_r = -1,
     const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
-    int total_q = 0, const uint8_t* __restrict__ sp_map = nullptr, int sp_nkb = 0) {
-  bwd_dkdv_unit<D, CAUSAL, WIN, VARLEN, SPARSE>(Q, K, V, dO, LSE, Delta, dK, dV, Hq, Hkv, Nq_arg,
-                                                Nk_arg, scale, scale_log2, BHkv, win_l, win_r,
-                                                cu_q, cu_k, total_q, sp_map, sp_nkb, blockIdx.x);
+    int total_q = 0, const uint8_t* __restrict__ sp_map = nullptr, int sp_nkb = 0,
+    const uint8_t* __restrict__ Q8 = nullptr, const int32_t* __restrict__ QE = nullptr) {
+  bwd_dkdv_unit<D, CAUSAL, WIN, VARLEN, SPARSE, FP8DS>(
+      Q, K, V, dO, LSE, Delta, dK, dV, Hq, Hkv, Nq_arg, Nk_arg, scale, scale_log2, BHkv, win_l,
+      win_r, cu_q, cu_k, total_q, sp_map, sp_nkb, Q8, QE, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -706,7 +828,14 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void bwd_dkdv_kernel(
 // DELTA: the kernel forms its rows' delta = dO . O itself (from O, beside the
 // dO rows it holds) and writes it to Delta for the dK/dV kernel that runs after
 // it; otherwise it reads Delta from the pre-pass.
-template <int D, bool CAUSAL, bool WIN, bool VARLEN, bool SPARSE, bool DELTA>
+// FP8DS: dQ^T += K^T dS^T runs on the 32x32x64 scaled fp8 MFMA ([CH18]
+// §18.6.2 (3)): dS^T in e5m2 with one power-of-two scale per (query, 32-key
+// block) -- both k-blocks of one product are the tile's two key blocks -- and
+// K in e4m3 from the quantiser's per-32-row blocks (K8, e8m0 scale words KE),
+// its tile and the tile's two scale words staged in LDS beside the bf16 K
+// and V (the tile is read with transposing byte reads).  S and dP stay bf16
+// products.
+template <int D, bool CAUSAL, bool WIN, bool VARLEN, bool SPARSE, bool DELTA, bool FP8DS>
 __device__ __forceinline__ void bwd_dq_unit(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -714,7 +843,9 @@ __device__ __forceinline__ void bwd_dq_unit(
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int Nq_arg, int Nk_arg, float scale,
     float scale_log2, int BH, int nqt, int win_l, int win_r, const int* __restrict__ cu_q,
     const int* __restrict__ cu_k, int total_q, const int* __restrict__ sp_ptr,
-    const int* __restrict__ sp_idx, const uint16_t* __restrict__ O, int unit) {
+    const int* __restrict__ sp_idx, const uint16_t* __restrict__ O,
+    const uint8_t* __restrict__ K8, const int32_t* __restrict__ KE, int unit) {
+  static_assert(!FP8DS || (D == 128 && !WIN && !VARLEN && !SPARSE), "fp8 dS: dense, d = 128");
   constexpr int NW = kDqWaves;
   constexpr int BR = kDqBr;
   constexpr int BC = kDqBc;
@@ -723,11 +854,20 @@ __device__ __forceinline__ void bwd_dq_unit(
   constexpr int ROWB = D * 2;
   constexpr int TILE = BC * ROWB;
   constexpr int LPW = TILE / 1024 / NW;
-  // Three slots of (K, V), one LDS variable each (see bwd_dkdv_kernel).
-  __shared__ __attribute__((aligned(1024))) char k0s[TILE], v0s[TILE], k1s[TILE], v1s[TILE],
-      k2s[TILE], v2s[TILE];
-  auto kslot = [&](int sl) -> char* { return sl == 0 ? k0s : sl == 1 ? k1s : k2s; };
-  auto vslot = [&](int sl) -> char* { return sl == 0 ? v0s : sl == 1 ? v1s : v2s; };
+  // Three slots, one LDS variable each holding the tile's K and V (and, with
+  // FP8DS, its e4m3 K rows and the two K scale words, one 256-byte copy per
+  // wave).  The compiler tracks only a few direct-to-LDS destinations one by
+  // one; with one variable per slot it sees that a slot being read is not the
+  // one in flight and adds no waits of its own.
+  constexpr int TILE8 = FP8DS ? BC * D : 0;
+  constexpr int KEW = FP8DS ? NW * 256 : 0;
+  constexpr int SLOT = 2 * TILE + TILE8 + KEW;
+  __shared__ __attribute__((aligned(1024))) char sl0[SLOT], sl1[SLOT], sl2[SLOT];
+  auto slot_base = [&](int sl) -> char* { return sl == 0 ? sl0 : sl == 1 ? sl1 : sl2; };
+  auto kslot = [&](int sl) -> char* { return slot_base(sl); };
+  auto vslot = [&](int sl) -> char* { return slot_base(sl) + TILE; };
+  auto k8slot = [&](int sl) -> char* { return slot_base(sl) + 2 * TILE; };
+  auto keslot = [&](int sl) -> char* { return slot_base(sl) + 2 * TILE + TILE8; };
 
   // (opaque to the optimiser: per-lane offsets derived from it are then
   // recomputed for each unit of a persistent loop instead of being kept
@@ -763,6 +903,15 @@ __device__ __forceinline__ void bwd_dq_unit(
   }
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kv_off, (uint32_t)Nk * SK * 2);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kv_off, (uint32_t)Nk * SK * 2);
+  // FP8DS: e4m3 K rows (dense [b][hkv][Nk][128]) and their 32-row scale bytes
+  const __amdgpu_buffer_rsrc_t rK8 =
+      make_rsrc(FP8DS ? (const void*)(K8 + kv_off) : (const void*)K, FP8DS ? (uint32_t)Nk * D : 0u);
+  const int nkb8 = (Nk + 31) / 32;
+  // (a tile's second key block past the end reads 0 here: a scale of 2^-127
+  // on codes that are all zero)
+  const __amdgpu_buffer_rsrc_t rKE =
+      make_rsrc(FP8DS ? (const void*)(KE + (size_t)(b * Hkv + hk) * nkb8) : (const void*)K,
+                FP8DS ? (uint32_t)nkb8 * 4 : 0u);
 
   const int qrow = q0 + wave * 32 + l32;
   const int qrow_c = qrow < Nq ? qrow : Nq - 1;
@@ -835,6 +984,13 @@ __device__ __forceinline__ void bwd_dq_unit(
   int ldo[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) ldo[i] = swz_src_offset<ROWB>(lane, wave * LPW + i, SK * 2);
+  // FP8DS: wave w moves e4m3 rows 8w .. 8w+7 of a tile (lane -> row 8w +
+  // lane/8, LDS chunk position lane%8 holding source chunk (lane%8) ^ swz),
+  // and the tile's two scale words into its own LDS copy (lane l: key block
+  // l%2 of the tile, at word l).
+  static_assert(!FP8DS || BC * D / 1024 == NW, "one 1 KB e4m3 load per wave per tile");
+  const int k8row = wave * 8 + (lane >> 3);
+  const int k8off = k8row * D + (((lane & 7) ^ f8_swz_t(k8row)) << 4);
   auto issue = [&](int j, int slot) {
     char* dk_ = kslot(slot) + wave * LPW * 1024;
     char* dv_ = vslot(slot) + wave * LPW * 1024;
@@ -843,7 +999,12 @@ __device__ __forceinline__ void bwd_dq_unit(
       buffer_load_lds16(rK, dk_ + i * 1024, ldo[i], tile_of(j) * BC * SK * 2);
       buffer_load_lds16(rV, dv_ + i * 1024, ldo[i], tile_of(j) * BC * SK * 2);
     }
+    if constexpr (FP8DS) {
+      buffer_load_lds16(rK8, k8slot(slot) + wave * 1024, k8off, tile_of(j) * BC * D);
+      buffer_load_lds4(rKE, keslot(slot) + wave * 256, 4 * (lane & 1), tile_of(j) * 8);
+    }
   };
+  constexpr int LOADS = 2 * LPW + (FP8DS ? 2 : 0);  // per tile and wave
   // A operands of S^T / dP^T (b128): key row kb*32 + l32, chunk 2*ks + hf.
   int ard[KSTEPS];
 #pragma unroll
@@ -857,6 +1018,31 @@ __device__ __forceinline__ void bwd_dq_unit(
     trd0[db] = tr_offset<ROWB>(lane, 0, 32 * db);
     trd1[db] = tr_offset<ROWB>(lane, 8, 32 * db);
   }
+
+  // FP8DS: A operand of dQ^T from the e4m3 K tile (transposing byte reads):
+  // byte i of lane half hf is key 32*(i/16) + 8*((i/4)%4) + 4*hf + i%4 of
+  // head dim 32*db + l32.  Source lane 2r + half of 16-lane group g16 addresses
+  // key row 8*(r/4) + 4*hf + r%4 (+ 16*(read%2) + 32*(read/2)), head dims
+  // 32*db + 16*(g16%2) + 8*half.
+  int k8rd[FP8DS ? DBLK : 1];
+  if constexpr (FP8DS) {
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int vr = j16 >> 1;
+    const int row = 8 * (vr >> 2) + 4 * hf + (vr & 3);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+      k8rd[db] = row * D + (((2 * db + (g16 & 1)) ^ f8_swz_t(row)) << 4) + 8 * (j16 & 1);
+  }
+  auto k8frag = [&](const char* k8s, int db) {
+    int w[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const i32x2_t x = lds_read_tr8(k8s + ((t >> 1) * 32 + (t & 1) * 16) * D + k8rd[db]);
+      w[2 * t] = x[0];
+      w[2 * t + 1] = x[1];
+    }
+    return i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+  };
 
   f32x16 dq[DBLK];
 #pragma unroll
@@ -880,8 +1066,8 @@ __device__ __forceinline__ void bwd_dq_unit(
   // One iteration per KV tile; S = slot (a compile-time constant).
   auto body = [&](int j, auto S) {
     constexpr int slot = decltype(S)::value;
-    // tile j has landed once at most the next step's loads (2*LPW) remain
-    wait_vmem_le<2 * LPW>();
+    // tile j has landed once at most the next step's loads remain
+    wait_vmem_le<LOADS>();
     lds_barrier();
     const char* ks_ = kslot(slot);
     const char* vs_ = vslot(slot);
@@ -909,6 +1095,10 @@ __device__ __forceinline__ void bwd_dq_unit(
     constexpr int PFA = 4, PFB = 3;
     auto ka_of = [&](int m) { return lds_read<u32x4>(ks_, (m & 1) * 32 * ROWB + ard[m >> 1]); };
     auto va_of = [&](int m) { return lds_read<u32x4>(vs_, (m & 1) * 32 * ROWB + ard[m >> 1]); };
+    // Phase B's operand order: FP8DS takes key block 0's eight products
+    // first, so that block 0's dS can be formed and quantised beside block
+    // 1's products; otherwise the blocks alternate.
+    auto vb_of = [&](int m) { return va_of(FP8DS ? (((m & 7) << 1) | (m >> 3)) : m); };
     // (A)
     u32x4 va[PFB];
     {
@@ -923,7 +1113,7 @@ __device__ __forceinline__ void bwd_dq_unit(
         const int kk = m >> 1, kb = m & 1;
         const u32x4 a = ka[m % PFA];
         if (m + PFA < NAB) ka[m % PFA] = ka_of(m + PFA);
-        else if (m + PFA - NAB < PFB) va[m + PFA - NAB] = va_of(m + PFA - NAB);
+        else if (m + PFA - NAB < PFB) va[m + PFA - NAB] = vb_of(m + PFA - NAB);
         s[kb] = mfma_32x32x16_bf16(a, qf[kk], s[kb]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -949,12 +1139,33 @@ __device__ __forceinline__ void bwd_dq_unit(
     }
     __builtin_amdgcn_sched_barrier(0);
     // (B)
+    // FP8DS: dS = P (dP - delta) in fp32 with one power-of-two scale per
+    // (query, 32-key block), the block maximum taken over this lane's 16 keys
+    // and the other half's 16; codes in e5m2.  Byte i of this lane's 32 is
+    // key 32*(i/16) + 8*((i/4)%4) + 4*hf + i%4, the order of the S
+    // accumulator (and of the K^T fragments).  Key block 0 is done between
+    // block 1's dP products, block 1 after them.
+    float am0 = 0.f, am1 = 0.f, sc0 = 1.f;
+    int e0 = 0;
+    int w8[FP8DS ? 8 : 1];
+    auto ds_slice = [&](int kb, int i) {  // elements 4i .. 4i+3 of key block kb
+#pragma unroll
+      for (int r = 4 * i; r < 4 * i + 4; ++r) {
+        dp[kb][r] = s[kb][r] * (dp[kb][r] - dlt);
+        if (kb == 0) am0 = fmaxf(am0, fabsf(dp[0][r]));
+        else am1 = fmaxf(am1, fabsf(dp[1][r]));
+      }
+    };
+    auto cvt_slice = [&](int kb, int i, float sc) {  // dword 4*kb + i of the codes
+      const int r0 = 4 * i;
+      w8[4 * kb + i] = cvt_bf8x4_div(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], sc);
+    };
     {
 #pragma unroll
       for (int m = 0; m < NAB; ++m) {
-        const int kk = m >> 1, kb = m & 1;
+        const int kk = FP8DS ? (m & 7) : (m >> 1), kb = FP8DS ? (m >> 3) : (m & 1);
         const u32x4 a = va[m % PFB];
-        if (m + PFB < NAB) va[m % PFB] = va_of(m + PFB);
+        if (m + PFB < NAB) va[m % PFB] = vb_of(m + PFB);
         dp[kb] = mfma_32x32x16_bf16(a, gf[kk], dp[kb]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -962,10 +1173,42 @@ __device__ __forceinline__ void bwd_dq_unit(
           const int x = EPB * m + t;
           s[x >> 4][x & 15] = fast_exp2(fmaf(s[x >> 4][x & 15], scale_log2, -lse2));
         }
+        if constexpr (FP8DS) {
+          static_assert(NAB == 16, "block 0's work spread over block 1's eight products");
+          if (m >= 8 && m < 12) ds_slice(0, m - 8);
+          if (m == 12) {
+            e0 = pow2_block_exp<16>(max_halves(am0));
+            sc0 = exp2_pos(e0);
+          }
+          if (m == 13) { cvt_slice(0, 0, sc0); cvt_slice(0, 1, sc0); }
+          if (m == 14) { cvt_slice(0, 2, sc0); cvt_slice(0, 3, sc0); }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // (C)
+    if constexpr (FP8DS) {
+      const char* k8s = k8slot(slot);
+      i32x8 ka8 = k8frag(k8s, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds_slice(1, i);
+      const int e1 = pow2_block_exp<16>(max_halves(am1));
+      const float sc1 = exp2_pos(e1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cvt_slice(1, i, sc1);
+      const i32x8 ds8 = i32x8{w8[0], w8[1], w8[2], w8[3], w8[4], w8[5], w8[6], w8[7]};
+      // scale operands: lane half hf supplies key block hf's scale
+      const int sb = (hf ? e1 : e0) + 127;
+      const int sa = lds_read<int>(keslot(slot) + wave * 256, 4 * hf);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const i32x8 a = ka8;
+        if (db + 1 < DBLK) ka8 = k8frag(k8s, db + 1);
+        dq[db] = mfma_32x32x64_fp8_bf8_scaled(a, ds8, dq[db], sa, sb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
     u32x4 dsb[2][2];
     auto ds_elem = [&](int kb, int r) {
       dp[kb][r] = s[kb][r] * (dp[kb][r] - dlt);
@@ -1001,10 +1244,28 @@ __device__ __forceinline__ void bwd_dq_unit(
       }
     }
   };
-  for (int j = 0; j < ntiles; j += 3) {
-    body(j, IntConst<0>{});
+  if constexpr (FP8DS) {
+    // (in this form the compiler's waits in the fp8 variant are already
+    // exact, and peeling the remainder as below makes it spill)
+    for (int j = 0; j < ntiles; j += 3) {
+      body(j, IntConst<0>{});
+      if (j + 1 < ntiles) body(j + 1, IntConst<1>{});
+      if (j + 2 < ntiles) body(j + 2, IntConst<2>{});
+    }
+  } else {
+    // Whole rounds of three in the loop and the remainder after it: the
+    // loop's back edge then always follows the same three steps, so the
+    // compiler's view of which slots are in flight at the loop head is exact
+    // (with a partial round able to reach the back edge it waited there for
+    // every load in flight, the next tiles' included).
+    int j = 0;
+    for (; j + 3 <= ntiles; j += 3) {
+      body(j, IntConst<0>{});
+      body(j + 1, IntConst<1>{});
+      body(j + 2, IntConst<2>{});
+    }
+    if (j < ntiles) body(j, IntConst<0>{});
     if (j + 1 < ntiles) body(j + 1, IntConst<1>{});
-    if (j + 2 < ntiles) body(j + 2, IntConst<2>{});
   }
   wait_vmem();  // the reloads of the last tile
 
@@ -1030,7 +1291,7 @@ __device__ __forceinline__ void bwd_dq_unit(
 // (PERSIST) a persistent grid walking that list in snake order, as for the
 // forward.
 template <int D, bool CAUSAL, bool WIN = false, bool VARLEN = false, bool SPARSE = false,
-          bool DELTA = false, bool PERSIST = false>
+          bool DELTA = false, bool PERSIST = false, bool FP8DS = false>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -1039,23 +1300,22 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_kernel(
     float scale_log2, int BH, int nqt, int win_l = -1, int win_r = -1,
     const int* __restrict__ cu_q = nullptr, const int* __restrict__ cu_k = nullptr,
     int total_q = 0, const int* __restrict__ sp_ptr = nullptr,
-    const int* __restrict__ sp_idx = nullptr, const uint16_t* __restrict__ O = nullptr) {
+    const int* __restrict__ sp_idx = nullptr, const uint16_t* __restrict__ O = nullptr,
+    const uint8_t* __restrict__ K8 = nullptr, const int32_t* __restrict__ KE = nullptr) {
   if constexpr (PERSIST) {
     const int n = BH * nqt;
     for (int i = 0;; ++i) {
       const int p = persistent_position(i, blockIdx.x, gridDim.x);
       if (p >= n) break;
-      bwd_dq_unit<D, CAUSAL, WIN, VARLEN, SPARSE, DELTA>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv,
-                                                         Nq_arg, Nk_arg, scale, scale_log2, BH,
-                                                         nqt, win_l, win_r, cu_q, cu_k, total_q,
-                                                         sp_ptr, sp_idx, O, p);
+      bwd_dq_unit<D, CAUSAL, WIN, VARLEN, SPARSE, DELTA, FP8DS>(
+          Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv, Nq_arg, Nk_arg, scale, scale_log2, BH, nqt, win_l,
+          win_r, cu_q, cu_k, total_q, sp_ptr, sp_idx, O, K8, KE, p);
       __syncthreads();  // every wave is done with the LDS slots before the next unit
     }
   } else {
-    bwd_dq_unit<D, CAUSAL, WIN, VARLEN, SPARSE, DELTA>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv,
-                                                       Nq_arg, Nk_arg, scale, scale_log2, BH, nqt,
-                                                       win_l, win_r, cu_q, cu_k, total_q, sp_ptr,
-                                                       sp_idx, O, blockIdx.x);
+    bwd_dq_unit<D, CAUSAL, WIN, VARLEN, SPARSE, DELTA, FP8DS>(
+        Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv, Nq_arg, Nk_arg, scale, scale_log2, BH, nqt, win_l,
+        win_r, cu_q, cu_k, total_q, sp_ptr, sp_idx, O, K8, KE, blockIdx.x);
   }
 }
 
@@ -1186,6 +1446,57 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   }
 #undef FA_LAUNCH_DQ
 #undef FA_LAUNCH_DQ_PERSIST
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_fp8(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, float* delta, void* dq, const uint8_t* k8,
+                             const int32_t* ke, const void* o, int B, int Hq, int Hkv, int Nq,
+                             int Nk, float scale, bool causal, hipStream_t stream) {
+  const int BH = B * Hq;
+  const int nqt = (Nq + kDqBr - 1) / kDqBr;
+  const dim3 block(kDqWaves * 64);
+  auto Q = (const uint16_t*)q;
+  auto K = (const uint16_t*)k;
+  auto V = (const uint16_t*)v;
+  auto G = (const uint16_t*)dout;
+  auto dQ = (uint16_t*)dq;
+  auto Op = (const uint16_t*)o;
+  const float sl2 = scale * kLog2e;
+  if (causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<128, true, false, false, false, true, true, true>),
+                       dim3(persistent_grid(BH * nqt)), block, 0, stream, Q, K, V, G, lse, delta,
+                       dQ, Hq, Hkv, Nq, Nk, scale, sl2, BH, nqt, -1, -1, nullptr, nullptr, 0,
+                       nullptr, nullptr, Op, k8, ke);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<128, false, false, false, false, true, false, true>),
+                       dim3(BH * nqt), block, 0, stream, Q, K, V, G, lse, delta, dQ, Hq, Hkv, Nq,
+                       Nk, scale, sl2, BH, nqt, -1, -1, nullptr, nullptr, 0, nullptr, nullptr, Op,
+                       k8, ke);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_fp8(const void* q, const void* k, const void* v, const void* dout,
+                               const float* lse, const float* delta, void* dk, void* dv,
+                               const uint8_t* q8, const int32_t* qe, int B, int Hq, int Hkv,
+                               int Nq, int Nk, float scale, bool causal, hipStream_t stream) {
+  const int BHkv = B * Hkv;
+  const dim3 grid(BHkv * ((Nk + kKvBkv - 1) / kKvBkv)), block(kKvWaves * 64);
+  auto Q = (const uint16_t*)q;
+  auto K = (const uint16_t*)k;
+  auto V = (const uint16_t*)v;
+  auto G = (const uint16_t*)dout;
+  auto dK = (uint16_t*)dk;
+  auto dV = (uint16_t*)dv;
+  const float sl2 = scale * kLog2e;
+  if (causal)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, false, false, false, true>), grid, block,
+                       dkdv_vbuf_bytes(128), stream, Q, K, V, G, lse, delta, dK, dV, Hq, Hkv, Nq,
+                       Nk, scale, sl2, BHkv, -1, -1, nullptr, nullptr, 0, nullptr, 0, q8, qe);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, false, false, false, true>), grid, block,
+                       dkdv_vbuf_bytes(128), stream, Q, K, V, G, lse, delta, dK, dV, Hq, Hkv, Nq,
+                       Nk, scale, sl2, BHkv, -1, -1, nullptr, nullptr, 0, nullptr, 0, q8, qe);
   return hipGetLastError();
 }
 

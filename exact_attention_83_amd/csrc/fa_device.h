@@ -149,6 +149,11 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char
                                                   int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
+// The same with 4 bytes per lane: LDS bytes [lds + 4*i, lds + 4*i + 4).
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, char* lds, int voff,
+                                                 int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, 0);
+}
 
 // Waits for this wave's vector-memory loads, issued through the builtin so
 // that the compiler's own wait bookkeeping knows about them (it then does not
@@ -189,6 +194,95 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 __device__ __forceinline__ float fdot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 operands (gfx950 32x32x64 scaled MFMA).
+//   v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds 32 bytes of A row m = l%32
+//   (B column n = l%32); bytes 0-15 belong to k-block 0 and bytes 16-31 to
+//   k-block 1 (32 k each), the lane half l/32 choosing which 16 of each
+//   block's 32 k it holds.  The block scale of A (row m, k-block kb) is byte 0
+//   (e8m0: 2^(byte - 127)) of lane m + 32*kb's scale operand, and likewise
+//   for B.  Within a block, k may be permuted freely as long as A and B agree.
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+
+// Both operands e4m3, unit block scales (e8m0 byte 127 is 2^0).
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// A e4m3, B e5m2, per-lane e8m0 block scales sa, sb (byte 0).
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp8_bf8_scaled(i32x8 a, i32x8 b, f32x16 c,
+                                                               int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 1, 0, sa, 0, sb);
+}
+// A e5m2, B e4m3, scales sa, sb, into an accumulator pinned to the
+// accumulation registers (as mfma_acc_pinned).  The wait states the hardware
+// needs between a VALU write of an operand or scale and its read by the
+// product are placed inside the statement (s_nop 4: five), since the compiler
+// does not look inside it.
+__device__ __forceinline__ void mfma_scale_bf8_fp8_pinned(f32x16& c, i32x8 a, i32x8 b, int sa,
+                                                          int sb) {
+  asm("s_nop 4\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:1"
+      : "+a"(c)
+      : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+// Four fp32 values (already within +-448) -> four e4m3 codes, value i in
+// byte i (round to nearest even).
+__device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+// Four fp32 values (within +-57344) -> four e5m2 codes, value i in byte i
+// (round to nearest even).
+__device__ __forceinline__ int cvt_bf8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_bf8_f32(c, d, lo, true);
+}
+
+// Power-of-two block scale: the smallest e with amax <= fmt_max * 2^e (0 for
+// amax = 0), kept >= -126 (so that 2^e is a normal float, and its e8m0 code
+// e + 127 is at least 1).  fmt_max = 0.875 * 2^T (T = 9 for e4m3's 448, 16 for
+// e5m2's 57344): with amax = 1.f * 2^(E-127), amax <= 0.875 * 2^(T+e) holds
+// from e = E - 127 - T + 1 when 1.f <= 1.75 and from one more otherwise.
+// Subnormal maxima fall to the clamp.
+template <int T>
+__device__ __forceinline__ int pow2_block_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int E = (int)(u >> 23);
+  const int e = E - 126 - T + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return amax > 0.f ? (e > -126 ? e : -126) : 0;
+}
+// 2^-e as a float, for -126 <= e <= 126.
+__device__ __forceinline__ float exp2_neg(int e) { return __int_as_float((127 - e) << 23); }
+// 2^e as a float, for -126 <= e <= 127.
+__device__ __forceinline__ float exp2_pos(int e) { return __int_as_float((127 + e) << 23); }
+
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+// Four fp32 values -> four e5m2 codes of x / s (s a power of two, the
+// quotients within +-57344), value i in byte i: v_cvt_scalef32_pk_bf8_f32
+// divides by its scale operand exactly for a power of two and rounds to
+// nearest even, like cvt_bf8x4 on the quotients.
+__device__ __forceinline__ int cvt_bf8x4_div(float a, float b, float c, float d, float s) {
+  s16x2_t r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, a, b, s, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, c, d, s, true);
+  return __builtin_bit_cast(int, r);
+}
+
+// Chunk swizzle of an fp8 tile (128-byte rows, 16-byte chunks) read through
+// the transposing byte read below (two lanes per row, 8 rows, one chunk per
+// lane pair): the read pattern spreads over all 64 banks.
+__device__ __forceinline__ int f8_swz_t(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
+
+// ds_read_b64_tr_b8: within each group of 16 lanes, lanes 2r and 2r+1 address
+// the two 8-byte halves of row r (r = 0..7) of an 8 x 16-byte tile, and output
+// lane i receives byte i of rows 0..7 (byte k of the result from row k).
+__device__ __forceinline__ i32x2_t lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p);
 }
 
 }  // namespace fa

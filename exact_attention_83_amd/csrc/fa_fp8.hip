@@ -25,19 +25,6 @@
 
 namespace fa {
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f32x16 mfma_32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  // unit block scales: the e8m0 exponent 127 is 2^0
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-
-// Four fp32 values (already within +-448) -> four e4m3 codes, value i in byte i.
-__device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-
 constexpr int kQBlk = 128;  // rows per quantisation block
 
 // ---------------------------------------------------------------------------
@@ -150,27 +137,68 @@ __global__ __launch_bounds__(128) void quantize_fp8_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// Power-of-two e4m3 quantiser for the fp8 gradient products ([CH18] §18.6.2
+// (3)): blocks of 32 rows x 128 dims; e = the smallest integer with
+// amax <= 448 * 2^e, codes = e4m3(x * 2^-e) (exact scaling, round to nearest
+// even), the block's e8m0 code e + 127 written beside (as a byte, or as a
+// 32-bit word for kernels that move it with 4-byte direct loads).  One wave
+// per block: lane l holds half l%2 of row l/2; 4 blocks per workgroup.
+constexpr int kP2Rows = 32;
+
+template <typename ET>
+__global__ __launch_bounds__(256) void quantize_pow2_e4m3_kernel(const uint16_t* __restrict__ X,
+                                                                 uint8_t* __restrict__ X8,
+                                                                 ET* __restrict__ XE, int N,
+                                                                 int nb, int total) {
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= total) return;
+  const int bh = blk / nb;
+  const int r0 = (blk - bh * nb) * kP2Rows;
+  const int row = r0 + (lane >> 1);
+  const bool live = row < N;
+  const size_t off = ((size_t)bh * N + row) * D + (lane & 1) * 64;
+  u32x4 ld[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ld[i] = live ? ldg<u32x4>(X + off + 8 * i) : u32x4{0, 0, 0, 0};
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(ld[i][w])), fabsf(bf16_hi(ld[i][w]))));
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  const int e = pow2_block_exp<9>(amax);
+  const float mul = exp2_neg(e);
+  int c[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      c[2 * i + h] = cvt_fp8x4(bf16_lo(ld[i][2 * h]) * mul, bf16_hi(ld[i][2 * h]) * mul,
+                               bf16_lo(ld[i][2 * h + 1]) * mul, bf16_hi(ld[i][2 * h + 1]) * mul);
+  if (live) {
+    uint8_t* yp = X8 + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      stg<u32x4>(yp + 16 * i, u32x4{(uint32_t)c[4 * i], (uint32_t)c[4 * i + 1],
+                                    (uint32_t)c[4 * i + 2], (uint32_t)c[4 * i + 3]});
+  }
+  if (lane == 0) XE[blk] = (ET)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
 namespace {
 constexpr int kF8Waves = 8;
 constexpr int kF8Br = 32 * kF8Waves;  // query rows per workgroup
 constexpr int kF8Bc = 64;             // keys per tile (one 64-deep k-step of P V)
 
-// Chunk swizzles of the fp8 K and V tiles (128-byte rows, 16-byte chunks):
-// K is read as the A operand of S^T = K Q^T (16 rows, one chunk pair each),
-// V through the transposing byte read (two lanes per row, 8 rows, one chunk
-// per lane pair), so each swizzle spreads its own read pattern over all 64
-// banks.
+// Chunk swizzle of the fp8 K tile (128-byte rows, 16-byte chunks), read as
+// the A operand of S^T = K Q^T (16 rows, one chunk pair each); V uses
+// f8_swz_t (transposing byte reads).
 __device__ __forceinline__ int f8_swz_k(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int f8_swz_v(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
-
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
-// ds_read_b64_tr_b8: within each group of 16 lanes, lanes 2r and 2r+1 address
-// the two 8-byte halves of row r (r = 0..7) of an 8 x 16-byte tile, and output
-// lane i receives byte i of rows 0..7 (byte k of the result from row k).
-__device__ __forceinline__ i32x2_t lds_read_tr8(const char* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p);
-}
 }  // namespace
 
 // FP8 forward, the bf16 forward's layout on the 32x32x64 fp8 MFMA: 8 waves x
@@ -253,7 +281,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
   const int drow = wave * 8 + (lane >> 3);
   const int dpos = lane & 7;
   const int koff = drow * ROWB + ((dpos ^ f8_swz_k(drow)) << 4);
-  const int voff = drow * ROWB + ((dpos ^ f8_swz_v(drow)) << 4);
+  const int voff = drow * ROWB + ((dpos ^ f8_swz_t(drow)) << 4);
   auto issue_k = [&](int j, int slot) { buffer_load_lds16(rK, kslot(slot) + wave * 1024, koff, j * TILE); };
   auto issue_v = [&](int j, int slot) { buffer_load_lds16(rV, vslot(slot) + wave * 1024, voff, j * TILE); };
 
@@ -280,7 +308,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
   int vrd[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
-    vrd[db] = vrow * ROWB + (((2 * db + (g16 & 1)) ^ f8_swz_v(vrow)) << 4) + 8 * vhalf;
+    vrd[db] = vrow * ROWB + (((2 * db + (g16 & 1)) ^ f8_swz_t(vrow)) << 4) + 8 * vhalf;
   auto vfrag = [&](const char* vs, int db) {
     int w[8];
 #pragma unroll
@@ -513,6 +541,24 @@ hipError_t launch_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, 
   const int nblk = (N + kQBlk - 1) / kQBlk;
   hipLaunchKernelGGL(quantize_fp8_kernel, dim3(B * H * nblk), dim3(128), 0, stream,
                      (const uint16_t*)x, signs, x8, scales, N, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_pow2_e4m3(const void* x, uint8_t* x8, uint8_t* xe, int BH, int N,
+                                     hipStream_t stream) {
+  const int nb = (N + kP2Rows - 1) / kP2Rows;
+  const int total = BH * nb;
+  hipLaunchKernelGGL(quantize_pow2_e4m3_kernel<uint8_t>, dim3((total + 3) / 4), dim3(256), 0,
+                     stream, (const uint16_t*)x, x8, xe, N, nb, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_pow2_e4m3_words(const void* x, uint8_t* x8, int32_t* xe, int BH, int N,
+                                           hipStream_t stream) {
+  const int nb = (N + kP2Rows - 1) / kP2Rows;
+  const int total = BH * nb;
+  hipLaunchKernelGGL(quantize_pow2_e4m3_kernel<int32_t>, dim3((total + 3) / 4), dim3(256), 0,
+                     stream, (const uint16_t*)x, x8, xe, N, nb, total);
   return hipGetLastError();
 }
 

@@ -60,6 +60,18 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* lse, float* delta, void* dq, int B, int Hq, int Hkv,
                          int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream,
                          int win_l = -1, int win_r = -1, const void* o = nullptr);
+// FP8 dS products: the dQ kernel (d = 128, delta formed from o) with
+// dQ = dS K on e5m2 dS x e4m3 K8 (e8m0 scale words ke, one per 32 key rows).
+hipError_t launch_bwd_dq_fp8(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, float* delta, void* dq, const uint8_t* k8,
+                             const int32_t* ke, const void* o, int B, int Hq, int Hkv, int Nq,
+                             int Nk, float scale, bool causal, hipStream_t stream);
+// FP8 dS products: the dK/dV kernel (d = 128) with dK = dS^T Q on e5m2 dS x
+// e4m3 Q8 (e8m0 scale words qe, one per 32 query rows).
+hipError_t launch_bwd_dkdv_fp8(const void* q, const void* k, const void* v, const void* dout,
+                               const float* lse, const float* delta, void* dk, void* dv,
+                               const uint8_t* q8, const int32_t* qe, int B, int Hq, int Hkv,
+                               int Nq, int Nk, float scale, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dkdv_varlen(const void* q, const void* k, const void* v, const void* dout,
                                   const float* lse, const float* delta, void* dk, void* dv,
                                   const int* cu_q, const int* cu_k, int batch, int Hq, int Hkv,
@@ -107,6 +119,13 @@ hipError_t launch_decode_noalloc(const void* q, const void* k, const void* v, vo
 
 hipError_t launch_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float* scales,
                                int B, int H, int N, int d, hipStream_t stream);
+// Power-of-two e4m3 quantisation of bf16 [BH][N][128] in blocks of 32 rows:
+// codes x8 (same layout), e8m0 scale bytes xe[BH][ceil(N/32)].
+hipError_t launch_quantize_pow2_e4m3(const void* x, uint8_t* x8, uint8_t* xe, int BH, int N,
+                                     hipStream_t stream);
+// The same with each scale code in a 32-bit word (xe[BH][ceil(N/32)]).
+hipError_t launch_quantize_pow2_e4m3_words(const void* x, uint8_t* x8, int32_t* xe, int BH, int N,
+                                           hipStream_t stream);
 hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                           const float* qs, const float* ks, const float* vs, void* o,
                           float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,

@@ -437,6 +437,49 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                      float scale, int causal, hipStream_t stream);
 
 /*
+ * Power-of-two e4m3 quantisation for the fp8 gradient products ([CH18]
+ * §18.6.2 (3); the operands of dQ = dS K and dK = dS^T Q).
+ *   x [B][H][N][d] bf16 in; x8 [B][H][N][d] e4m3fn codes out;
+ *   x_scale [B][H][ceil(N/32)] bytes out, one per block of 32 rows x d.
+ *   Each block gets e = the smallest integer with max|x| <= 448 * 2^e (0 for
+ *   an all-zero block), codes = e4m3(x * 2^-e) (the scaling is exact;
+ *   rounding to nearest even) and x_scale = e + 127 (an e8m0 byte: the block
+ *   holds code * 2^(x_scale - 127)).  e is kept >= -126: blocks whose maximum
+ *   is below 448 * 2^-126 are scaled by 2^126 (their small values may round
+ *   to zero).
+ *   d == 128; x, x8 16-byte aligned.
+ */
+fa_status fa_quantize_pow2_e4m3(const void* x, uint8_t* x8, uint8_t* x_scale,
+                                int B, int H, int N, int d, hipStream_t stream);
+
+/*
+ * Bytes of workspace fa_bwd_fp8 needs: delta [B][Hq][Nq] fp32, the e4m3
+ * copies of K and Q with their 32-row scale codes (one 32-bit word each),
+ * each part rounded up to 256 bytes.
+ */
+size_t fa_bwd_fp8_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/*
+ * Backward with fp8 dS products ([CH18] §18.6.2 (3)): S, P, dP and dS are
+ * formed as in fa_bwd (bf16 products, fp32 softmax terms, delta = rowsum(dO *
+ * O) from the given o); the two dS products then run on the scaled fp8
+ * matrix cores with fp32 accumulation: dQ = scale * dS K with dS in e5m2, one
+ * power-of-two scale per (query row, 32-key block), and dK = scale * dS^T Q
+ * with dS in e5m2, one power-of-two scale per (key, 32-query block), against
+ * K and Q in e4m3 (fa_quantize_pow2_e4m3 blocks, formed here into the
+ * workspace).  dV = P^T dO stays bf16.
+ *   Arguments as fa_bwd; workspace at least fa_bwd_fp8_workspace_size bytes,
+ *   16-byte aligned (contents on entry do not matter).  d == 128.
+ * Launches on `stream`: the K and Q quantisers, dQ (which also forms delta),
+ * dK/dV.  Deterministic.
+ */
+fa_status fa_bwd_fp8(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, hipStream_t stream);
+
+/*
  * Host-side view of the forward's work order ([L21] slides 27-46: longest
  * processing time first).  Writes, for each of the n work units the forward
  * launches in dispatch order, its (b*Hq + h) index, its query-tile index and

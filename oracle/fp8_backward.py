@@ -20,7 +20,14 @@ Readings where the page is silent or garbled (each listed in the design notes):
     dK = dS^T Q, dS in blocks of one key x 32 query rows and Q in blocks of 32
     query rows (all blocks aligned at multiples of 32 from the first row);
   * rounding is to nearest, ties to even; no value exceeds the format's
-    largest finite value, by the choice of scale.
+    largest finite value, by the choice of scale;
+  * delta_i = rowsum(dO_i * O_i) ([CH18] §18.4.4) is formed from O as the
+    backward receives it, the forward's output in the interface's precision
+    (bf16) -- the caller passes it as ``o``; without ``o`` the exact
+    rowsum(P * dP) is used.  With e5m2's coarse steps the difference matters:
+    a change of delta in its ninth bit can move an element of dS across a
+    rounding boundary, one step being up to a quarter of its value, which in
+    a row that sees few keys shifts the whole row of dQ.
 
 With power-of-two scales a normal value rounds to the same relative grid
 whatever its block's exponent; the exponent decides only which small values
@@ -35,17 +42,23 @@ from oracle import attention as A
 from oracle import fp8 as F8
 
 
-def head_backward_fp8(q, k, v, do, scale, causal, quantize=True):
+def head_backward_fp8(q, k, v, do, scale, causal, quantize=True, o=None):
     """One head's (dq, dk, dv) with fp8 dS products (see the module notes).
-    q, do [Nq][d]; k, v [Nk][d] (float32 values, e.g. widened bf16).  With
-    quantize=False every quantisation step is the identity, which must give
-    the exact backward (oracle.attention.head_backward)."""
+    q, do [Nq][d]; k, v [Nk][d] (float32 values, e.g. widened bf16); o [Nq][d]
+    the forward's output as the backward receives it (delta = rowsum(dO * O)),
+    or None for the exact delta.  With quantize=False every quantisation step
+    is the identity, which must give the exact backward
+    (oracle.attention.head_backward) when o is exact."""
     q32, k32 = np.asarray(q, np.float32), np.asarray(k, np.float32)
     qd, kd, v, do = (np.asarray(t, np.float64) for t in (q, k, v, do))
     p, _, _ = A.softmax_rows(A.scores(qd, kd, scale, causal))
     dv = p.T @ do
     dp = do @ v.T
-    ds = A.softmax_backward(p, dp)
+    if o is None:
+        ds = A.softmax_backward(p, dp)
+    else:
+        delta = (do * np.asarray(o, np.float64)).sum(axis=1)
+        ds = p * (dp - delta[:, None])
     nq, nk = ds.shape
     if not quantize:
         return scale * (ds @ kd), scale * (ds.T @ qd), dv
@@ -61,9 +74,10 @@ def head_backward_fp8(q, k, v, do, scale, causal, quantize=True):
     return dq, dk, dv
 
 
-def backward_fp8(q, k, v, do, scale, causal=False, quantize=True):
-    """Batched fp8-dS backward: q, do [B][Hq][Nq][d], k, v [B][Hkv][Nk][d]
-    -> (dQ, dK, dV) float64; a KV head's gradients sum over its query heads."""
+def backward_fp8(q, k, v, do, scale, causal=False, quantize=True, o=None):
+    """Batched fp8-dS backward: q, do (and o, if given) [B][Hq][Nq][d], k, v
+    [B][Hkv][Nk][d] -> (dQ, dK, dV) float64; a KV head's gradients sum over
+    its query heads."""
     q, k, v, do = (np.asarray(t, np.float32) for t in (q, k, v, do))
     B, Hq, Nq, d = q.shape
     Hkv = k.shape[1]
@@ -74,7 +88,7 @@ def backward_fp8(q, k, v, do, scale, causal=False, quantize=True):
         for h in range(Hq):
             hk = A.kv_head(h, Hq, Hkv)
             a, bk, bv = head_backward_fp8(q[b, h], k[b, hk], v[b, hk], do[b, h], scale, causal,
-                                          quantize)
+                                          quantize, None if o is None else o[b, h])
             dq[b, h] = a
             dk[b, hk] += bk
             dv[b, hk] += bv

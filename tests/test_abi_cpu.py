@@ -124,6 +124,35 @@ def test_fp8_validation(lib):
                           0.1, 0, None) == fa.FA_ERR_INVALID_ARG
 
 
+def test_fp8_backward_validation_and_workspace(lib):
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 100, 70, 128
+    r = lambda n: (n + 255) // 256 * 256
+    need = lib.fa_bwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+    assert need == (r(B * Hq * Nq * 4) + r(B * Hkv * Nk * d) + r(B * Hkv * 3 * 4) +
+                    r(B * Hq * Nq * d) + r(B * Hq * 4 * 4))
+    assert lib.fa_bwd_fp8_workspace_size(B, Hq, 0, Nq, Nk, d) == 0
+
+    def call(ws=FAKE, ws_bytes=need, **kw):
+        a = dict(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, scale=0.1, causal=0)
+        a.update(kw)
+        return lib.fa_bwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes,
+                              a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                              a["causal"], None)
+    assert call(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    # the bf16 backward's workspace alone is not enough
+    assert call(ws_bytes=lib.fa_bwd_workspace_size(B, Hq, Nq, d)) == fa.FA_ERR_WORKSPACE
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(d=64, ws_bytes=10 ** 9) == fa.FA_ERR_UNSUPPORTED
+    assert call(causal=1) == fa.FA_ERR_UNSUPPORTED              # Nq != Nk
+    assert call(Hkv=3) == fa.FA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == fa.FA_ERR_INVALID_ARG
+    q = lib.fa_quantize_pow2_e4m3
+    assert q(FAKE, FAKE, FAKE, 1, 1, 64, 64, None) == fa.FA_ERR_UNSUPPORTED
+    assert q(FAKE, MIS, FAKE, 1, 1, 64, 128, None) == fa.FA_ERR_INVALID_ARG
+    assert q(FAKE, FAKE, None, 1, 1, 64, 128, None) == fa.FA_ERR_INVALID_ARG
+    assert q(FAKE, FAKE, FAKE, 1, 1, 0, 128, None) == fa.FA_ERR_INVALID_ARG
+
+
 def test_dense_paths_reject_slabs_past_2gib(lib):
     """One (b, head) slab of Q, K or V is addressed through a buffer descriptor
     with a 32-bit size and signed offsets: a slab of 2 GiB or more must be

@@ -90,6 +90,10 @@ def test_valid_calls_reach_the_launch_under_asan(sanitized_lib):
             lib.fa_decode_combine(A, A, A, A, 2, 8, 128, 16, None),
             lib.fa_decode_splitkv_noalloc(A, A, A, A, A, 2, 8, 2, 4096, 128, 0.1, 16, None),
             lib.fa_quantize_fp8(A, None, A, A, 1, 2, 300, 128, None),
+            lib.fa_quantize_pow2_e4m3(A, A, A, 1, 2, 300, 128, None),
+            lib.fa_bwd_fp8(A, A, A, A, A, A, A, A, A, A,
+                           lib.fa_bwd_fp8_workspace_size(2, 4, 2, 300, 300, 128),
+                           2, 4, 2, 300, 300, 128, 0.1, 1, None),
         ]
         assert all(c == fa.FA_ERR_HIP for c in codes), codes
         bh, qt, cost = fa.fa_fwd_schedule(2, 16, 8192, 8192, 128, True)

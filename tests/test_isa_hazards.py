@@ -1,10 +1,11 @@
 """The dK/dV kernel's accumulator-pinned matrix products are written in inline
-assembly, where the compiler does not place the two wait states the hardware
+assembly, where the compiler does not place the wait states the hardware
 needs between a VALU write of a register and its read by a matrix
 instruction.  This test compiles the backward source for gfx950 with the
 library's own flags and checks the generated assembly: no VALU instruction
-writes a source or accumulator register of such a product in the two
-instructions before it."""
+writes a source, scale or accumulator register of such a product within the
+wait states before it (two for the bf16 product; five, which its statement
+places itself, for the scaled fp8 product), counting an s_nop N as N + 1."""
 import os
 import re
 import shutil
@@ -15,6 +16,8 @@ import pytest
 from exact_attention_83_amd import build as B
 
 PINNED = re.compile(r"^v_mfma_f32_32x32x16_bf16 a\[")
+PINNED_FP8 = re.compile(r"^v_mfma_scale_f32_32x32x64_f8f6f4 a\[")
+WAITS = {"bf16": 2, "fp8": 5}
 
 
 def _regs(tok):
@@ -55,23 +58,38 @@ def _functions(asm):
         yield name, ins
 
 
+def _hazards(ins, i, read, need):
+    """VALU writes of `read` registers within `need` wait states before ins[i]."""
+    found, waited, k = [], 0, i - 1
+    while k >= 0 and waited < need:
+        prev = ins[k]
+        m = re.match(r"s_nop (\d+)", prev)
+        if m:
+            waited += int(m.group(1)) + 1
+        else:
+            if prev.startswith("v_") and not prev.startswith("v_mfma"):
+                ops = _operands(prev)
+                if ops and _regs(ops[0]) & read:
+                    found.append(prev)
+            waited += 1
+        k -= 1
+    return found
+
+
 def test_no_valu_write_right_before_a_pinned_product(bwd_asm):
-    n_pinned = 0
+    counts = {"bf16": 0, "fp8": 0}
     bad = []
     for name, ins in _functions(bwd_asm):
         for i, line in enumerate(ins):
-            if not PINNED.match(line):
+            kind = "bf16" if PINNED.match(line) else "fp8" if PINNED_FP8.match(line) else None
+            if kind is None:
                 continue
-            n_pinned += 1
+            counts[kind] += 1
             ops = _operands(line)
-            read = _regs(ops[0]) | _regs(ops[1]) | _regs(ops[2])
-            for k in (1, 2):
-                prev = ins[i - k]
-                if prev.startswith("v_") and not prev.startswith("v_mfma"):
-                    written = _regs(_operands(prev)[0]) if _operands(prev) else set()
-                    if written & read:
-                        bad.append((name[:60], prev, line))
-    assert n_pinned > 0, "no accumulator-pinned products found (kernel or pattern changed)"
+            read = set().union(*(_regs(o) for o in ops[:3 if kind == "bf16" else 6]))
+            for prev in _hazards(ins, i, read, WAITS[kind]):
+                bad.append((name[:60], prev, line))
+    assert counts["bf16"] > 0 and counts["fp8"] > 0, counts
     assert not bad, bad[:5]
 
 
@@ -84,4 +102,10 @@ def test_register_parser():
            "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]"]
     ops = _operands(ins[2])
     read = _regs(ops[0]) | _regs(ops[1]) | _regs(ops[2])
-    assert _regs(_operands(ins[0])[0]) & read
+    assert _hazards(ins, 2, read, 2) == [ins[0]]
+    # five wait states from an s_nop 4 cover the fp8 product; s_nop 3 does not
+    fp8 = "v_mfma_scale_f32_32x32x64_f8f6f4 a[0:15], v[0:7], v[8:15], a[0:15], v20, v21"
+    read = set().union(*(_regs(o) for o in _operands(fp8)[:6]))
+    assert _hazards(["v_mov_b32_e32 v21, 127", "s_nop 4", fp8], 2, read, 5) == []
+    assert _hazards(["v_mov_b32_e32 v21, 127", "s_nop 3", fp8], 2, read, 5) == [
+        "v_mov_b32_e32 v21, 127"]

@@ -164,6 +164,29 @@ def test_unquantised_path_is_the_exact_backward(causal):
         assert np.abs(a - b).max() < 1e-13 * max(1.0, np.abs(b).max())
 
 
+def test_delta_from_the_given_output():
+    """With o = the exact O the delta rowsum(dO * O) equals rowsum(P * dP)
+    ([CH18] §18.4.4), so the unquantised result is the exact backward; a
+    perturbation E of o moves delta_i by rowsum(dO_i * E_i) and dQ_i by
+    exactly -scale * delta_i' * (P K)_i (dK_j by -scale * sum_i delta_i' P_ij
+    Q_i), the closed form of dS = P (dP - delta)."""
+    N, d, scale = 37, 8, 0.45
+    q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
+    for causal in (False, True):
+        o, _ = A.head_forward(q, k, v, scale, causal)
+        base = FB.head_backward_fp8(q, k, v, do, scale, causal, quantize=False)
+        with_o = FB.head_backward_fp8(q, k, v, do, scale, causal, quantize=False, o=o)
+        for a, b in zip(base, with_o):
+            assert np.abs(a - b).max() < 1e-12
+        e = rng.standard_normal((N, d)) * 1e-3
+        pert = FB.head_backward_fp8(q, k, v, do, scale, causal, quantize=False, o=o + e)
+        dd = (do * e).sum(axis=1)
+        p, _, _ = A.softmax_rows(A.scores(q, k, scale, causal))
+        assert np.abs(pert[0] - (with_o[0] - scale * dd[:, None] * (p @ k))).max() < 1e-12
+        assert np.abs(pert[1] - (with_o[1] - scale * (p * dd[:, None]).T @ q)).max() < 1e-12
+        assert np.array_equal(pert[2], with_o[2])
+
+
 def _bounds(ds, other, fmt_ds, blk_ds, blk_other, scale):
     """Elementwise bound on |scale * (ds^ other^ - ds other)| from the two
     operands' per-element rounding bounds:
