@@ -347,8 +347,8 @@ fa_status fa_bwd_fp8(const void* q, const void* k, const void* v, const void* o,
   uint8_t* q8 = reinterpret_cast<uint8_t*>(ws);
   ws += round256((size_t)B * Hq * Nq * d);
   int32_t* qe = reinterpret_cast<int32_t*>(ws);
-  hipError_t e = fa::launch_quantize_pow2_e4m3_words(k, k8, ke, B * Hkv, Nk, stream);
-  if (e == hipSuccess) e = fa::launch_quantize_pow2_e4m3_words(q, q8, qe, B * Hq, Nq, stream);
+  hipError_t e = fa::launch_quantize_pow2_e4m3_words2(k, k8, ke, B * Hkv, Nk, q, q8, qe, B * Hq,
+                                                      Nq, stream);
   if (e == hipSuccess)
     e = fa::launch_bwd_dq_fp8(q, k, v, dout, lse, delta, dq, k8, ke, o, B, Hq, Hkv, Nq, Nk, scale,
                               causal != 0, stream);
@@ -361,6 +361,7 @@ fa_status fa_bwd_fp8(const void* q, const void* k, const void* v, const void* o,
 fa_status fa_quantize_pow2_e4m3(const void* x, uint8_t* x8, uint8_t* x_scale, int B, int H,
                                 int N, int d, hipStream_t stream) {
   if (!aligned16(x) || !aligned16(x8) || x_scale == nullptr) return FA_ERR_INVALID_ARG;
+  // (codes are stored 8 bytes at a time)
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (d != 128) return FA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * ((N + 31) / 32) >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;

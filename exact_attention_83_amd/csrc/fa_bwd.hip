@@ -697,18 +697,20 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     // (4) dK += dS^T Q.
     if constexpr (FP8DS) {
       // this tile's dS in e5m2 with one power-of-two scale per (key, tile)
-      // (the maximum over both lane halves), its Q fragment halves and scale
+      // (the maximum over both lane halves), its Q fragment halves and scale.
+      // The second tile of a pair quantises key block 1 between key block
+      // 0's products.
       int dsc[KB][4], esc[KB], q8h[DBLK][4];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      float scl[KB];
+      auto block_scale = [&](int kb) {
         const int e = pow2_block_exp<16>(max_halves(am[kb]));
-        const float sc = exp2_pos(e);
+        scl[kb] = exp2_pos(e);
         esc[kb] = e + 127;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dsc[kb][i] = cvt_bf8x4_div(dpb[kb][4 * i], dpb[kb][4 * i + 1], dpb[kb][4 * i + 2],
-                                     dpb[kb][4 * i + 3], sc);
-      }
+      };
+      auto quant = [&](int kb, int i) {
+        dsc[kb][i] = cvt_bf8x4_div(dpb[kb][4 * i], dpb[kb][4 * i + 1], dpb[kb][4 * i + 2],
+                                   dpb[kb][4 * i + 3], scl[kb]);
+      };
       const char* q8s = qs + Q8OFF;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
@@ -720,7 +722,13 @@ __device__ __forceinline__ void bwd_dkdv_unit(
         q8h[db][3] = x1[1];
       }
       const int qe = lds_read<int>(qs + QEOFF + wave * 256, 0);
+      block_scale(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) quant(0, i);
+      block_scale(1);
       if (slot == 0 && !lone) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) quant(1, i);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           esc_prev[kb] = esc[kb];
@@ -736,22 +744,37 @@ __device__ __forceinline__ void bwd_dkdv_unit(
         // k-block 0 = the pair's first tile (or this lone tile), k-block 1 =
         // the second tile (or zeros with unit scales); lane half hf supplies
         // k-block hf's scales
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const i32x8 a = lone ? i32x8{dsc[kb][0], dsc[kb][1], dsc[kb][2], dsc[kb][3], 0, 0, 0, 0}
-                               : i32x8{dsc_prev[kb][0], dsc_prev[kb][1], dsc_prev[kb][2],
-                                       dsc_prev[kb][3], dsc[kb][0], dsc[kb][1], dsc[kb][2],
-                                       dsc[kb][3]};
-          const int sa = lone ? (hf ? 127 : esc[kb]) : (hf ? esc[kb] : esc_prev[kb]);
-          const int sb = lone ? (hf ? 127 : qe) : (hf ? qe : qe_prev);
+        const int sb = lone ? (hf ? 127 : qe) : (hf ? qe : qe_prev);
+        auto operand_b = [&](int db) {
+          return lone ? i32x8{q8h[db][0], q8h[db][1], q8h[db][2], q8h[db][3], 0, 0, 0, 0}
+                      : i32x8{q8h_prev[db][0], q8h_prev[db][1], q8h_prev[db][2],
+                              q8h_prev[db][3], q8h[db][0], q8h[db][1], q8h[db][2], q8h[db][3]};
+        };
+        auto operand_a = [&](int kb) {
+          return lone ? i32x8{dsc[kb][0], dsc[kb][1], dsc[kb][2], dsc[kb][3], 0, 0, 0, 0}
+                      : i32x8{dsc_prev[kb][0], dsc_prev[kb][1], dsc_prev[kb][2], dsc_prev[kb][3],
+                              dsc[kb][0], dsc[kb][1], dsc[kb][2], dsc[kb][3]};
+        };
+        auto scale_a = [&](int kb) {
+          return lone ? (hf ? 127 : esc[kb]) : (hf ? esc[kb] : esc_prev[kb]);
+        };
+        {
+          const i32x8 a = operand_a(0);
+          const int sa = scale_a(0);
 #pragma unroll
           for (int db = 0; db < DBLK; ++db) {
-            const i32x8 b =
-                lone ? i32x8{q8h[db][0], q8h[db][1], q8h[db][2], q8h[db][3], 0, 0, 0, 0}
-                     : i32x8{q8h_prev[db][0], q8h_prev[db][1], q8h_prev[db][2], q8h_prev[db][3],
-                             q8h[db][0], q8h[db][1], q8h[db][2], q8h[db][3]};
-            mfma_scale_bf8_fp8_pinned(dk[kb][db], a, b, sa, sb);
+            mfma_scale_bf8_fp8_pinned(dk[0][db], a, operand_b(db), sa, sb);
+            __builtin_amdgcn_sched_barrier(0);
+            quant(1, db);
+            __builtin_amdgcn_sched_barrier(0);
           }
+        }
+        {
+          const i32x8 a = operand_a(1);
+          const int sa = scale_a(1);
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db)
+            mfma_scale_bf8_fp8_pinned(dk[1][db], a, operand_b(db), sa, sb);
         }
       }
     } else {

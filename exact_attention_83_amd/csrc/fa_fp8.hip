@@ -142,26 +142,39 @@ __global__ __launch_bounds__(128) void quantize_fp8_kernel(const uint16_t* __res
 // amax <= 448 * 2^e, codes = e4m3(x * 2^-e) (exact scaling, round to nearest
 // even), the block's e8m0 code e + 127 written beside (as a byte, or as a
 // 32-bit word for kernels that move it with 4-byte direct loads).  One wave
-// per block: lane l holds half l%2 of row l/2; 4 blocks per workgroup.
+// per block; load i of lane l covers row 4i + l/16, elements 8*(l%16) .. +8,
+// so that each load and store instruction of a wave touches one contiguous
+// range (1 KB in, 512 bytes out).  One launch can quantise two tensors (the
+// blocks of the second follow those of the first), 4 blocks per workgroup.
 constexpr int kP2Rows = 32;
 
 template <typename ET>
-__global__ __launch_bounds__(256) void quantize_pow2_e4m3_kernel(const uint16_t* __restrict__ X,
-                                                                 uint8_t* __restrict__ X8,
-                                                                 ET* __restrict__ XE, int N,
-                                                                 int nb, int total) {
+struct P2Tensor {
+  const uint16_t* x;
+  uint8_t* x8;
+  ET* xe;
+  int N, nb, total;  // rows per (b, h), blocks per (b, h), blocks
+};
+
+template <typename ET>
+__global__ __launch_bounds__(256) void quantize_pow2_e4m3_kernel(P2Tensor<ET> t0, P2Tensor<ET> t1) {
   constexpr int D = 128;
   const int lane = threadIdx.x & 63;
-  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= total) return;
-  const int bh = blk / nb;
-  const int r0 = (blk - bh * nb) * kP2Rows;
-  const int row = r0 + (lane >> 1);
-  const bool live = row < N;
-  const size_t off = ((size_t)bh * N + row) * D + (lane & 1) * 64;
+  int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool second = blk >= t0.total;
+  const P2Tensor<ET> t = second ? t1 : t0;
+  if (second) blk -= t0.total;
+  if (blk >= t.total) return;
+  const int bh = blk / t.nb;
+  const int r0 = (blk - bh * t.nb) * kP2Rows;
+  const int col = (lane & 15) * 8;
+  const size_t base = ((size_t)bh * t.N + r0) * D;
   u32x4 ld[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ld[i] = live ? ldg<u32x4>(X + off + 8 * i) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    ld[i] = r0 + row < t.N ? ldg<u32x4>(t.x + base + row * D + col) : u32x4{0, 0, 0, 0};
+  }
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -172,21 +185,16 @@ __global__ __launch_bounds__(256) void quantize_pow2_e4m3_kernel(const uint16_t*
   for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
   const int e = pow2_block_exp<9>(amax);
   const float mul = exp2_neg(e);
-  int c[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      c[2 * i + h] = cvt_fp8x4(bf16_lo(ld[i][2 * h]) * mul, bf16_hi(ld[i][2 * h]) * mul,
-                               bf16_lo(ld[i][2 * h + 1]) * mul, bf16_hi(ld[i][2 * h + 1]) * mul);
-  if (live) {
-    uint8_t* yp = X8 + off;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      stg<u32x4>(yp + 16 * i, u32x4{(uint32_t)c[4 * i], (uint32_t)c[4 * i + 1],
-                                    (uint32_t)c[4 * i + 2], (uint32_t)c[4 * i + 3]});
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    const int c0 = cvt_fp8x4(bf16_lo(ld[i][0]) * mul, bf16_hi(ld[i][0]) * mul,
+                             bf16_lo(ld[i][1]) * mul, bf16_hi(ld[i][1]) * mul);
+    const int c1 = cvt_fp8x4(bf16_lo(ld[i][2]) * mul, bf16_hi(ld[i][2]) * mul,
+                             bf16_lo(ld[i][3]) * mul, bf16_hi(ld[i][3]) * mul);
+    if (r0 + row < t.N) stg<u32x2>(t.x8 + base + row * D + col, u32x2{(uint32_t)c0, (uint32_t)c1});
   }
-  if (lane == 0) XE[blk] = (ET)(e + 127);
+  if (lane == 0) t.xe[blk] = (ET)(e + 127);
 }
 
 // ---------------------------------------------------------------------------
@@ -544,21 +552,28 @@ hipError_t launch_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, 
   return hipGetLastError();
 }
 
+template <typename ET>
+static P2Tensor<ET> p2_tensor(const void* x, uint8_t* x8, ET* xe, int BH, int N) {
+  const int nb = (N + kP2Rows - 1) / kP2Rows;
+  return P2Tensor<ET>{(const uint16_t*)x, x8, xe, N, nb, BH * nb};
+}
+
 hipError_t launch_quantize_pow2_e4m3(const void* x, uint8_t* x8, uint8_t* xe, int BH, int N,
                                      hipStream_t stream) {
-  const int nb = (N + kP2Rows - 1) / kP2Rows;
-  const int total = BH * nb;
-  hipLaunchKernelGGL(quantize_pow2_e4m3_kernel<uint8_t>, dim3((total + 3) / 4), dim3(256), 0,
-                     stream, (const uint16_t*)x, x8, xe, N, nb, total);
+  const P2Tensor<uint8_t> t = p2_tensor(x, x8, xe, BH, N);
+  const P2Tensor<uint8_t> none{nullptr, nullptr, nullptr, 0, 1, 0};
+  hipLaunchKernelGGL(quantize_pow2_e4m3_kernel<uint8_t>, dim3((t.total + 3) / 4), dim3(256), 0,
+                     stream, t, none);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_pow2_e4m3_words(const void* x, uint8_t* x8, int32_t* xe, int BH, int N,
-                                           hipStream_t stream) {
-  const int nb = (N + kP2Rows - 1) / kP2Rows;
-  const int total = BH * nb;
-  hipLaunchKernelGGL(quantize_pow2_e4m3_kernel<int32_t>, dim3((total + 3) / 4), dim3(256), 0,
-                     stream, (const uint16_t*)x, x8, xe, N, nb, total);
+hipError_t launch_quantize_pow2_e4m3_words2(const void* x0, uint8_t* x8_0, int32_t* xe0, int BH0,
+                                            int N0, const void* x1, uint8_t* x8_1, int32_t* xe1,
+                                            int BH1, int N1, hipStream_t stream) {
+  const P2Tensor<int32_t> t0 = p2_tensor(x0, x8_0, xe0, BH0, N0);
+  const P2Tensor<int32_t> t1 = p2_tensor(x1, x8_1, xe1, BH1, N1);
+  hipLaunchKernelGGL(quantize_pow2_e4m3_kernel<int32_t>, dim3((t0.total + t1.total + 3) / 4),
+                     dim3(256), 0, stream, t0, t1);
   return hipGetLastError();
 }
 

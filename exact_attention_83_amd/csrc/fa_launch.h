@@ -123,9 +123,11 @@ hipError_t launch_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, 
 // codes x8 (same layout), e8m0 scale bytes xe[BH][ceil(N/32)].
 hipError_t launch_quantize_pow2_e4m3(const void* x, uint8_t* x8, uint8_t* xe, int BH, int N,
                                      hipStream_t stream);
-// The same with each scale code in a 32-bit word (xe[BH][ceil(N/32)]).
-hipError_t launch_quantize_pow2_e4m3_words(const void* x, uint8_t* x8, int32_t* xe, int BH, int N,
-                                           hipStream_t stream);
+// The same for two tensors in one launch, each scale code in a 32-bit word
+// (xe[BH][ceil(N/32)]).
+hipError_t launch_quantize_pow2_e4m3_words2(const void* x0, uint8_t* x8_0, int32_t* xe0, int BH0,
+                                            int N0, const void* x1, uint8_t* x8_1, int32_t* xe1,
+                                            int BH1, int N1, hipStream_t stream);
 hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                           const float* qs, const float* ks, const float* vs, void* o,
                           float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
