@@ -594,7 +594,7 @@ __device__ __forceinline__ void bwd_dkdv_unit(
           if constexpr (WIN)
             out = out || (win_l >= 0 && key < qi - win_l) || (win_r >= 0 && key > qi + win_r);
           if constexpr (SPARSE) out = out || !listed;
-          if (out) sb[kb][r] = -INFINITY;
+          sb[kb][r] = out ? -INFINITY : sb[kb][r];
         }
       }
     }
@@ -1157,7 +1157,7 @@ __device__ __forceinline__ void bwd_dq_unit(
           if constexpr (WIN)
             out = out || (win_l >= 0 && key < qrow - win_l) || (win_r >= 0 && key > qrow + win_r);
           if constexpr (SPARSE) out = out || key < 0;
-          if (out) s[kb][r] = -INFINITY;
+          s[kb][r] = out ? -INFINITY : s[kb][r];
         }
     }
     __builtin_amdgcn_sched_barrier(0);

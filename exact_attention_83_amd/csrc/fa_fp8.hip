@@ -15,9 +15,10 @@
 //
 // Forward: the bf16 kernel's structure (S^T = K Q^T with queries on the MFMA
 // n axis, P^T reused as the B operand of O^T += V^T P^T) on the gfx950
-// 32x32x64 fp8 MFMA.  Per-block scales fold into the exp2 argument (Q, K) and
-// into the running-output rescale factor (V).  P is rounded to e4m3 after
-// multiplication by 2^8, which keeps small probabilities out of the subnormal
+// 32x32x64 fp8 MFMA.  Q and K's per-block scales fold into one coefficient of
+// the exp2 argument per tile, V's into the exp2 argument relative to the
+// largest V scale of the row's keys.  P is rounded to e4m3 after
+// multiplication by 2^3, which keeps small probabilities out of the subnormal
 // range; the factor cancels in O / l.
 
 #include "fa_device.h"

@@ -290,7 +290,7 @@ __device__ __forceinline__ void fwd_bf16_unit(
           if constexpr (WIN)
             out = out || (win_l >= 0 && key < qrow - win_l) || (win_r >= 0 && key > qrow + win_r);
           if constexpr (SPARSE) out = out || key < 0;
-          if (out) s[kb][r] = -INFINITY;
+          s[kb][r] = out ? -INFINITY : s[kb][r];
         }
     }
   };
