@@ -508,7 +508,6 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     tile_head(it, &bh, &q0, &listed);
     wait_vmem();
     lds_barrier();
-    if (it + 1 < total) issue(it + 1, slot ^ 1);
     // FP8DS: first (slot 0) or second (slot 1) tile of a pair; a first tile
     // with no second one runs the products itself, against zeros
     const bool lone = FP8DS && slot == 0 && it + 1 >= total;
@@ -556,6 +555,10 @@ __device__ __forceinline__ void bwd_dkdv_unit(
       u32x4 qa[PF1];
 #pragma unroll
       for (int p = 0; p < PF1; ++p) qa[p] = lds_read<u32x4>(qs, ard[p]);
+      // the next tile's loads after this tile's first LDS reads, so that
+      // their address work runs while the reads are in flight
+      asm volatile("" ::: "memory");
+      if (it + 1 < total) issue(it + 1, slot ^ 1);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const u32x4 a = qa[ks % PF1];
