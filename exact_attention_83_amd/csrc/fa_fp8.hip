@@ -7,11 +7,11 @@
 // J = diag(sign) H / sqrt(d); (QJ)(KJ)^T = QK^T while outliers are spread over
 // the whole row).
 //
-// Quantiser, one workgroup (128 threads) per (b, h, 128-row block): the block
-// is staged through LDS with coalesced loads, each thread then owns one row,
-// applies the sign flip and an in-register fast Walsh-Hadamard transform, the
-// block's amax is reduced across the workgroup, and the codes are written
-// through LDS with coalesced stores.
+// Quantiser, one workgroup (4 waves) per (b, h, 128-row block): the block is
+// staged through LDS with direct loads, each lane pair then owns one row,
+// applies the sign flip and a fast Walsh-Hadamard transform (in registers,
+// the last stage across the pair), the block's amax is reduced across the
+// workgroup, and the codes are written through LDS with coalesced stores.
 //
 // Forward: the bf16 kernel's structure (S^T = K Q^T with queries on the MFMA
 // n axis, P^T reused as the B operand of O^T += V^T P^T) on the gfx950
@@ -29,94 +29,107 @@ namespace fa {
 constexpr int kQBlk = 128;  // rows per quantisation block
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void quantize_fp8_kernel(const uint16_t* __restrict__ X,
+// Quantiser, one workgroup of 4 waves per (b, h, 128-row block): the block
+// (32 KB) goes from HBM straight into LDS, 1 KB per wave instruction, each
+// 16-byte chunk c of row r stored at position c ^ (r % 16), so that the 16
+// lanes reading one chunk of 16 consecutive rows hit distinct banks.  Lanes l
+// and l + 32 of wave w then hold the two halves of row 32w + l % 32 (64
+// elements each): ROT applies the sign flip and the first six stages of the
+// natural-order Walsh-Hadamard transform in registers, the last stage (pairs
+// j, j + 64) across the two lane halves through v_permlane32_swap, and the
+// 1/sqrt(128) factor.  The block maximum is reduced over the workgroup, and
+// the codes leave through LDS (the same area) with coalesced stores.
+template <bool ROT>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __restrict__ X,
                                                            const int8_t* __restrict__ signs,
                                                            uint8_t* __restrict__ X8,
                                                            float* __restrict__ scales, int N,
                                                            int nblk) {
   constexpr int D = 128;
-  constexpr int IP = D * 2 + 16;  // bf16 staging pitch
-  constexpr int OP = D + 16;      // code staging pitch
-  __shared__ __attribute__((aligned(16))) char stage[kQBlk * IP];
-  __shared__ float wmax[2];
+  constexpr int ROWB = D * 2;
+  __shared__ __attribute__((aligned(1024))) char stage[kQBlk * ROWB];
+  __shared__ float wmax[4];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hf = lane >> 5;
   const int bh = blockIdx.x / nblk;
   const int blk = blockIdx.x - bh * nblk;
   const int r0 = blk * kQBlk;
   const int rows = min(kQBlk, N - r0);
-  const uint16_t* xp = X + ((size_t)bh * N + r0) * D;
-  uint8_t* yp = X8 + ((size_t)bh * N + r0) * D;
-
-  // Coalesced block load, 16 chunks of 16 bytes per row, and the sign vector:
-  // every load of the thread is issued before the first is used, so the
-  // block's 32 KB are in flight together.
-  constexpr int NLD = kQBlk * 16 / 128;
-  u32x4 ld[NLD];
+  // (rows past N read as zero through the descriptor's bound)
+  const __amdgpu_buffer_rsrc_t rX =
+      make_rsrc(X + ((size_t)bh * N + r0) * D, (uint32_t)rows * ROWB);
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int c = tid + i * 128;
-    const int r = c >> 4, col = c & 15;
-    ld[i] = r < rows ? ldg<u32x4>(xp + (size_t)r * D + col * 8) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < 8; ++i) {
+    const int b1k = wave * 8 + i;  // 1 KB block: rows 4*b1k .. +3
+    const int row = b1k * 4 + (lane >> 4);
+    const int pos = lane & 15;
+    buffer_load_lds16(rX, stage + b1k * 1024, row * ROWB + ((pos ^ (row & 15)) << 4), 0);
   }
-  u32x4 sg[D / 16];
-  if (signs) {
+  u32x4 sg[ROT ? 4 : 1];
+  if constexpr (ROT) {
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) sg[i] = ldg<u32x4>(signs + 16 * i);
+    for (int i = 0; i < 4; ++i) sg[i] = ldg<u32x4>(signs + 64 * hf + 16 * i);
   }
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int c = tid + i * 128;
-    lds_write<u32x4>(stage, (c >> 4) * IP + (c & 15) * 16, ld[i]);
-  }
+  wait_vmem();
   __syncthreads();
 
-  float x[D];
+  const int row = wave * 32 + (lane & 31);
+  float x[64];
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    u32x4 v = lds_read<u32x4>(stage, tid * IP + c * 16);
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 v = lds_read<u32x4>(stage, row * ROWB + (((8 * hf + i) ^ (row & 15)) << 4));
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      x[c * 8 + 2 * w] = bf16_lo(v[w]);
-      x[c * 8 + 2 * w + 1] = bf16_hi(v[w]);
+      x[8 * i + 2 * w] = bf16_lo(v[w]);
+      x[8 * i + 2 * w + 1] = bf16_hi(v[w]);
     }
   }
-  if (signs) {
+  if constexpr (ROT) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      const int8_t sgn = (int8_t)(sg[i / 16][(i / 4) % 4] >> (8 * (i % 4)));
-      x[i] = sgn < 0 ? -x[i] : x[i];
+    for (int j = 0; j < 64; ++j) {
+      const int8_t sgn = (int8_t)(sg[j / 16][(j / 4) % 4] >> (8 * (j % 4)));
+      x[j] = sgn < 0 ? -x[j] : x[j];
     }
-    // natural-order fast Walsh-Hadamard transform (Sylvester H_128)
 #pragma unroll
-    for (int len = 1; len < D; len <<= 1)
+    for (int len = 1; len < 64; len <<= 1)
 #pragma unroll
-      for (int i = 0; i < D; i += 2 * len)
+      for (int i = 0; i < 64; i += 2 * len)
 #pragma unroll
         for (int j = i; j < i + len; ++j) {
           const float a = x[j], b = x[j + len];
           x[j] = a + b;
           x[j + len] = a - b;
         }
+    // last stage: element j of the lower half (lanes 0-31) with element j of
+    // the upper half; r[0] is the lower half's value and r[1] the upper's, in
+    // every lane
     const float inv_sqrt = 0.088388347648318440550f;  // 1/sqrt(128)
 #pragma unroll
-    for (int i = 0; i < D; ++i) x[i] *= inv_sqrt;
+    for (int j = 0; j < 64; ++j) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j]),
+                                                      false, false);
+      const float lo = __uint_as_float(r[0]), up = __uint_as_float(r[1]);
+      x[j] = (hf ? lo - up : lo + up) * inv_sqrt;
+    }
   }
   float amax = 0.f;
-  if (tid < rows) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  }
+  for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(x[j]));
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(wmax[0], wmax[1]);
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();  // (also: every wave is done reading the staged inputs)
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const bool zero = amax == 0.f;
   const float r = zero ? 0.f : 448.f / amax;
 
-  // codes for this thread's row -> LDS (reusing the staging buffer)
+  // codes of this half row -> LDS row `row` (128 bytes, 16-byte chunk c at
+  // position c ^ (row % 8)), then coalesced stores
+  constexpr int OROWB = D;
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < 4; ++c) {
     int w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -126,13 +139,19 @@ __global__ __launch_bounds__(128) void quantize_fp8_kernel(const uint16_t* __res
         v[e] = fminf(fmaxf(x[c * 16 + q * 4 + e] * r, -448.f), 448.f);
       w[q] = cvt_fp8x4(v[0], v[1], v[2], v[3]);
     }
-    lds_write<u32x4>(stage, tid * OP + c * 16,
+    const int chunk = 4 * hf + c;
+    lds_write<u32x4>(stage, row * OROWB + ((chunk ^ (row & 7)) << 4),
                      u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]});
   }
   __syncthreads();
-  for (int c = tid; c < kQBlk * 8; c += 128) {
+  uint8_t* yp = X8 + ((size_t)bh * N + r0) * D;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = tid + 256 * k;
     const int rr = c >> 3, col = c & 7;
-    if (rr < rows) stg<u32x4>(yp + (size_t)rr * D + col * 16, lds_read<u32x4>(stage, rr * OP + col * 16));
+    if (rr < rows)
+      stg<u32x4>(yp + (size_t)rr * D + col * 16,
+                 lds_read<u32x4>(stage, rr * OROWB + ((col ^ (rr & 7)) << 4)));
   }
   if (tid == 0) scales[blockIdx.x] = zero ? 1.f : amax / 448.f;
 }
@@ -548,8 +567,12 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
 hipError_t launch_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float* scales,
                                int B, int H, int N, int d, hipStream_t stream) {
   const int nblk = (N + kQBlk - 1) / kQBlk;
-  hipLaunchKernelGGL(quantize_fp8_kernel, dim3(B * H * nblk), dim3(128), 0, stream,
-                     (const uint16_t*)x, signs, x8, scales, N, nblk);
+  if (signs)
+    hipLaunchKernelGGL(quantize_fp8_kernel<true>, dim3(B * H * nblk), dim3(256), 0, stream,
+                       (const uint16_t*)x, signs, x8, scales, N, nblk);
+  else
+    hipLaunchKernelGGL(quantize_fp8_kernel<false>, dim3(B * H * nblk), dim3(256), 0, stream,
+                       (const uint16_t*)x, signs, x8, scales, N, nblk);
   return hipGetLastError();
 }
 
