@@ -227,6 +227,35 @@ __device__ __forceinline__ int swz_src_offset(int lane, int blk, int stride = RO
   return r * stride + ((p ^ bwd_swz<ROWB>(r)) << 4);
 }
 
+// Slot schedule of the bf16 dK/dV tile's elementwise work.  Slot g is the
+// product g of phases 2-4 (dP: 0-15, dV: 16-31, dK: 32-47); after issuing it
+// the wave packs to bf16 the pairs finished in slot g - 1 and then computes
+// the next elements of P and of dS due in slot g, in element order.
+// P ends in slot 22 (a dV product of k-step 1 first runs in slot 24) and dS
+// in slot 37 (a dK product of k-step 1 first runs in slot 40), so the
+// exponentials spread over the dP and dV products and the dS arithmetic over
+// the dV and dK products instead of piling up in one phase each.
+// P: one element per slot in slots 0-22, two in those with g % 5 = 1 or 3;
+// dS: two per slot in slots 22-37.  The counts below are the elements
+// finished by the end of slot g (none for g < 0).
+__host__ __device__ constexpr int dkdv_p_cum(int g) {
+  return g < 0 ? 0
+               : (g < 22 ? g : 22) + 1 + 2 * (((g < 22 ? g : 22) + 1) / 5) +
+                     (((g < 22 ? g : 22) + 1) % 5 > 1) + (((g < 22 ? g : 22) + 1) % 5 > 3);
+}
+__host__ __device__ constexpr int dkdv_ds_cum(int g) {
+  return g < 22 ? 0 : 2 * ((g < 37 ? g : 37) - 21);
+}
+// every P element done (and packed) before the first dV product that reads
+// it, every dS element before its dK product: rows 0-15 are elements 0-15
+static_assert(dkdv_p_cum(0) == 1 && dkdv_p_cum(1) == 3 && dkdv_p_cum(4) == 7 &&
+                  dkdv_p_cum(21) == 31 && dkdv_p_cum(22) == 32 && dkdv_p_cum(47) == 32 &&
+                  dkdv_p_cum(14) >= 16,
+              "P schedule");
+static_assert(dkdv_ds_cum(21) == 0 && dkdv_ds_cum(22) == 2 && dkdv_ds_cum(37) == 32 &&
+                  dkdv_ds_cum(47) == 32 && dkdv_ds_cum(30) >= 16,
+              "dS schedule");
+
 // ---------------------------------------------------------------------------
 // dK, dV.  Wave w owns KB blocks of 32 keys, kv0 + 32*KB*w + 32*kb + (0..31).
 // Their K rows stay in registers and their V rows in the wave's own LDS
@@ -515,19 +544,22 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     const char* gs = qs + QTILE;
     const char* ls = qs + 2 * QTILE;
 
-    // Four phases of NPH products each: (1) S = Q K^T; (2) dP = dO V^T with
-    // P = exp(S*scale - lse) of the finished S computed between its products;
-    // (3) dV += P^T dO with dS = P (dP - delta) computed between its products;
-    // (4) dK += dS^T Q.  LDS operands are read two product pairs ahead (Q in
-    // phase 1 three), and each phase's first ones during the last products of
-    // the phase before it (this kernel has one wave per SIMD, so nothing else
-    // hides LDS latency).
-    // Element x of phases 2/3 (EPP per product) is register r = 4*(x/8) + x%4
-    // of block kb = (x/4)%2; register r holds query row 8*(r/4) + 4*hf + r%4.
+    // Four phases of NPH products each: (1) S = Q K^T; (2) dP = dO V^T;
+    // (3) dV += P^T dO; (4) dK += dS^T Q.  P = exp(S*scale - lse) of the
+    // finished S and dS = P (dP - delta) are computed between the products of
+    // phases 2-4 (bf16 at d = 128: on the slot schedule of dkdv_p_cum; else P
+    // in phase 2 and dS in phase 3, EPP elements per product).  LDS operands are read
+    // two product pairs ahead (Q in phase 1 three), and each phase's first
+    // ones during the last products of the phase before it (this kernel has
+    // one wave per SIMD, so nothing else hides LDS latency).
+    // Element x (of 32 per lane) is register r = 4*(x/8) + x%4 of block kb =
+    // (x/4)%2; register r holds query row 8*(r/4) + 4*hf + r%4.
     constexpr int NPH = KB * KSTEPS;  // products per phase
     constexpr int EPP = 32 / NPH;     // elements per product (per lane)
     constexpr int NPR = NPH / 2;      // product pairs per phase
     static_assert(KB == 2 && 2 * DBLK * KB == NPH && EPP * NPH == 32, "phase shapes");
+    // the slot schedule is laid out for 16 products per phase (d = 128)
+    constexpr bool SPREAD = !FP8DS && NPH == 16;
     f32x16 sb[KB], dpb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -603,15 +635,62 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     }
     __builtin_amdgcn_sched_barrier(0);
     u32x4 pa[KB][2], dsa[KB][2];  // [kb][k-step]
+    f32x4 nl;  // -lse * log2(e) of P's current row group
+    f32x4 dl;  // delta of dS's current row group
+    // P of element x (in place of S); the next row group's lse is read when
+    // a row group starts
+    auto elem_p = [&](int x) {
+      const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
+      if ((x & 7) == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          nl[q] = -lvn[q] * kLog2e;
+          // a row that sees no key (lse = -inf, possible only with a
+          // sparse pattern) gets P = 0 rather than exp(-inf + inf)
+          if constexpr (SPARSE) nl[q] = lvn[q] == -INFINITY ? -INFINITY : nl[q];
+        }
+        if (gr < 3) lvn = lds_read<f32x4>(ls, ((gr + 1) * 8 + hf * 4) * 4);
+      }
+      sb[kbe][r] = fast_exp2(fmaf(sb[kbe][r], scale_log2, nl[e]));
+    };
+    // bf16 A operand of the element pair (x - 1, x), x odd
+    auto pack_p = [&](int x) {
+      const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
+      pa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(sb[kbe][r - 1], sb[kbe][r]);
+    };
+    // dS of element x (in place of dP), and its pair's bf16 A operand
+    auto elem_ds = [&](int x) {
+      const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
+      if ((x & 7) == 0) {
+        dl = dln;
+        if (gr < 3) dln = lds_read<f32x4>(ls, BQ * 4 + ((gr + 1) * 8 + hf * 4) * 4);
+      }
+      dpb[kbe][r] = sb[kbe][r] * (dpb[kbe][r] - dl[e]);
+    };
+    auto pack_ds = [&](int x) {
+      const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
+      dsa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(dpb[kbe][r - 1], dpb[kbe][r]);
+    };
+    // SPREAD: the elementwise work of slot g (see dkdv_p_cum).  A pair is
+    // packed one slot after its second element: right behind it the pack
+    // would wait for the result.
+    auto slot_work = [&](int g) {
+#pragma unroll
+      for (int x = 1; x < 32; x += 2)
+        if (x >= dkdv_p_cum(g - 2) && x < dkdv_p_cum(g - 1)) pack_p(x);
+#pragma unroll
+      for (int x = 1; x < 32; x += 2)
+        if (x >= dkdv_ds_cum(g - 2) && x < dkdv_ds_cum(g - 1)) pack_ds(x);
+#pragma unroll
+      for (int x = 0; x < 32; ++x)
+        if (x >= dkdv_p_cum(g - 1) && x < dkdv_p_cum(g)) elem_p(x);
+#pragma unroll
+      for (int x = 0; x < 32; ++x)
+        if (x >= dkdv_ds_cum(g - 1) && x < dkdv_ds_cum(g)) elem_ds(x);
+    };
     // (2) dP, with P (in place of S) and its bf16 A operands.  Pair ks uses
     // the dO fragment ga and the V fragments of both key blocks.
     {
-      // bf16 A operand of the element pair (x - 1, x), x odd
-      auto pack_p = [&](int x) {
-        const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
-        pa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(sb[kbe][r - 1], sb[kbe][r]);
-      };
-      f32x4 nl;  // -lse * log2(e) of the current row group
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const u32x4 g = ga[ks & 1];
@@ -633,32 +712,25 @@ __device__ __forceinline__ void bwd_dkdv_unit(
           const int m = 2 * ks + kb;
           dpb[kb] = mfma_32x32x16_bf16(g, v[kb], dpb[kb]);
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (SPREAD) {
+            slot_work(m);
+          } else {
+            // all of P here, EPP elements per product; the previous
+            // product's pairs are packed one product after their exp
 #pragma unroll
-          for (int t = 0; t < EPP; ++t) {
-            const int x = EPP * m + t, gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
-            if ((x & 7) == 0) {
+            for (int t = 0; t < EPP; ++t) elem_p(EPP * m + t);
+            if (m > 0) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                nl[q] = -lvn[q] * kLog2e;
-                // a row that sees no key (lse = -inf, possible only with a
-                // sparse pattern) gets P = 0 rather than exp(-inf + inf)
-                if constexpr (SPARSE) nl[q] = lvn[q] == -INFINITY ? -INFINITY : nl[q];
-              }
-              if (gr < 3) lvn = lds_read<f32x4>(ls, ((gr + 1) * 8 + hf * 4) * 4);
+              for (int t = 1; t < EPP; t += 2) pack_p(EPP * (m - 1) + t);
             }
-            sb[kbe][r] = fast_exp2(fmaf(sb[kbe][r], scale_log2, nl[e]));
-          }
-          // The previous product's pairs are packed here, one product after
-          // their exp: packing right behind the exp costs a wait state each.
-          if (m > 0) {
-#pragma unroll
-            for (int t = 1; t < EPP; t += 2) pack_p(EPP * (m - 1) + t);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if constexpr (!SPREAD) {
 #pragma unroll
-      for (int t = 1; t < EPP; t += 2) pack_p(EPP * (NPH - 1) + t);
+        for (int t = 1; t < EPP; t += 2) pack_p(EPP * (NPH - 1) + t);
+      }
     }
     // (3) dV += P^T dO, with dS = P (dP - delta) and its bf16 A operands
     // (FP8DS: the largest |dS| of each key block, over this lane's rows).
@@ -666,7 +738,6 @@ __device__ __forceinline__ void bwd_dkdv_unit(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) am[kb] = 0.f;
     {
-      f32x4 dl;
 #pragma unroll
       for (int j = 0; j < NPR; ++j) {
         const u32x4 b = gb[j & 1];
@@ -677,20 +748,17 @@ __device__ __forceinline__ void bwd_dkdv_unit(
           const int m = 2 * j + kb;
           mfma_acc_pinned(dv[kb][j % DBLK], pa[kb][j / DBLK], b);
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (SPREAD) {
+            slot_work(NPH + m);
+          } else {
+            // all of dS here (FP8DS: with the largest magnitude per key
+            // block; else each pair packed right behind its second element)
 #pragma unroll
-          for (int t = 0; t < EPP; ++t) {
-            const int x = EPP * m + t, gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
-            if ((x & 7) == 0) {
-              dl = dln;
-              if (gr < 3) dln = lds_read<f32x4>(ls, BQ * 4 + ((gr + 1) * 8 + hf * 4) * 4);
-            }
-            dpb[kbe][r] = sb[kbe][r] * (dpb[kbe][r] - dl[e]);
-            if constexpr (FP8DS) {
-              am[kbe] = fmaxf(am[kbe], fabsf(dpb[kbe][r]));
-            } else {
-              if (e & 1)
-                dsa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] =
-                    pack_bf16(dpb[kbe][r - 1], dpb[kbe][r]);
+            for (int t = 0; t < EPP; ++t) {
+              const int x = EPP * m + t, kbe = (x >> 2) & 1, r = 4 * (x >> 3) + (x & 3);
+              elem_ds(x);
+              if constexpr (FP8DS) am[kbe] = fmaxf(am[kbe], fabsf(dpb[kbe][r]));
+              else if (x & 1) pack_ds(x);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -786,7 +854,15 @@ __device__ __forceinline__ void bwd_dkdv_unit(
         const u32x4 b = qb[j & 1];
         if (j + 2 < NPR) qb[j & 1] = trB(qs, j + 2);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mfma_acc_pinned(dk[kb][j % DBLK], dsa[kb][j / DBLK], b);
+        for (int kb = 0; kb < KB; ++kb) {
+          const int g = 2 * NPH + 2 * j + kb;
+          mfma_acc_pinned(dk[kb][j % DBLK], dsa[kb][j / DBLK], b);
+          if (SPREAD && g <= 38) {
+            __builtin_amdgcn_sched_barrier(0);
+            slot_work(g);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
     }
   };
