@@ -427,17 +427,23 @@ __device__ __forceinline__ void bwd_dkdv_unit(
   const int per_head = SPARSE ? nact * (kSpBq / BQ) : max(0, qt_end - qt_begin);
   const int total = per_head * G;
   // query tile `it` of the loop: head bh, first row q0, and (SPARSE) whether
-  // this wave's key block is listed for it
+  // this wave's key block is listed for it.  Tiles run from the last query
+  // tile down: every work unit of a head then starts on the same tile
+  // and the units running side by side (one XCD holds all of a head's
+  // units) read the same Q and dO rows at about the same time, from L2
+  // (causal: 14% less HBM fetch than starting each unit at its diagonal).
   auto tile_head = [&](int it, int* bh, int* q0, bool* listed = nullptr) {
     const int gi = it / per_head;
     const int x = it - gi * per_head;
     *bh = b * Hq + hk * G + gi;
     if constexpr (SPARSE) {
-      const int e = __builtin_amdgcn_readfirstlane(sp_list[x / (kSpBq / BQ)]);
-      *q0 = (e & 0xffff) * kSpBq + (x % (kSpBq / BQ)) * BQ;
+      // the listed blocks' tiles in the same descending order
+      const int xr = per_head - 1 - x;
+      const int e = __builtin_amdgcn_readfirstlane(sp_list[xr / (kSpBq / BQ)]);
+      *q0 = (e & 0xffff) * kSpBq + (xr % (kSpBq / BQ)) * BQ;
       if (listed) *listed = (e >> (16 + wave)) & 1;
     } else {
-      *q0 = (qt_begin + x) * BQ;
+      *q0 = (qt_end - 1 - x) * BQ;
     }
   };
   int qoff[LPW];
