@@ -143,9 +143,10 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         float scale, int causal, hipStream_t stream);
 
 /*
- * Forward, fp32 in and out (same layout and meaning as fa_fwd).  d == 64.
- * Query and key tiles are 64 rows, so Nk = 256 exercises four rounds of
- * online rescaling.
+ * Forward, fp32 in and out: the tiled forward of [CH18] §18.4.3 (online
+ * softmax across key tiles, Fig. 18-16) with the same layout and meaning as
+ * fa_fwd, everything in fp32.  d == 64.  Query and key tiles are 64 rows,
+ * so Nk = 256 exercises four rounds of online rescaling.
  */
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -270,7 +271,11 @@ fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const voi
                           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                           float scale, int causal, hipStream_t stream);
 
-/* Backward, fp32 tensors, d == 64.  Same meaning as fa_bwd; deterministic. */
+/*
+ * Backward, fp32 tensors, d == 64: the recompute backward of [CH18] §18.4.4
+ * (P rebuilt from lse, delta = rowsum(dO * O), dS = P (dP - delta)), with the
+ * same meaning and workspace as fa_bwd; deterministic.
+ */
 fa_status fa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                      const float* dout, const float* lse,
                      float* dq, float* dk, float* dv,
@@ -420,8 +425,9 @@ fa_status fa_quantize_fp8(const void* x, const int8_t* signs, uint8_t* x8, float
                           int B, int H, int N, int d, hipStream_t stream);
 
 /*
- * FP8 forward: fa_fwd on e4m3 operands with per-128-row-block fp32 scales
- * (from fa_quantize_fp8).  S = (Q8 K8^T) * s_q * s_k * scale; softmax in
+ * FP8 forward ([CH18] §18.6.2 (1)-(2): e4m3 operands with per-block scales;
+ * [L21] slide 24: incoherent processing by the quantiser): fa_fwd on e4m3
+ * operands with per-128-row-block fp32 scales (from fa_quantize_fp8).  S = (Q8 K8^T) * s_q * s_k * scale; softmax in
  * fp32; P is rounded to e4m3 for the P V product; O is bf16, lse fp32.
  *   q8 [B][Hq][Nq][d], k8,v8 [B][Hkv][Nk][d]; q_scale [B][Hq][ceil(Nq/128)],
  *   k_scale, v_scale [B][Hkv][ceil(Nk/128)].  d == 128.
