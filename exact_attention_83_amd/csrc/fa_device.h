@@ -231,15 +231,18 @@ __device__ __forceinline__ void mfma_scale_bf8_fp8_pinned(f32x16& c, i32x8 a, i3
 }
 
 // Four fp32 values (already within +-448) -> four e4m3 codes, value i in
-// byte i (round to nearest even).
+// byte i (round to nearest even).  Each conversion writes one 16-bit half
+// and keeps the other, and the two together write both, so the register
+// they start from is arbitrary: a's bits, which lets the result take a's
+// register (a zero there would cost a move per call).
 __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 // Four fp32 values (within +-57344) -> four e5m2 codes, value i in byte i
-// (round to nearest even).
+// (round to nearest even); the starting register as in cvt_fp8x4.
 __device__ __forceinline__ int cvt_bf8x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_bf8_f32(c, d, lo, true);
 }
 
@@ -267,7 +270,8 @@ typedef short s16x2_t __attribute__((ext_vector_type(2)));
 // divides by its scale operand exactly for a power of two and rounds to
 // nearest even, like cvt_bf8x4 on the quotients.
 __device__ __forceinline__ int cvt_bf8x4_div(float a, float b, float c, float d, float s) {
-  s16x2_t r = {0, 0};
+  // (starting register as in cvt_fp8x4)
+  s16x2_t r = __builtin_bit_cast(s16x2_t, __float_as_int(a));
   r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, a, b, s, false);
   r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, c, d, s, true);
   return __builtin_bit_cast(int, r);
