@@ -11,6 +11,14 @@ its own workload, and reported under "parts": the non-causal forward at the
 same shape, the d=64 prefill forward, the split-KV decode (GB/s of the
 algorithmic bytes K+V+Q+O+LSE) and the fp8 forward.
 
+The device's clock climbs back over some tens of milliseconds after any pause
+of the host (a part timed right after its inputs were made ran up to 15%
+slower in its first 20 calls than from the fourth batch of 20 on).  The
+headline steps are timed exactly as asked (W warmup steps, then K timed
+ones); each part is timed after --settle-ms of its own calls, and the step
+is timed once more the same way and reported as "step_steady", beside the
+headline value, not in place of it.
+
 Prints ONE JSON line.  --gpus above 1 is not supported (one-GPU build).
 """
 from __future__ import annotations
@@ -35,9 +43,29 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def timed(fn, iters, stream):
-    """Average ms of fn() over iters calls, measured with HIP events on stream."""
+def settle(fn, stream, min_ms):
+    """Call fn() until at least min_ms of device time has passed on stream,
+    so that a rate timed next is the sustained one."""
     import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    done, n = 0.0, 1
+    while done < min_ms:
+        s.record(stream)
+        for _ in range(n):
+            fn()
+        e.record(stream)
+        e.synchronize()
+        done += s.elapsed_time(e)
+        n = min(2 * n, 64)
+
+
+def timed(fn, iters, stream, settle_ms=0.0):
+    """Average ms of fn() over iters calls, measured with HIP events on stream
+    (after settle_ms of untimed calls)."""
+    import torch
+    if settle_ms > 0:
+        settle(fn, stream, settle_ms)
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     s.record(stream)
@@ -228,6 +256,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed device time of its own calls before each part is timed")
     ap.add_argument("--only", default="", help="comma list of parts to time (default all)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 256 MiB fp32 read+write kernel first (a known-size "
@@ -338,6 +368,35 @@ def main(argv=None):
     log(f"step {ms_step:.3f} ms: fwd {fwd_ms:.3f} ms ({rate(w.fwd_flops(), fwd_ms):.0f} TF), "
         f"dkdv {dkdv_ms:.3f} ms, dq {dq_ms:.3f} ms, bwd {rate(w.bwd_flops(), bwd_ms):.0f} TF")
 
+    # the same K steps again after --settle-ms of steps: the sustained rate,
+    # reported beside the headline value (which is timed exactly after the W
+    # warmup steps), never in its place
+    if a.settle_ms > 0:
+        settle(lambda: (fwd(), bwd_dq(), bwd_dkdv()), stream, a.settle_ms)
+        sm = [tuple(ev() for _ in range(4)) for _ in range(a.steps)]
+        for e0, e1, e2, e3 in sm:
+            e0.record(stream)
+            fwd()
+            e1.record(stream)
+            bwd_dq()
+            e2.record(stream)
+            bwd_dkdv()
+            e3.record(stream)
+        torch.cuda.synchronize()
+        s_avg = lambda i, j: sum(m[i].elapsed_time(m[j]) for m in sm) / a.steps
+        s_step, s_fwd, s_dq, s_dkdv = s_avg(0, 3), s_avg(0, 1), s_avg(1, 2), s_avg(2, 3)
+        s_bwd = s_step - s_fwd
+        parts["step_steady"] = {
+            "settle_ms": a.settle_ms, "ms": round(s_step, 4),
+            "tflops": round(rate(step_flops, s_step), 1),
+            "frac_peak": round(rate(step_flops, s_step) / PEAK_BF16_TFLOPS, 4),
+            "fwd_ms": round(s_fwd, 4),
+            "fwd_frac_peak": round(rate(w.fwd_flops(), s_fwd) / PEAK_BF16_TFLOPS, 4),
+            "bwd_ms": round(s_bwd, 4), "dq_ms": round(s_dq, 4), "dkdv_ms": round(s_dkdv, 4),
+            "bwd_frac_peak": round(rate(w.bwd_flops(), s_bwd) / PEAK_BF16_TFLOPS, 4)}
+        log(f"steady step {s_step:.3f} ms ({rate(step_flops, s_step):.0f} TF): fwd {s_fwd:.3f} ms, "
+            f"dq {s_dq:.3f} ms, dkdv {s_dkdv:.3f} ms, bwd {rate(w.bwd_flops(), s_bwd):.0f} TF")
+
     iters = max(5, a.steps)
     if not only or "fp8_bwd" in only:
         # the same causal step's backward with the fp8 dS products (K and Q
@@ -356,8 +415,8 @@ def main(argv=None):
             fa.fa_quantize_pow2_e4m3(k, k8, ke, w.B, w.Hkv, w.Nk, w.d, sh)
 
         b8()
-        t8 = timed(b8, iters, stream)
-        tq = timed(kq, iters, stream)
+        t8 = timed(b8, iters, stream, a.settle_ms)
+        tq = timed(kq, iters, stream, a.settle_ms)
         parts["fp8_bwd_causal"] = {
             "ms": round(t8, 4), "tflops": round(rate(w.bwd_flops(), t8), 1),
             "vs_bf16_bwd": round(bwd_ms / t8, 4), "quant_ms_each": round(tq, 4),
@@ -365,7 +424,7 @@ def main(argv=None):
         log(f"fp8 bwd {t8:.3f} ms (bf16 {bwd_ms:.3f}), quantiser {tq:.3f} ms each (K, Q)")
         del ws8, k8, ke
     if not only or "fwd" in only:
-        t = timed(lambda: fwd(False), iters, stream)
+        t = timed(lambda: fwd(False), iters, stream, a.settle_ms)
         tf = 2 * w.fwd_flops() / (t * 1e-3) / 1e12
         parts["fwd_noncausal"] = {"ms": round(t, 4), "tflops": round(tf, 1),
                                   "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
@@ -381,7 +440,7 @@ def main(argv=None):
         f = lambda: fa.fa_fwd(xp["q"], xp["k"], xp["v"], op, lp, wp.B, wp.Hq, wp.Hkv, wp.Nq,
                               wp.Nk, wp.d, wp.scale, False, sh)
         f()
-        t = timed(f, iters, stream)
+        t = timed(f, iters, stream, a.settle_ms)
         tf = wp.fwd_flops() / (t * 1e-3) / 1e12
         parts["fwd_prefill_d64"] = {"ms": round(t, 4), "tflops": round(tf, 1),
                                     "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
@@ -406,9 +465,9 @@ def main(argv=None):
             fa.fa_decode_combine(opart, lpart, od, ld, wd.B, wd.Hq, wd.d, S, sh)
 
         split(); combine()
-        t_all = timed(lambda: (split(), combine()), iters, stream)
-        t_split = timed(split, iters, stream)
-        t_comb = timed(combine, iters, stream)
+        t_all = timed(lambda: (split(), combine()), iters, stream, a.settle_ms)
+        t_split = timed(split, iters, stream, a.settle_ms)
+        t_comb = timed(combine, iters, stream, a.settle_ms)
         nbytes = 2 * wd.B * wd.Hkv * wd.Nk * wd.d * 2 + 2 * wd.B * wd.Hq * wd.d * 2 + wd.B * wd.Hq * 4
         gbs = nbytes / (t_all * 1e-3) / 1e9
         parts["decode"] = {"ms": round(t_all, 4), "split_ms": round(t_split, 4),
@@ -431,7 +490,7 @@ def main(argv=None):
             fa.fa_decode_combine(opt, lpt, ot, lt, wd.B, wd.Hq * NQ, wd.d, S, sh)
 
         tokens()
-        t_tok = timed(tokens, iters, stream)
+        t_tok = timed(tokens, iters, stream, a.settle_ms)
         nb_tok = (2 * wd.B * wd.Hkv * wd.Nk * wd.d * 2 + 2 * wd.B * wd.Hq * NQ * wd.d * 2
                   + wd.B * wd.Hq * NQ * 4)
         gbs_tok = nb_tok / (t_tok * 1e-3) / 1e9
@@ -462,8 +521,8 @@ def main(argv=None):
                              *wa)
 
         wf(); wb()
-        tfw = timed(wf, iters, stream)
-        tbw = timed(wb, iters, stream)
+        tfw = timed(wf, iters, stream, a.settle_ms)
+        tbw = timed(wb, iters, stream, a.settle_ms)
         fl = ww.fwd_flops()
         parts["window_causal"] = {"window": [ww.window_left, ww.window_right],
                                   "fwd_ms": round(tfw, 4),
@@ -492,7 +551,7 @@ def main(argv=None):
                                    wsp.Nq, wsp.Nk, wsp.d, wsp.scale, wsp.causal, pd, idd, mb, sh)
 
         spf()
-        t = timed(spf, iters, stream)
+        t = timed(spf, iters, stream, a.settle_ms)
         tf = wsp.fwd_flops() / (t * 1e-3) / 1e12
         parts["fwd_block_sparse"] = {"ms": round(t, 4), "tflops": round(tf, 1),
                                      "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -508,7 +567,7 @@ def main(argv=None):
                                    wsp.scale, wsp.causal, pd, idd, mb, sh)
 
         spb()
-        tb = timed(spb, iters, stream)
+        tb = timed(spb, iters, stream, a.settle_ms)
         tfb = wsp.bwd_flops() / (tb * 1e-3) / 1e12
         parts["fwd_block_sparse"].update({"bwd_ms": round(tb, 4), "bwd_tflops": round(tfb, 1),
                                           "bwd_frac_peak": round(tfb / PEAK_BF16_TFLOPS, 4)})
@@ -535,7 +594,7 @@ def main(argv=None):
             fa.fa_decode_combine(opg, lpg, og, lg, wg.B, wg.Hq, wg.d, S, sh)
 
         paged()
-        t = timed(paged, iters, stream)
+        t = timed(paged, iters, stream, a.settle_ms)
         keys = sum(wg.seqlens)
         nbytes = 2 * keys * wg.Hkv * wg.d * 2 + 2 * wg.B * wg.Hq * wg.d * 2 + wg.B * wg.Hq * 4
         gbs = nbytes / (t * 1e-3) / 1e9
@@ -560,7 +619,7 @@ def main(argv=None):
                              wv.scale, wv.causal, sh)
 
         vfwd()
-        t = timed(vfwd, iters, stream)
+        t = timed(vfwd, iters, stream, a.settle_ms)
         tf = wv.fwd_flops() / (t * 1e-3) / 1e12
         parts["fwd_varlen"] = {"ms": round(t, 4), "tflops": round(tf, 1),
                                "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -576,7 +635,7 @@ def main(argv=None):
                              wv.total, wv.total, mx, mx, wv.d, wv.scale, wv.causal, sh)
 
         vbwd()
-        tb = timed(vbwd, iters, stream)
+        tb = timed(vbwd, iters, stream, a.settle_ms)
         tfb = wv.bwd_flops() / (tb * 1e-3) / 1e12
         parts["fwd_varlen"].update({"bwd_ms": round(tb, 4), "bwd_tflops": round(tfb, 1),
                                     "bwd_frac_peak": round(tfb / PEAK_BF16_TFLOPS, 4)})
@@ -603,8 +662,8 @@ def main(argv=None):
                           wf.d, wf.scale, False, sh)
 
         f8()
-        t = timed(f8, iters, stream)
-        tq = timed(quant, iters, stream)
+        t = timed(f8, iters, stream, a.settle_ms)
+        tq = timed(quant, iters, stream, a.settle_ms)
         tf = wf.fwd_flops() / (t * 1e-3) / 1e12
         qbytes = 3 * wf.B * wf.Hq * wf.Nq * wf.d * (2 + 1)
         parts["fp8_fwd"] = {"ms": round(t, 4), "tflops": round(tf, 1),
