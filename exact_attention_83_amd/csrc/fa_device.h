@@ -239,6 +239,12 @@ __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
+// The same, starting from a register the caller names (one whose value is
+// dead, where a itself is still read afterwards).
+__device__ __forceinline__ int cvt_fp8x4_from(int start, float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, start, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
 // Four fp32 values (within +-57344) -> four e5m2 codes, value i in byte i
 // (round to nearest even); the starting register as in cvt_fp8x4.
 __device__ __forceinline__ int cvt_bf8x4(float a, float b, float c, float d) {

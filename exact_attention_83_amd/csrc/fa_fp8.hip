@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void quantize_pow2_e4m3_kernel(P2Tensor<ET> t0
 
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kF8Waves = 8;
+constexpr int kF8Waves = 4;
 constexpr int kF8Br = 32 * kF8Waves;  // query rows per workgroup
 constexpr int kF8Bc = 64;             // keys per tile (one 64-deep k-step of P V)
 
@@ -228,8 +228,11 @@ constexpr int kF8Bc = 64;             // keys per tile (one 64-deep k-step of P 
 __device__ __forceinline__ int f8_swz_k(int r) { return (r >> 1) & 7; }
 }  // namespace
 
-// FP8 forward, the bf16 forward's layout on the 32x32x64 fp8 MFMA: 8 waves x
-// 32 query rows, S^T = K Q^T with Q in registers (B operand), P^T rounded to
+// FP8 forward, the bf16 forward's layout on the 32x32x64 fp8 MFMA: 4 waves x
+// 32 query rows per workgroup, two workgroups per CU (so the two waves on a
+// SIMD belong to different workgroups, and one held at its workgroup's
+// barrier by a lazy rescale leaves the SIMD to the other), S^T = K Q^T with Q
+// in registers (B operand), P^T rounded to
 // e4m3 as the B operand of O^T += V^T P^T, K and V tiles of 64 keys straight
 // from HBM into two LDS slots each (swizzled), V^T A operands from transposing
 // byte reads.  The QK^T products of tile i+1 and the PV products of tile i-1
@@ -248,7 +251,7 @@ __device__ __forceinline__ int f8_swz_k(int r) { return (r >> 1) & 7; }
 // pipeline 2.19, 2.27, 2.32, 2.37% (one head); S = 0 is used.  S cancels in
 // O / l (LSE subtracts it).
 template <bool CAUSAL>
-__global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
+__global__ __launch_bounds__(kF8Waves * 64, 8 / kF8Waves) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nq, int Nk,
@@ -260,7 +263,8 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
   constexpr int ROWB = D;              // bytes per fp8 row
   constexpr int TILE = BC * ROWB;      // 8 KB
   constexpr int DBLK = D / 32;
-  static_assert(TILE / 1024 == NW, "one 1 KB direct load per wave per tile");
+  constexpr int LPW = TILE / 1024 / NW;  // 1 KB direct loads per wave per tile
+  static_assert(LPW * NW * 1024 == TILE, "the waves' direct loads cover a tile");
   __shared__ __attribute__((aligned(1024))) char kb0[TILE], kb1[TILE], vb0[TILE], vb1[TILE];
   auto kslot = [&](int s) -> char* { return s == 0 ? kb0 : kb1; };
   auto vslot = [&](int s) -> char* { return s == 0 ? vb0 : vb1; };
@@ -309,14 +313,27 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
     for (int m = 1; m < 64; m <<= 1) svm = fmaxf(svm, __shfl_xor(svm, m, 64));
   }
 
-  // Direct loads: wave w moves rows 8w .. 8w+7 of a tile; lane -> row 8w +
-  // lane/8, LDS chunk position lane%8 holding source chunk (lane%8) ^ swz.
-  const int drow = wave * 8 + (lane >> 3);
+  // Direct loads: load t of wave w moves rows 8c .. 8c+7 of a tile (c =
+  // w * LPW + t); lane -> row 8c + lane/8, LDS chunk position lane%8 holding
+  // source chunk (lane%8) ^ swz.
   const int dpos = lane & 7;
-  const int koff = drow * ROWB + ((dpos ^ f8_swz_k(drow)) << 4);
-  const int voff = drow * ROWB + ((dpos ^ f8_swz_t(drow)) << 4);
-  auto issue_k = [&](int j, int slot) { buffer_load_lds16(rK, kslot(slot) + wave * 1024, koff, j * TILE); };
-  auto issue_v = [&](int j, int slot) { buffer_load_lds16(rV, vslot(slot) + wave * 1024, voff, j * TILE); };
+  int koff[LPW], voff[LPW];
+#pragma unroll
+  for (int t = 0; t < LPW; ++t) {
+    const int drow = (wave * LPW + t) * 8 + (lane >> 3);
+    koff[t] = drow * ROWB + ((dpos ^ f8_swz_k(drow)) << 4);
+    voff[t] = drow * ROWB + ((dpos ^ f8_swz_t(drow)) << 4);
+  }
+  auto issue_k = [&](int j, int slot) {
+#pragma unroll
+    for (int t = 0; t < LPW; ++t)
+      buffer_load_lds16(rK, kslot(slot) + (wave * LPW + t) * 1024, koff[t], j * TILE);
+  };
+  auto issue_v = [&](int j, int slot) {
+#pragma unroll
+    for (int t = 0; t < LPW; ++t)
+      buffer_load_lds16(rV, vslot(slot) + (wave * LPW + t) * 1024, voff[t], j * TILE);
+  };
 
   // K A operand (row kb*32 + l32, head dims 64*st + 32*hf .. +32 = chunks
   // c0 = 4*st + 2*hf and c0 + 1, stored at positions c0 ^ swz and that ^ 1).
@@ -488,22 +505,25 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void fwd_fp8_kernel(
       // again (nothing reads it), so that no branch splits the step
       issue_k(min(i + 2, ntiles - 1), u);
       issue_v(i, u);
-      float p[32];
+      float x[32], p[32];  // exp arguments, p'
       int pw[8];
       auto F = [&](int gg) {
 #pragma unroll
         for (int e = gg * EPG; e < (gg + 1) * EPG; ++e)
-          p[e] = fmaf(s_cur[e >> 4][e & 15], ci, bias);
+          x[e] = fmaf(s_cur[e >> 4][e & 15], ci, bias);
       };
       auto X = [&](int gg) {
 #pragma unroll
-        for (int e = gg * EPG; e < (gg + 1) * EPG; ++e) p[e] = fast_exp2(p[e]);
+        for (int e = gg * EPG; e < (gg + 1) * EPG; ++e) p[e] = fast_exp2(x[e]);
       };
       auto A = [&](int gg) {
 #pragma unroll
         for (int e = gg * EPG; e < (gg + 1) * EPG; ++e) lt += p[e];
         const int k = gg;  // EPG == 4: one dword of four codes per group
-        pw[k] = cvt_fp8x4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
+        // (the codes start from the register of an exp argument, dead by
+        // now, while the p' values still feed the row sum)
+        pw[k] = cvt_fp8x4_from(__float_as_int(x[4 * k]), p[4 * k], p[4 * k + 1], p[4 * k + 2],
+                               p[4 * k + 3]);
         settle(pw[k]);
       };
       static_assert(EPG == 4, "one packed dword per group");
