@@ -10,8 +10,8 @@ Pages cited (by title and section):
   [L21]   "CMU 11-868 L21 FlashAttention" lecture digest (quidproquo.cc)
 
 Conventions (readings of the pages where they are silent or disagree):
-  * scores are multiplied by ``scale`` (the spec convention); [CH18]
-    §18.2.1 writes the same thing as a division by sqrt(d_k).
+  * scores are multiplied by ``scale`` (the library's argument, 1/sqrt(d) by
+    default); [CH18] §18.2.1 writes the same thing as a division by sqrt(d_k).
   * GQA: query head hq reads KV head hq // (Hq // Hkv)  ([CH18] §18.2.2 requires
     Hq to be a multiple of Hkv; the contiguous-group map is our reading).
   * causal is top-left aligned and only defined for Nq == Nk: key j is allowed

@@ -1,7 +1,7 @@
 """Parity of the HIP path against the fp64 oracle, element by element, on the
 same seeded inputs.  Every call goes through the C ABI (ctypes binding).
 
-Tolerances (from the benchmark spec of the problem):
+Tolerances (the accuracy bars the library is held to):
   bf16, fp32 accumulation: O max-abs <= 1e-2, LSE max-abs <= 1e-3,
                            dQ/dK/dV relative L2 <= 1e-2
   fp32 tiny configuration: all of the above <= 1e-5
