@@ -10,12 +10,15 @@
 //   * the G = Hq/Hkv query heads of the group, times the Nq query tokens, are
 //     the n axis of S^T = K Q^T on the 32x32x16 MFMA (column n = g*Nq + t; n =
 //     32 >= G*Nq; the columns past it hold zero queries).
-//   * each wave streams 32-key blocks of the chunk (blocks w, w+4, ...): K
-//     goes from global memory straight into A-operand registers (each lane
-//     reads 128 contiguous bytes of one key row; the head-dim order inside a
-//     k-step is permuted identically in Q), V goes through a per-wave LDS
-//     region where it is stored transposed for O^T += V^T P^T.
-//   * the next block's loads are issued before the current block's math.
+//   * each wave streams 32-key blocks of the chunk (blocks w, w+4, ...)
+//     through one K and one V slot of its own in LDS: direct global-to-LDS
+//     loads, each instruction moving 1 KB of consecutive rows, marked
+//     non-temporal (every key row is read once); K fragments are b128 reads,
+//     V^T fragments transposing reads (ds_read_b64_tr_b16), both from
+//     chunk-swizzled rows.
+//   * the next block's K is loaded as soon as the current block's K reads
+//     are done (after S), its V after the current PV products; the wave waits
+//     for both at the top of the next iteration.
 //   * the 4 waves' (max, sum, O) are merged in LDS and the chunk's normalised
 //     output and logsumexp are written.
 // The work is bound by HBM reads of K and V (about 4 FLOP per byte); MFMA
@@ -38,6 +41,31 @@ static __device__ __align__(256) unsigned char scratch[fa::kNoAllocScratchBytes]
 namespace fa {
 
 namespace {
+// Cache-policy bits of the K/V loads: nt (non-temporal).
+constexpr int kStreamPolicy = 2;
+// Chunk swizzles of the K and V block rows (the forward's tile swizzles):
+// K rows l32 = 0..15 read one chunk each, V rows 4i..4i+3 read four
+// consecutive chunks each, without bank conflicts.
+template <int D>
+__device__ __forceinline__ int dec_swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int dec_swz_v(int r) {
+  return D == 128 ? (4 * (r & 3)) : (4 * ((r >> 1) & 1));
+}
+typedef __attribute__((address_space(1))) void glb_void_t;
+// One wave copies 64 x 16 bytes from global memory to LDS: lane i reads 16
+// bytes at its own address `src` and writes LDS bytes [lds + 16*i, +16);
+// `lds` must be wave-uniform.  Non-temporal: streamed data.
+__device__ __forceinline__ void global_load_lds16_stream(const uint16_t* src, char* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds, 16, 0, kStreamPolicy);
+}
+// Waits for this wave's outstanding LDS reads.
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+}  // namespace
+
+namespace {
 constexpr int kDecWaves = 4;
 constexpr int kDecBlk = 32;  // keys per wave iteration
 }  // namespace
@@ -54,17 +82,20 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     int Hq, int Hkv, int Nk, int num_splits, float scale, float scale_log2,
     const int* __restrict__ table, const int* __restrict__ seqlens, int page_shift,
     int max_pages, int num_pages, int chunk, int Nq = 1, int causal = 0) {
-  constexpr int KS = D / 16;      // k-steps over the head dim
+  constexpr int KS = D / 16;          // k-steps over the head dim
   constexpr int DBLK = D / 32;
-  constexpr int DCH = D / 8;      // 16-byte chunks per row
-  constexpr int HALF = D / 2;     // head dims per lane half for K loads
-  constexpr int VP = kDecBlk * 2 + 8;           // V^T pitch (bytes)
-  constexpr int VREG = kDecBlk * D / 8 / 64;    // 16-byte V chunks per lane
-  constexpr int KREG = KS;                      // 16-byte K chunks per lane
-  __shared__ __attribute__((aligned(16))) char vt_all[kDecWaves * D * VP];
+  constexpr int ROWB = D * 2;         // bytes per key row
+  constexpr int NCH = ROWB / 16;      // 16-byte chunks per row
+  constexpr int RPL = 64 / NCH;       // rows per 1 KB direct load
+  constexpr int LPB = kDecBlk / RPL;  // direct loads per 32-row block
+  constexpr int SLOT = kDecBlk * ROWB;
+  // Per wave: one K and one V slot of a 32-key block (row-major, swizzled).
+  // After the loop the same bytes hold the merge buffer red_o[32][D + 1].
+  __shared__ __attribute__((aligned(1024))) char slots[kDecWaves][2][SLOT];
   __shared__ float red_m[kDecWaves][32];
   __shared__ float red_l[kDecWaves][32];
-  __shared__ float red_o[32][D + 1];
+  static_assert(32 * (D + 1) * 4 <= (int)sizeof(slots), "merge buffer fits in the slots");
+  float (*red_o)[D + 1] = reinterpret_cast<float (*)[D + 1]>(&slots[0][0][0]);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,48 +135,66 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
       return (size_t)key * D;
     }
   };
-  char* vt = vt_all + wave * D * VP;
+  char* kslot = slots[wave][0];
+  char* vslot = slots[wave][1];
 
   // Q^T B operand: column n = l32 is query head hk*G + l32 (zero past G).
-  // k-step ks, element i of lane half hf is head dim hf*HALF + ks*8 + i.
+  // k-step ks, element i of lane half hf is head dim 16*ks + 8*hf + i.
   u32x4 qf[KS];
   {
     const bool valid = l32 < NC;
     const uint16_t* qp = Q + (((size_t)b * Hq + hk * G) * Nq + (valid ? l32 : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 x = ldg<u32x4>(qp + hf * HALF + ks * 8);
+      u32x4 x = ldg<u32x4>(qp + ks * 16 + hf * 8);
       qf[ks] = valid ? x : u32x4{0, 0, 0, 0};
     }
   }
 
   const int nblk = key_end > key_begin ? (key_end - key_begin + kDecBlk - 1) / kDecBlk : 0;
-  u32x4 kreg[KREG], vreg[VREG];
-  // V staging: lane -> 4 consecutive keys (group l/DCH) x 8 head dims.
-  const int v_grp = lane / DCH;
-  const int v_col = lane - v_grp * DCH;
-  constexpr int VGRP_PER_ROUND = 64 / DCH;  // key groups covered per round
-
-  auto load_blk = [&](int blk) {
+  // Direct loads of one 32-key block (K or V) into this wave's slot: load i
+  // moves rows RPL*i .. RPL*i + RPL-1, lane -> row RPL*i + lane/NCH, LDS
+  // chunk position lane%NCH holding source chunk (lane%NCH) ^ swz(row).  Rows
+  // past the chunk's keys repeat its last key (their scores are masked), and
+  // the loads are non-temporal: every key row is read by this workgroup only.
+  auto issue_blk = [&](char* dst, const uint16_t* base, int blk, bool is_v) {
     const int k0 = key_begin + blk * kDecBlk;
     int pg0 = 0, pg1 = 0;
     if constexpr (PAGED) {
       pg0 = min(max(trow[k0 >> page_shift], 0), num_pages - 1);
       pg1 = min(max(trow[(min(k0 + kDecBlk, key_end) - 1) >> page_shift], 0), num_pages - 1);
     }
-    int key = k0 + l32;
-    key = key < key_end ? key : key_end - 1;
-    const uint16_t* kr = Kp + row_off(key, k0, pg0, pg1) + hf * HALF;
 #pragma unroll
-    for (int i = 0; i < KREG; ++i) kreg[i] = ldg<u32x4>(kr + i * 8);
-#pragma unroll
-    for (int i = 0; i < VREG; ++i) {
-      const int round = i / 4;
-      int vk = k0 + (round * VGRP_PER_ROUND + v_grp) * 4 + (i & 3);
-      vk = vk < key_end ? vk : key_end - 1;
-      vreg[i] = ldg<u32x4>(Vp + row_off(vk, k0, pg0, pg1) + v_col * 8);
+    for (int i = 0; i < LPB; ++i) {
+      const int r = RPL * i + lane / NCH;
+      const int pos = lane % NCH;
+      int key = k0 + r;
+      key = key < key_end ? key : key_end - 1;
+      const int src = pos ^ (is_v ? dec_swz_v<D>(r) : dec_swz_k<D>(r));
+      global_load_lds16_stream(base + row_off(key, k0, pg0, pg1) + src * 8, dst + i * 1024);
     }
   };
+  // K A operand of k-step ks: row l32, head dims 16*ks + 8*hf .. +8 (chunk
+  // 2*ks + hf).
+  int krd[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) krd[ks] = l32 * ROWB + (((2 * ks + hf) ^ dec_swz_k<D>(l32)) << 4);
+  // V^T A operand (head-dim block db, keys 16*st ..): two ds_read_b64_tr_b16.
+  // In each 16-lane group g (= lane/16), source lane j addresses key row
+  // 4*(g/2) + j/4 (+ 16*st, + 8 for the second read) at head dims
+  // 32*db + 16*(g%2) + 4*(j%4); output lane i of the group then holds head
+  // dim 32*db + 16*(g%2) + i of those four keys, which is the key order of the
+  // P^T B operand below.
+  const int g16 = lane >> 4;
+  const int j16 = lane & 15;
+  const int vrow = 4 * (g16 >> 1) + (j16 >> 2);
+  const int vsw = dec_swz_v<D>(vrow);  // rows vrow + 8, +16, +24 share it
+  int vrd[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    const int c = 4 * db + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    vrd[db] = vrow * ROWB + ((c ^ vsw) << 4) + (j16 & 1) * 8;
+  }
 
   f32x16 o[DBLK];
 #pragma unroll
@@ -153,26 +202,20 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   int blk = wave;
-  if (blk < nblk) load_blk(blk);
+  if (blk < nblk) {
+    issue_blk(kslot, Kp, blk, false);
+    issue_blk(vslot, Vp, blk, true);
+  }
   for (; blk < nblk; blk += kDecWaves) {
-    // V block -> LDS transposed ([d][key]) as 8-byte runs of 4 keys.
-#pragma unroll
-    for (int rd = 0; rd < VREG / 4; ++rd)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const u32x4* r = vreg + rd * 4;
-        uint32_t lo = (e & 1) ? pack_hi16(r[0][w], r[1][w]) : pack_lo16(r[0][w], r[1][w]);
-        uint32_t hi = (e & 1) ? pack_hi16(r[2][w], r[3][w]) : pack_lo16(r[2][w], r[3][w]);
-        lds_write<u32x2>(vt, (v_col * 8 + e) * VP + ((rd * VGRP_PER_ROUND + v_grp) * 4) * 2,
-                         u32x2{lo, hi});
-      }
+    wait_vmem();  // this block's K and V are in the slots
     f32x16 s = f32x16{0};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma_32x32x16_bf16(kreg[ks], qf[ks], s);
+    for (int ks = 0; ks < KS; ++ks) s = mfma_32x32x16_bf16(lds_read<u32x4>(kslot, krd[ks]), qf[ks], s);
+    // the K slot is free once this wave's reads of it are done
+    wait_lds_reads();
+    if (blk + kDecWaves < nblk) issue_blk(kslot, Kp, blk + kDecWaves, false);
 
     const int k0 = key_begin + blk * kDecBlk;
-    if (blk + kDecWaves < nblk) load_blk(blk + kDecWaves);
 
     if (k0 + kDecBlk > key_end) {
 #pragma unroll
@@ -211,26 +254,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
       pb[st] = u32x4{pack_bf16(p[8 * st + 0], p[8 * st + 1]), pack_bf16(p[8 * st + 2], p[8 * st + 3]),
                      pack_bf16(p[8 * st + 4], p[8 * st + 5]), pack_bf16(p[8 * st + 6], p[8 * st + 7])};
 
-    // The V^T region was written by other lanes of this wave.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int off = (db * 32 + l32) * VP + (st * 16 + hf * 4) * 2;
-        u32x2 a0 = lds_read<u32x2>(vt, off);
-        u32x2 a1 = lds_read<u32x2>(vt, off + 16);
+        const char* vp = vslot + st * 16 * ROWB + vrd[db];
+        const u32x2 a0 = lds_read_tr16(vp);
+        const u32x2 a1 = lds_read_tr16(vp + 8 * ROWB);
         o[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[st], o[db]);
       }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wait_lds_reads();
+    if (blk + kDecWaves < nblk) issue_blk(vslot, Vp, blk + kDecWaves, true);
   }
 
   // Merge the four waves.  Lane (l32, hf) holds head column l32 and head dims
-  // 32*db + 8*(r/4) + 4*hf + r%4.  Each wave rescales its partial output to
+  // 32*db + 8*(r/4) + 4*hf + r%4.  (red_o reuses the slots: every wave has
+  // waited for its last loads and passes the barrier below before any write.)  Each wave rescales its partial output to
   // the merged max and sum, then the waves add into one LDS buffer in a fixed
   // order (deterministic).
   const float l_tot = l_run + xor32(l_run);
