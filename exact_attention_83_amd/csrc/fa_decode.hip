@@ -157,13 +157,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   // chunk position lane%NCH holding source chunk (lane%NCH) ^ swz(row).  Rows
   // past the chunk's keys repeat its last key (their scores are masked), and
   // the loads are non-temporal: every key row is read by this workgroup only.
-  auto issue_blk = [&](char* dst, const uint16_t* base, int blk, bool is_v) {
-    const int k0 = key_begin + blk * kDecBlk;
-    int pg0 = 0, pg1 = 0;
+  // Paged: the block's two page ids (looked up once per block, ahead of its
+  // loads, so that the table reads are not waited for at the load).
+  auto block_pages = [&](int blk, int* pg0, int* pg1) {
+    *pg0 = 0;
+    *pg1 = 0;
     if constexpr (PAGED) {
-      pg0 = min(max(trow[k0 >> page_shift], 0), num_pages - 1);
-      pg1 = min(max(trow[(min(k0 + kDecBlk, key_end) - 1) >> page_shift], 0), num_pages - 1);
+      const int k0 = key_begin + blk * kDecBlk;
+      *pg0 = min(max(trow[k0 >> page_shift], 0), num_pages - 1);
+      *pg1 = min(max(trow[(min(k0 + kDecBlk, key_end) - 1) >> page_shift], 0), num_pages - 1);
     }
+  };
+  auto issue_blk = [&](char* dst, const uint16_t* base, int blk, bool is_v, int pg0, int pg1) {
+    const int k0 = key_begin + blk * kDecBlk;
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
       const int r = RPL * i + lane / NCH;
@@ -203,17 +209,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
 
   int blk = wave;
   if (blk < nblk) {
-    issue_blk(kslot, Kp, blk, false);
-    issue_blk(vslot, Vp, blk, true);
+    int pg0, pg1;
+    block_pages(blk, &pg0, &pg1);
+    issue_blk(kslot, Kp, blk, false, pg0, pg1);
+    issue_blk(vslot, Vp, blk, true, pg0, pg1);
   }
   for (; blk < nblk; blk += kDecWaves) {
+    const bool more = blk + kDecWaves < nblk;
+    int npg0 = 0, npg1 = 0;  // the next block's pages
+    if (more) block_pages(blk + kDecWaves, &npg0, &npg1);
     wait_vmem();  // this block's K and V are in the slots
     f32x16 s = f32x16{0};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s = mfma_32x32x16_bf16(lds_read<u32x4>(kslot, krd[ks]), qf[ks], s);
     // the K slot is free once this wave's reads of it are done
     wait_lds_reads();
-    if (blk + kDecWaves < nblk) issue_blk(kslot, Kp, blk + kDecWaves, false);
+    if (more) issue_blk(kslot, Kp, blk + kDecWaves, false, npg0, npg1);
 
     const int k0 = key_begin + blk * kDecBlk;
 
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
         o[db] = mfma_32x32x16_bf16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[st], o[db]);
       }
     wait_lds_reads();
-    if (blk + kDecWaves < nblk) issue_blk(vslot, Vp, blk + kDecWaves, true);
+    if (more) issue_blk(vslot, Vp, blk + kDecWaves, true, npg0, npg1);
   }
 
   // Merge the four waves.  Lane (l32, hf) holds head column l32 and head dims
