@@ -25,6 +25,17 @@
 
 namespace fa {
 
+namespace {
+// The rotating quantiser reads each input row once: its direct loads use
+// the non-temporal cache policy (bit nt = 2).  Its stores keep the default
+// policy: the codes are read next by the fp8 forward, which measured slower
+// when they had been written non-temporally.
+__device__ __forceinline__ void buffer_load_lds16_stream(__amdgpu_buffer_rsrc_t r, char* lds, int voff,
+                                                         int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 2);
+}
+}  // namespace
+
 constexpr int kQBlk = 128;  // rows per quantisation block
 
 // ---------------------------------------------------------------------------
@@ -64,7 +75,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
     const int b1k = wave * 8 + i;  // 1 KB block: rows 4*b1k .. +3
     const int row = b1k * 4 + (lane >> 4);
     const int pos = lane & 15;
-    buffer_load_lds16(rX, stage + b1k * 1024, row * ROWB + ((pos ^ (row & 15)) << 4), 0);
+    buffer_load_lds16_stream(rX, stage + b1k * 1024, row * ROWB + ((pos ^ (row & 15)) << 4), 0);
   }
   u32x4 sg[ROT ? 4 : 1];
   if constexpr (ROT) {
