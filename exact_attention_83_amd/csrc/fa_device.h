@@ -104,12 +104,23 @@ __device__ __forceinline__ void lds_write(char* base, int off, T v) {
   *reinterpret_cast<T*>(base + off) = v;
 }
 
-// Work order of query-tile work units: longest first under causal masking
-// ([L21] slides 27-46).  Consecutive units walk the (b,h) index fastest, so
-// units of one (b,h) land on the same XCD (workgroups are dealt round-robin
-// over the 8 XCDs) and share K/V in its L2.
+// Work order of query-tile work units.  Workgroups are dealt round-robin over
+// the 8 XCDs (workgroup t runs on XCD t % 8), each with its own L2.  Causal:
+// longest first ([L21] slides 27-46), consecutive units walking the (b,h)
+// index fastest, so that the units of one (b,h) land on the same XCD and
+// share K/V in its L2.  Equal-cost units (not causal, BH a multiple of 8):
+// XCD x takes every query tile of (b,h) x, then of x + 8, ..., so that its
+// compute units stream one (b,h)'s K/V at the same time instead of several
+// (b,h)'s at once.
+constexpr int kXcds = 8;
 __host__ __device__ inline void query_tile_of(int t, int BH, int nqt, bool causal, int* bh,
                                               int* qt) {
+  if (!causal && BH % kXcds == 0) {
+    const int j = t / kXcds;
+    *bh = t % kXcds + kXcds * (j / nqt);
+    *qt = j % nqt;
+    return;
+  }
   *bh = t % BH;
   *qt = causal ? (nqt - 1 - t / BH) : (t / BH);
 }

@@ -230,6 +230,24 @@ def test_forward_schedule_is_lpt_permutation(lib, B, H, N, d, causal):
         assert all(cost[i] == ref[qt[i]] for i in range(len(cost)))
 
 
+@pytest.mark.parametrize("B,H,N", [(2, 16, 8192), (4, 16, 2048), (1, 8, 1000)])
+def test_equal_cost_schedule_keeps_one_head_per_xcd(lib, B, H, N):
+    """Without the causal mask every unit costs the same, and workgroup t
+    (dealt to XCD t % 8) takes the query tiles of one (b, h) after another:
+    the units of an XCD's first nqt workgroups all belong to one (b, h),
+    every (b, h) stays on one XCD, and each (b, h) covers its tiles in order."""
+    bh, qt, cost = fa.fa_fwd_schedule(B, H, N, N, 128, False)
+    nqt = max(qt) + 1
+    assert sorted(zip(bh, qt)) == [(x, y) for x in range(B * H) for y in range(nqt)]
+    assert all(b % 8 == t % 8 for t, b in enumerate(bh))
+    for x in range(8):
+        mine = [(bh[t], qt[t]) for t in range(x, len(bh), 8)]
+        for r in range(0, len(mine), nqt):
+            heads = {h for h, _ in mine[r:r + nqt]}
+            assert len(heads) == 1, (x, r, heads)
+            assert [q for _, q in mine[r:r + nqt]] == list(range(nqt))
+
+
 @pytest.mark.parametrize("workers", [3, 256, 512])
 def test_forward_schedule_matches_greedy_lpt(lib, workers):
     """Dispatching the work units in the library's order to equal-speed
