@@ -385,6 +385,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 8 / kF8Waves) void fwd_fp8_kernel(
   // Per-tile coefficients: c_j multiplies the raw fp8 product (log2 units),
   // e_j = log2(s_v / s_vmax) is added to the exp argument, r_j = s_vmax / s_v
   // converts the tile's sum of p' back to p.
+  static_assert(kQBlk == 2 * BC, "a quantisation block holds the two tiles of a loop iteration");
   auto tile_coef = [&](int j, float* c, float* e, float* r) {
     const int blk = (j * BC) / kQBlk;
     const float sk = KS[(size_t)bhk * nkb + blk];
@@ -489,7 +490,9 @@ __global__ __launch_bounds__(kF8Waves * 64, 8 / kF8Waves) void fwd_fp8_kernel(
     }
     l_run += lt_prev * ri_prev;
   };
-  auto step = [&](int i, auto U) {
+  // (ci, ei, ri: the coefficients of tile i's key block; the two tiles of a
+  // loop iteration, 2m and 2m + 1, share block m)
+  auto step = [&](int i, auto U, float ci, float ei, float ri) {
     constexpr int u = decltype(U)::value;
     f32x16* s_cur = sbuf[u];
     f32x16* s_nxt = sbuf[u ^ 1];
@@ -500,8 +503,6 @@ __global__ __launch_bounds__(kF8Waves * 64, 8 / kF8Waves) void fwd_fp8_kernel(
       settle_tile(s_nxt, pbuf[u ^ 1]);
       mask(i, s_cur);
     }
-    float ci, ei, ri;
-    tile_coef(i, &ci, &ei, &ri);
     const float bias = ei - M + kP8Shift;
     float lt = 0.f;
     {
@@ -567,8 +568,10 @@ __global__ __launch_bounds__(kF8Waves * 64, 8 / kF8Waves) void fwd_fp8_kernel(
     lds_barrier();
   };
   for (int i0 = 0; i0 < ntiles; i0 += 2) {
-    step(i0, IntConst<0>{});
-    if (i0 + 1 < ntiles) step(i0 + 1, IntConst<1>{});
+    float ci, ei, ri;
+    tile_coef(i0, &ci, &ei, &ri);
+    step(i0, IntConst<0>{}, ci, ei, ri);
+    if (i0 + 1 < ntiles) step(i0 + 1, IntConst<1>{}, ci, ei, ri);
   }
   // the last tile's check
   if ((ntiles - 1) & 1) settle_tile(sbuf[1], pbuf[1]);
