@@ -535,6 +535,22 @@ __device__ __forceinline__ void bwd_dkdv_unit(
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) settle(kf[kb][ks]);
+  // V enters dP = dO V^T negated and the dP accumulators start at delta, so
+  // that they end at delta - dP and dS = P (dP - delta) is one multiply by
+  // -P: each wave flips the sign bits of its own V rows once, when they have
+  // landed (before the first tile's products; LDS operations of one wave run
+  // in order).
+  auto negate_v = [&]() {
+    constexpr int NCHK = VROWS * ROWB / 16 / 64;  // 16-byte chunks per lane
+#pragma unroll
+    for (int c = 0; c < NCHK; ++c) {
+      const int off = (c * 64 + lane) * 16;
+      u32x4 x = lds_read<u32x4>(vw, off);
+      x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      lds_write<u32x4>(vw, off, x);
+    }
+    asm volatile("" ::: "memory");
+  };
   if (total > 0) issue(0, 0);
   auto body = [&](int it, auto S) {
     constexpr int slot = decltype(S)::value;
@@ -543,6 +559,7 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     tile_head(it, &bh, &q0, &listed);
     wait_vmem();
     lds_barrier();
+    if (it == 0) negate_v();
     // FP8DS: first (slot 0) or second (slot 1) tile of a pair; a first tile
     // with no second one runs the products itself, against zeros
     const bool lone = FP8DS && slot == 0 && it + 1 >= total;
@@ -566,12 +583,9 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     static_assert(KB == 2 && 2 * DBLK * KB == NPH && EPP * NPH == 32, "phase shapes");
     // the slot schedule is laid out for 16 products per phase (d = 128)
     constexpr bool SPREAD = !FP8DS && NPH == 16;
-    f32x16 sb[KB], dpb[KB];
+    f32x16 sb[KB], dpb[KB];  // dpb: set to delta at the end of phase 1
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      sb[kb] = f32x16{0};
-      dpb[kb] = f32x16{0};
-    }
+    for (int kb = 0; kb < KB; ++kb) sb[kb] = f32x16{0};
     // Transposed B operand (dO^T or Q^T rows) of pair j of phases 3/4:
     // st = j / DBLK, db = j % DBLK.
     auto trB = [&](const char* base, int j) {
@@ -585,7 +599,6 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     u32x4 ga[2], va[2][KB];  // phase 2: dO and V fragments, two pairs ahead
     f32x4 lvn;               // phase 2: lse of the current row group
     u32x4 gb[2], qb[2];      // phases 3 / 4: first two transposed B operands
-    f32x4 dln;               // phase 3: delta of the current row group
     // (1) S: pair ks shares the Q fragment, read PF1 pairs ahead.
     {
       constexpr int PF1 = 3;
@@ -610,6 +623,16 @@ __device__ __forceinline__ void bwd_dkdv_unit(
             for (int kb = 0; kb < KB; ++kb) va[pp][kb] = lds_read<u32x4>(vw, kb * 32 * ROWB + ard[pp]);
           } else {
             lvn = lds_read<f32x4>(ls, (hf * 4) * 4);
+            // the dP accumulators start at the delta of this lane's rows
+            // (register 4g + e: row 8g + 4*hf + e)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 d4 = lds_read<f32x4>(ls, BQ * 4 + (g * 8 + hf * 4) * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dpb[kb][4 * g + e] = d4[e];
+              }
           }
         }
 #pragma unroll
@@ -642,7 +665,6 @@ __device__ __forceinline__ void bwd_dkdv_unit(
     __builtin_amdgcn_sched_barrier(0);
     u32x4 pa[KB][2], dsa[KB][2];  // [kb][k-step]
     f32x4 nl;  // -lse * log2(e) of P's current row group
-    f32x4 dl;  // delta of dS's current row group
     // P of element x (in place of S); the next row group's lse is read when
     // a row group starts
     auto elem_p = [&](int x) {
@@ -664,14 +686,10 @@ __device__ __forceinline__ void bwd_dkdv_unit(
       const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
       pa[kbe][gr >> 1][2 * (gr & 1) + (e >> 1)] = pack_bf16(sb[kbe][r - 1], sb[kbe][r]);
     };
-    // dS of element x (in place of dP), and its pair's bf16 A operand
+    // dS of element x (in place of dP, which holds delta - dP here)
     auto elem_ds = [&](int x) {
-      const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
-      if ((x & 7) == 0) {
-        dl = dln;
-        if (gr < 3) dln = lds_read<f32x4>(ls, BQ * 4 + ((gr + 1) * 8 + hf * 4) * 4);
-      }
-      dpb[kbe][r] = sb[kbe][r] * (dpb[kbe][r] - dl[e]);
+      const int kbe = (x >> 2) & 1, r = 4 * (x >> 3) + (x & 3);
+      dpb[kbe][r] = -sb[kbe][r] * dpb[kbe][r];
     };
     auto pack_ds = [&](int x) {
       const int gr = x >> 3, kbe = (x >> 2) & 1, e = x & 3, r = 4 * gr + e;
@@ -711,7 +729,6 @@ __device__ __forceinline__ void bwd_dkdv_unit(
         } else {
           // phase 3's first operands
           gb[ks + 2 - KSTEPS] = trB(gs, ks + 2 - KSTEPS);
-          if (ks + 1 == KSTEPS) dln = lds_read<f32x4>(ls, BQ * 4 + (hf * 4) * 4);
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -1060,6 +1077,11 @@ __device__ __forceinline__ void bwd_dq_unit(
   } else {
     dlt = Delta[l_off + qrow_c];
   }
+  // dO enters dP^T = V dO^T negated and the dP accumulators start at delta,
+  // so that they end at delta - dP and dS = P (dP - delta) is one multiply by
+  // -P (the sign flip is exact; the dO fragments serve nothing else below)
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) gf[ks] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 
   int kv_end = CAUSAL ? min(Nk, q0 + BR) : Nk;
   int jf = 0;  // first key tile visited
@@ -1190,12 +1212,9 @@ __device__ __forceinline__ void bwd_dq_unit(
     constexpr int EPB = 32 / NAB;        // elements per phase-B product
     constexpr int NCB = 2 * DBLK;        // phase-C products per key block
     constexpr int EPC = 16 / NCB;        // block-1 elements per block-0 product
-    f32x16 s[2], dp[2];
+    f32x16 s[2], dp[2];  // dp: set to delta just before phase B
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{0};
-      dp[kb] = f32x16{0};
-    }
+    for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{0};
     // LDS operands are read PF products ahead of their use (the latency of
     // a read is several products long, and only one other wave shares the
     // SIMD to hide it).  Operand m of phases A and B: key block m % 2, k-step
@@ -1253,13 +1272,17 @@ __device__ __forceinline__ void bwd_dq_unit(
     // key 32*(i/16) + 8*((i/4)%4) + 4*hf + i%4, the order of the S
     // accumulator (and of the K^T fragments).  Key block 0 is done between
     // block 1's dP products, block 1 after them.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      dp[kb] = f32x16{dlt, dlt, dlt, dlt, dlt, dlt, dlt, dlt,
+                      dlt, dlt, dlt, dlt, dlt, dlt, dlt, dlt};
     float am0 = 0.f, am1 = 0.f, sc0 = 1.f;
     int e0 = 0;
     int w8[FP8DS ? 8 : 1];
     auto ds_slice = [&](int kb, int i) {  // elements 4i .. 4i+3 of key block kb
 #pragma unroll
       for (int r = 4 * i; r < 4 * i + 4; ++r) {
-        dp[kb][r] = s[kb][r] * (dp[kb][r] - dlt);
+        dp[kb][r] = -s[kb][r] * dp[kb][r];
         if (kb == 0) am0 = fmaxf(am0, fabsf(dp[0][r]));
         else am1 = fmaxf(am1, fabsf(dp[1][r]));
       }
@@ -1319,7 +1342,7 @@ __device__ __forceinline__ void bwd_dq_unit(
     }
     u32x4 dsb[2][2];
     auto ds_elem = [&](int kb, int r) {
-      dp[kb][r] = s[kb][r] * (dp[kb][r] - dlt);
+      dp[kb][r] = -s[kb][r] * dp[kb][r];
       if (r & 1) {
         const int st = r >> 3, w = (r & 7) >> 1;
         dsb[kb][st][w] = pack_bf16(dp[kb][r - 1], dp[kb][r]);
