@@ -166,10 +166,11 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Nq, int d);
  *   gradient is summed over the query heads of its group.
  *   workspace: at least fa_bwd_workspace_size(B,Hq,Nq,d) bytes, 16-byte
  *   aligned; its contents on entry do not matter.
- * Three launches on `stream`: delta_i = dO_i . O_i (equal to rowsum(P * dP),
- * [CH18] §18.4.4); dK and dV, one work unit per KV tile accumulating over the
- * query tiles; dQ, one work unit per query tile accumulating over the KV
- * tiles.  No atomics: results are deterministic.
+ * Two launches on `stream`: dQ, one work unit per query tile accumulating
+ * over the KV tiles, which also forms delta_i = dO_i . O_i (equal to
+ * rowsum(P * dP), [CH18] §18.4.4) from its rows' dO and O and writes it to the
+ * workspace; then dK and dV, one work unit per KV tile accumulating over the
+ * query tiles.  No atomics: results are deterministic.
  *   d in {64, 128}.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -202,7 +203,7 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
  *   bytes, 16-byte aligned: delta, then a byte map of the pattern (query
  *   tiles x key blocks) that the call rebuilds from the lists each time.
  * A row that sees no key gets dQ = 0; a key that no row sees dK = dV = 0.
- * Four launches on `stream` (delta, the map, dK/dV, dQ); deterministic.
+ * Three launches on `stream` (the map, dQ with delta, dK/dV); deterministic.
  *   d in {64, 128}; ceil(Nq / FA_SPARSE_BLOCK_Q) <= 256 (FA_ERR_UNSUPPORTED
  *   above: a dK/dV work unit keeps the query tiles it visits in 256 slots).
  */
@@ -227,7 +228,7 @@ fa_status fa_bwd_block_sparse(const void* q, const void* k, const void* v, const
  *   16-byte aligned (delta, head-major like lse).
  * Gradients never cross a sequence boundary; a key with no visible query
  * (e.g. a sequence with keys but no queries) gets dK = dV = 0, a query with
- * no key dQ = 0.  Same three launches as fa_bwd; deterministic.
+ * no key dQ = 0.  Same two launches as fa_bwd; deterministic.
  *   d in {64, 128}; total_q * Hq * d * 2 and total_k * Hkv * d * 2 < 2^31.
  */
 fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
