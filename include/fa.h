@@ -72,8 +72,10 @@ int fa_version(void);
  *   bf16 (nearest-even).
  * Work units (query tiles) are ordered longest first ([L21] slides 27-46);
  * causal, a persistent grid of one workgroup per compute unit walks that list
- * (fa_persistent_schedule; [L21] slide 26), otherwise one workgroup per unit
- * is launched in that order.
+ * (fa_persistent_schedule; [L21] slide 26).  Otherwise every unit costs the
+ * same and one workgroup per unit is launched, in an order that gives each
+ * XCD (workgroup t runs on XCD t % 8) the query tiles of one (b, h) after
+ * another when B*Hq is a multiple of 8 (fa_fwd_schedule shows the order).
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d,
