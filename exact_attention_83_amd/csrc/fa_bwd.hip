@@ -5,10 +5,13 @@
 // with one factor of the score scale) and §18.4.4 (recomputation: P is rebuilt
 // tile by tile from the saved logsumexp, so no rescaling is needed; only O(N)
 // row statistics are kept from the forward).  The row term rowsum(P * dP)
-// equals dO_i . O_i, which a pre-pass computes from O and dO.
+// equals dO_i . O_i, which the dQ kernel forms from its rows' O and dO (or a
+// pre-pass computes) and writes for the dK/dV kernel.  Both kernels start
+// their dP accumulators at that delta and feed dO V^T one factor negated, so
+// dS = P * (dP - delta) is a single multiply by -P.
 //
-// The bf16 path runs the delta pre-pass and then two kernels (see the
-// comment above bwd_dkdv_kernel).  Causal: a KV tile only visits the query
+// The bf16 path runs the dQ kernel (forming delta) and then the dK/dV kernel
+// (see the comments above both).  Causal: a KV tile only visits the query
 // tiles that reach its keys, a query tile only the key tiles up to its last
 // row, and only tiles crossing the diagonal are masked ([CH18] §18.5.2 (4):
 // the skipped gradients are structurally zero).  Work units are launched
