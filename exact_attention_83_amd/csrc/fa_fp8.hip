@@ -16,7 +16,8 @@
 // Forward: the bf16 kernel's structure (S^T = K Q^T with queries on the MFMA
 // n axis, P^T reused as the B operand of O^T += V^T P^T) on the gfx950
 // 32x32x64 fp8 MFMA.  Q and K's per-block scales fold into one coefficient of
-// the exp2 argument per tile, V's into the exp2 argument relative to the
+// the exp2 argument per 128-key block (two tiles), V's into the exp2 argument
+// relative to the
 // largest V scale of the row's keys.  P relative to a lazily updated
 // reference max is rounded to e4m3 as it is.
 
