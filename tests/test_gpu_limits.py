@@ -14,6 +14,9 @@ Tolerances are the bf16 ones of the parity tests: O max-abs 1e-2, LSE max-abs
 1e-3, gradients relative L2 1e-2; with millions of keys each row of O is a
 mean of nearly uniform weights and its entries are small (about 1e-3 here),
 so O is also held to relative L2 1e-2 per checked row.
+
+The fp8 quantiser and forward are checked at their own limit, one head of
+2^24 - 40 one-byte keys, in the last test.
 """
 import math
 
@@ -22,6 +25,7 @@ import pytest
 import torch
 
 from oracle import attention as A
+from oracle import fp8 as F8
 from tests.conftest import say
 
 pytestmark = pytest.mark.gpu
@@ -106,3 +110,75 @@ def test_backward_longest_head(fa_gpu, long_kv):
         e = rel_l2(f64(got), want)
         print(f"{name} relative L2 {e:.2e}")
         assert e <= BF16_GRAD, (name, e)
+
+
+# fp8: one head of 2^24 - 40 keys.  The e4m3 K and V hold 2^31 - 5120 bytes
+# each (the same 2^31-byte bound, now on one-byte elements); their bf16
+# sources, 4 GiB each, go through the quantiser, whose per-block addresses
+# are 64-bit.  The last 128-row block holds 88 rows, the last 64-key tile 24.
+NK8 = (1 << 24) - 40
+P8 = 128 * 1021          # key period: whole 128-row blocks, a prime count of them
+FP8_REL = 5e-2
+
+
+def test_fp8_longest_head(fa_gpu):
+    """Quantiser and fp8 forward at the fp8 key-length limit, GQA (two query
+    heads on the KV head), 96 query rows, non-causal, no rotation.
+
+    K and V repeat a seeded pattern of P8 keys (128 whole periods and a
+    partial one of 49112 keys), so the oracle quantises 179800 rows rather
+    than 16.8 million: its quantisation works per 128-row block and the
+    period is a whole number of blocks, so the blocks of the full head are
+    the pattern's blocks repeated, then the partial period's own blocks
+    (whose last one is the head's ragged 88-row block).  A read from the
+    wrong key tile lands on other data, since 1021 blocks is prime to every
+    power of two.  The forward itself runs in the oracle over all NK8 keys.
+    Codes and scales of K and V are checked bit-exact over the whole head;
+    O (rows 0, 47, 95 of both heads) to relative L2 5e-2 per row against the
+    oracle's fp8 pipeline, LSE to 5e-2 absolute."""
+    assert NK8 * D < 1 << 31
+    m, rem = divmod(NK8, P8)
+    g = torch.Generator(device="cuda").manual_seed(8405)
+    kp = torch.randn(P8, D, generator=g, device="cuda").to(torch.bfloat16)
+    vp = torch.randn(P8, D, generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn(1, 2, 96, D, generator=g, device="cuda").to(torch.bfloat16)
+    k = kp.repeat(m + 1, 1)[:NK8].reshape(1, 1, NK8, D).contiguous()
+    v = vp.repeat(m + 1, 1)[:NK8].reshape(1, 1, NK8, D).contiguous()
+    say(f"fp8 quantiser + forward at the key-length limit: Nq=96 Nk={NK8} Hq=2 Hkv=1")
+    q8, qs = fa_gpu.quantize_fp8(q, None)
+    k8, ks = fa_gpu.quantize_fp8(k, None)
+    v8, vs = fa_gpu.quantize_fp8(v, None)
+    o, lse = fa_gpu.forward_fp8(q8, k8, v8, qs, ks, vs, causal=False)
+    torch.cuda.synchronize()
+    del k, v
+
+    say("fp8 limit: oracle quantisation of the key pattern")
+    qd = F8.dequantize(*F8.quantize(q.float().cpu().numpy()))
+    deq = []
+    for name, pat, got8, gots in (("k", kp, k8, ks), ("v", vp, v8, vs)):
+        pat = pat.float().cpu().numpy()[None, None]
+        cp, sp = F8.quantize(pat)
+        cr, sr = F8.quantize(pat[:, :, :rem])
+        got8, gots = got8.cpu().numpy(), gots.cpu().numpy()
+        want_s = np.concatenate([np.tile(sp, (1, 1, m)), sr], axis=2)
+        assert np.array_equal(gots, want_s), name
+        for i in range(m):
+            assert np.array_equal(got8[:, :, i * P8:(i + 1) * P8], cp), (name, i)
+        assert np.array_equal(got8[:, :, m * P8:], cr), name
+        del got8
+        full = np.empty((1, 1, NK8, D))
+        dp, dr = F8.dequantize(cp, sp), F8.dequantize(cr, sr)
+        for i in range(m):
+            full[:, :, i * P8:(i + 1) * P8] = dp
+        full[:, :, m * P8:] = dr
+        deq.append(full)
+    print(f"codes and scales of K and V bit-exact ({NK8} keys)")
+
+    say("fp8 limit: oracle forward over all keys")
+    rows = [0, 47, 95]
+    ro, rl = A.forward(qd, deq[0], deq[1], 1 / math.sqrt(D), False, rows=rows)
+    got = f64(o)[:, :, rows]
+    er = max(rel_l2(got[0, h, i], ro[0, h, i]) for h in range(2) for i in range(len(rows)))
+    el = np.abs(f64(lse)[:, :, rows] - rl).max()
+    print(f"O worst row relative L2 {er:.2e}, LSE max-abs {el:.2e}")
+    assert er <= FP8_REL and el <= 5e-2, (er, el)
